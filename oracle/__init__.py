@@ -1,0 +1,34 @@
+"""fp64 CPU oracle for the verification step of speculative sampling.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or execute anything in
+this package: only the tests, the smoke check and the bench's CPU-baseline leg use it. It shares
+no code with the HIP library (no kernels, headers, tables or helpers); the seeded input
+generators in `synthetic/` are the only code both sides use.
+
+Modules
+  reference  vectorised NumPy oracle in float64 (greedy, sampling, outcome prediction,
+             hit check, decision margins and near-tie flags)
+  naive      the same rules as literal pure-Python loops (math.exp, running sums), used only to
+             cross-check `reference` on tiny inputs
+
+Sources (page titles and sections):
+  [SD]   "speculative decodingとは" (lotook.com): section "speculative decodingはどのような手順で
+         動くのか?" (the four-stage loop; stage 3 accept/reject, stage 4 residual resample and
+         bonus token), section "speculative decodingとKV cache、プロンプトキャッシュの関係は?"
+         (KV-cache rewind) and the FAQ entry on output quality (losslessness).
+  [SSD]  "Speculative Speculative Decoding (SSD)" (jiwasawa.github.io): section
+         "1. Outcome Prediction (The Saguaro Cache)".
+  [D3D]  "LLMの生成を5倍速くする「D3D」を図で読む" (animemo.app): sections "検証のしくみ①",
+         "検証のしくみ③", "検証のまとめ", "答え:ありうる結果すべてに、先回りして下書きする",
+         "ヒット", "ミス".
+
+Pin status: every function is pinned by a CPU test except the parts the pages give no formula
+for (Saguaro's fan-out optimiser and Saguaro sampling), which are not implemented here.
+"""
+from .reference import (NEAR_TIE, decode_logits, softmax, residual_weights, inverse_cdf,
+                        verify_sample_request, verify_greedy_request, predict_request,
+                        verify_sample, verify_greedy, predict_outcomes, outcome_hit)
+
+__all__ = ["NEAR_TIE", "decode_logits", "softmax", "residual_weights", "inverse_cdf",
+           "verify_sample_request", "verify_greedy_request", "predict_request", "verify_sample",
+           "verify_greedy", "predict_outcomes", "outcome_hit"]

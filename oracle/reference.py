@@ -1,0 +1,240 @@
+"""Vectorised fp64 oracle (test infrastructure only; see the package docstring).
+
+Notation (as on the pages): K drafts x_0..x_{K-1}; the target gives K+1 next-token rows, row k
+being its distribution for draft slot k and row K the extra row used when every draft is
+accepted; the draft gives one row per slot. p_k = softmax(l^t_k / T), q_k = softmax(l^d_k / T).
+m is the first rejected slot (0-based, so m drafts were accepted); tau = m + 1 tokens advance.
+
+Readings where the pages leave a step open:
+  * temperature: p = softmax(l / T); T = 0 is the greedy rule and has its own entry point;
+  * accept slot k iff u_k < r_k with r_k = 1 when p_k(x_k) >= q_k(x_k), else p/q, so a draft the
+    target likes at least as much is always kept whatever u_k in [0,1) is;
+  * the residual (or bonus) draw uses the one extra uniform u_K by inverse CDF: the smallest v
+    whose running sum C_v exceeds u_K * Z; if round-off leaves none, the last v of positive
+    weight; a zero-weight token is never drawn;
+  * a draft token outside [0,V), or (sampling) one whose draft logit is -inf, is a row error:
+    tau = -1, tokens all -1, kv unchanged, reported probabilities NaN;
+  * kv_out = kv_in + tau (the round advances the committed length by tau).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEAR_TIE = 1e-5  # decision margins below this are flagged near-ties
+
+
+# ----------------------------------------------------------------------------------------------
+# inputs
+def decode_logits(stored: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact promotion of stored logits to float64 (bf16 bit patterns or float32 values)."""
+    if dtype == "bf16":
+        bits = np.ascontiguousarray(stored, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.asarray(stored, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------------------------
+# building blocks
+def softmax(logits: np.ndarray, T: float) -> np.ndarray:
+    """Temperature softmax of one row: p_v = exp(l_v/T) / sum_w exp(l_w/T).
+
+    Evaluated with the row maximum subtracted (the same quantity, without overflow). Sampling
+    "at temperature" and greedy being "temperature zero" are how [SD] stage 3 and its results
+    table speak of T; the ratio form l/T is the plain reading.
+    """
+    z = np.asarray(logits, dtype=np.float64) / np.float64(T)
+    e = np.exp(z - np.max(z))
+    return e / np.sum(e)
+
+
+def residual_weights(p: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Residual weights max(0, p - q) at the first rejected slot ([SD] stage 4: the replacement
+    is drawn from a residual distribution adjusted by both models' probabilities)."""
+    return np.maximum(p - q, 0.0)
+
+
+def inverse_cdf(w: np.ndarray, u: float):
+    """Draw a token from weights w (unnormalised) with one uniform u in [0,1).
+
+    C is the running sum of w in token order (sequential float64), Z = C[V-1]; the token is the
+    smallest v with C_v > u*Z. If round-off leaves no such v, the last v with w_v > 0.
+    Returns (y, C, Z, t) with t = u*Z.
+    """
+    C = np.cumsum(w)
+    Z = float(C[-1])
+    t = float(u) * Z
+    above = np.nonzero(C > t)[0]
+    if above.size:
+        y = int(above[0])
+    else:
+        y = int(np.nonzero(w > 0)[0][-1])
+    return y, C, Z, t
+
+
+def _cdf_margin(C: np.ndarray, Z: float, t: float, y: int) -> float:
+    lo = float(C[y - 1]) if y > 0 else 0.0
+    return min(float(C[y]) - t, t - lo) / Z
+
+
+# ----------------------------------------------------------------------------------------------
+# one request
+def verify_sample_request(t_rows: np.ndarray, d_rows: np.ndarray, x, u, kv_in: int, T: float):
+    """Speculative-sampling verification of one request ([SD] stages 3 and 4).
+
+    t_rows [K+1,V], d_rows [K,V] float64 logits; x [K] draft tokens; u [K+1] uniforms; T > 0.
+    Returns a dict with tokens [K+1], tau, kv_out, p_x [K], q_x [K], m (first rejected slot or
+    K), y, resid_mass (Z), margin (smallest decision margin) and flagged.
+    """
+    K = len(x)
+    V = t_rows.shape[1]
+    x = [int(v) for v in x]
+    u = np.asarray(u, dtype=np.float64)
+    out = dict(tokens=np.full(K + 1, -1, np.int64), tau=-1, kv_out=int(kv_in),
+               p_x=np.full(K, np.nan), q_x=np.full(K, np.nan), m=-1, y=-1,
+               resid_mass=np.nan, margin=np.inf, flagged=False, row_error=False)
+
+    # a draft token must be a token the draft could have sampled
+    if any(v < 0 or v >= V for v in x) or any(np.isneginf(d_rows[k, x[k]]) for k in range(K)):
+        out["row_error"] = True
+        return out
+
+    p = [softmax(t_rows[k], T) for k in range(K + 1)]
+    q = [softmax(d_rows[k], T) for k in range(K)]
+    P = np.array([p[k][x[k]] for k in range(K)])
+    Q = np.array([q[k][x[k]] for k in range(K)])
+    out["p_x"], out["q_x"] = P, Q
+
+    # stage 3: left to right; p >= q always kept, otherwise kept with probability p/q
+    margins = []
+    m = K
+    for k in range(K):
+        r = 1.0 if P[k] >= Q[k] else P[k] / Q[k]
+        margins.append(abs(u[k] - r))
+        if not (u[k] < r):
+            m = k
+            break
+
+    # stage 4: residual at the first rejection, or the bonus row when all K drafts were kept
+    w = residual_weights(p[m], q[m]) if m < K else p[K]
+    if not np.sum(w) > 0.0:
+        w = p[m]        # cannot happen in exact arithmetic after a rejection; p_m as fallback
+    y, C, Z, t = inverse_cdf(w, u[K])
+    margins.append(_cdf_margin(C, Z, t, y))
+
+    tokens = np.full(K + 1, -1, np.int64)
+    tokens[:m] = x[:m]
+    tokens[m] = y
+    tau = m + 1
+    out.update(tokens=tokens, tau=tau, kv_out=int(kv_in) + tau, m=m, y=y, resid_mass=Z,
+               margin=float(min(margins)), flagged=bool(min(margins) < NEAR_TIE))
+    return out
+
+
+def verify_greedy_request(t_rows: np.ndarray, x, kv_in: int):
+    """Greedy verification of one request ([SD] stage 3 at temperature zero; [D3D] sections
+    "検証のしくみ③" and "検証のまとめ"): keep drafts left to right while each equals the target's
+    top choice for its slot; at the first mismatch place the target's own top choice and drop the
+    rest; if all K match, the extra row's top choice is appended. Ties go to the lowest id."""
+    K = len(x)
+    V = t_rows.shape[1]
+    x = [int(v) for v in x]
+    out = dict(tokens=np.full(K + 1, -1, np.int64), tau=-1, kv_out=int(kv_in), m=-1, y=-1,
+               g=None, row_error=False)
+    if any(v < 0 or v >= V for v in x):
+        out["row_error"] = True
+        return out
+    g = [int(np.argmax(t_rows[k])) for k in range(K + 1)]   # first maximum = lowest id
+    m = K
+    for k in range(K):
+        if x[k] != g[k]:
+            m = k
+            break
+    tokens = np.full(K + 1, -1, np.int64)
+    tokens[:m] = x[:m]
+    tokens[m] = g[m]
+    out.update(tokens=tokens, tau=m + 1, kv_out=int(kv_in) + m + 1, m=m, y=g[m], g=g)
+    return out
+
+
+def predict_request(d_rows: np.ndarray, F: int, T: float):
+    """Outcome keys of one request ([SSD] section "1. Outcome Prediction": the token placed at a
+    rejection is predicted from the draft's top logits).
+
+    keys[k, f] for slot k: the F token ids with the largest draft logits, ordered by logit
+    descending and id ascending. key_prob[k, f] = q_k(key) at T > 0; at T = 0 the argmax key gets
+    1 and the others 0.
+    """
+    K = d_rows.shape[0]
+    keys = np.argsort(-d_rows, axis=1, kind="stable")[:, :F]
+    if T > 0:
+        prob = np.stack([softmax(d_rows[k], T)[keys[k]] for k in range(K)])
+    else:
+        prob = np.zeros((K, F))
+        prob[:, 0] = 1.0
+    return keys.astype(np.int64), prob
+
+
+def outcome_hit(keys_row: np.ndarray, m: int, y: int, K: int, positions: int = None) -> bool:
+    """Whether a verification outcome (m drafts kept, token y placed at slot m) was predicted.
+
+    Hit iff the rejection happened at a slot that has keys (m < K, and m < `positions` when a
+    position limit is given) and y is among that slot's keys ([D3D] sections "ヒット" and "ミス":
+    a placed token outside the prepared candidates, or a rejection beyond the prepared slots, is a
+    miss). A round with every draft kept has no key here and counts as a miss.
+    """
+    limit = K if positions is None else min(K, positions)
+    if m < 0 or m >= limit:
+        return False
+    return bool(np.any(np.asarray(keys_row[m]) == y))
+
+
+# ----------------------------------------------------------------------------------------------
+# batches
+def _request_slices(n: int, requests):
+    return range(n) if requests is None else requests
+
+
+def verify_sample(target, draft, dtype, tokens, uniforms, kv_len, T, requests=None):
+    """Batch wrapper: returns arrays over the selected requests (all by default)."""
+    idx = list(_request_slices(target.shape[0], requests))
+    K = tokens.shape[1]
+    res = [verify_sample_request(decode_logits(target[b], dtype), decode_logits(draft[b], dtype),
+                                 tokens[b], np.asarray(uniforms[b], np.float64),
+                                 int(kv_len[b]), float(np.float32(T)))
+           for b in idx]
+    return _stack(res, idx, K, sample=True)
+
+
+def verify_greedy(target, dtype, tokens, kv_len, requests=None):
+    idx = list(_request_slices(target.shape[0], requests))
+    K = tokens.shape[1]
+    res = [verify_greedy_request(decode_logits(target[b], dtype), tokens[b], int(kv_len[b]))
+           for b in idx]
+    return _stack(res, idx, K, sample=False)
+
+
+def predict_outcomes(draft, dtype, F, T, requests=None):
+    idx = list(_request_slices(draft.shape[0], requests))
+    out = [predict_request(decode_logits(draft[b], dtype), F, float(np.float32(T))) for b in idx]
+    return dict(requests=np.array(idx), keys=np.stack([o[0] for o in out]),
+                key_prob=np.stack([o[1] for o in out]))
+
+
+def _stack(res, idx, K, sample):
+    d = dict(requests=np.array(idx),
+             tokens=np.stack([r["tokens"] for r in res]),
+             tau=np.array([r["tau"] for r in res]),
+             kv_out=np.array([r["kv_out"] for r in res]),
+             m=np.array([r["m"] for r in res]),
+             y=np.array([r["y"] for r in res]),
+             row_error=np.array([r["row_error"] for r in res]))
+    if sample:
+        d.update(p_x=np.stack([r["p_x"] for r in res]), q_x=np.stack([r["q_x"] for r in res]),
+                 margin=np.array([r["margin"] for r in res]),
+                 flagged=np.array([r["flagged"] for r in res]),
+                 resid_mass=np.array([r["resid_mass"] for r in res]))
+    else:
+        d.update(flagged=np.zeros(len(res), bool))
+    return d
