@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Bench of the speculative-sampling verification step on one MI355X.
+
+Workload (one "step"): one spec_verify_sample call over a full batch already resident in HBM,
+B=64 requests, K=4 drafts, V=128256, bf16 logits, T=0.7 (the C3 batched-serving workload:
+target N(0,3^2) + Zipf bias, draft noise std per request ~ U(0.3,2.0)). Four seeded input sets
+(591 MB) are rotated so the 256 MB Infinity Cache cannot serve a call from the previous one.
+
+Prints ONE JSON line on stdout: verified draft rows/s (B*K per call), the whole call's
+algorithmic HBM rate, the roofline of the dominant kernel (the streaming statistics kernel,
+timed with start/stop events on its own launches inside the timed region), and the fp64 oracle
+timed on this host's cores as a CPU baseline. Diagnostics go to stderr.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from synthetic import make_workload  # noqa: E402
+
+METRIC = "verified draft rows/sec and HBM GB/s (% of peak), B=64 K=4 V=128256 bf16"
+HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E, published
+CPU_POOL_CAP = 16          # host share of one GPU
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=4, help="rotated input sets")
+    ap.add_argument("--cpu-repeats", type=int, default=16,
+                    help="passes of the oracle over the 64 requests of set 0")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the greedy and outcome-key timings")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------------------ CPU baseline
+_WL = None
+
+
+def _oracle_requests(reqs):
+    import oracle
+    wl = _WL
+    oracle.verify_sample(wl.target, wl.draft, wl.dtype, wl.tokens, wl.uniforms, wl.kv_len, wl.T,
+                         requests=reqs)
+    return len(reqs)
+
+
+def cpu_baseline(wl, repeats):
+    """The fp64 oracle as it is, over a fork pool on this host's cores (before any GPU use)."""
+    import multiprocessing as mp
+    global _WL
+    _WL = wl
+    workers = max(1, min(CPU_POOL_CAP, len(os.sched_getaffinity(0))))
+    tasks = [b for _ in range(repeats) for b in range(wl.B)]
+    slices = [tasks[i::workers] for i in range(workers)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_requests, [[0]] * workers)          # warm the workers
+        t0 = time.perf_counter()
+        done = sum(pool.map(_oracle_requests, slices))
+        dt = time.perf_counter() - t0
+    rows = done * wl.K
+    return dict(value=rows / dt, unit="verified draft rows/s", cores=workers, kind="oracle",
+                sample=f"{repeats} passes over the {wl.B} requests of input set 0 "
+                       f"({done} request verifications, {rows} draft rows, fp64 NumPy oracle, "
+                       f"{dt:.2f} s wall on {workers} processes)")
+
+
+# ------------------------------------------------------------------------------ GPU
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build runs the verification step on a single "
+              "MI355X (requests shard across GPUs with no exchange; see the design notes). "
+              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    log(f"generating {args.sets} C3 input sets")
+    sets = [make_workload(3, r) for r in range(args.sets)]
+    wl0 = sets[0]
+    B, K, V = wl0.B, wl0.K, wl0.V
+    elem = wl0.elem_bytes
+    bytes_per_call = B * (2 * K + 1) * V * elem
+
+    cpu = None
+    if not args.no_cpu:
+        log("oracle CPU baseline")
+        cpu = cpu_baseline(wl0, args.cpu_repeats)
+        log(f"cpu: {cpu['value']:.1f} rows/s on {cpu['cores']} processes")
+
+    import torch
+    import speculative_decoding_verification_12_amd as sv
+    sv.load_library()
+    hip = sv.hip_runtime()
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"device {torch.cuda.get_device_name(0)}")
+
+    def upload(wl):
+        lg = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+        return dict(t=lg(wl.target), d=lg(wl.draft), x=torch.from_numpy(wl.tokens).to(dev),
+                    u=torch.from_numpy(wl.uniforms).to(dev), kv=torch.from_numpy(wl.kv_len).to(dev))
+
+    dsets = [upload(w) for w in sets]
+    ws = sv.new_workspace(B, K, V, 3)
+    out = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+               tau=torch.empty(B, dtype=torch.int32, device=dev),
+               kv_len=torch.empty(B, dtype=torch.int32, device=dev),
+               p=torch.empty((B, K), dtype=torch.float32, device=dev),
+               q=torch.empty((B, K), dtype=torch.float32, device=dev))
+    T = float(wl0.T)
+
+    def call(i, events=None):
+        s = dsets[i % len(dsets)]
+        sv.spec_verify_sample(s["t"], s["d"], s["x"], s["u"], s["kv"], T, ws, out=out,
+                              events=events)
+
+    # quick correctness check of what is timed (8 requests of set 0 against the oracle)
+    import oracle
+    call(0)
+    torch.cuda.synchronize()
+    ref = oracle.verify_sample(wl0.target, wl0.draft, wl0.dtype, wl0.tokens, wl0.uniforms,
+                               wl0.kv_len, wl0.T, requests=range(8))
+    got = out["tokens"][:8].cpu().numpy()
+    for i in range(8):
+        if not ref["flagged"][i] and not np.array_equal(got[i], ref["tokens"][i]):
+            raise SystemExit(f"bench output differs from the oracle at request {i}")
+
+    # events for the per-kernel timing: 4 per step
+    n_ev = 4 * args.steps
+    evs = (ctypes.c_void_p * n_ev)()
+    ev_base = ctypes.addressof(evs)
+    ev_size = ctypes.sizeof(ctypes.c_void_p)
+
+    def ev_ptr(i):
+        return ctypes.cast(ev_base + i * ev_size, ctypes.POINTER(ctypes.c_void_p))
+
+    for i in range(n_ev):
+        if hip.hipEventCreate(ev_ptr(i)) != 0:
+            raise SystemExit("hipEventCreate failed")
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, each one spec_verify_sample call (timed variant)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        call(i, events=ev_ptr(4 * i))
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / args.steps
+
+    def elapsed(a, b):
+        f = ctypes.c_float()
+        if hip.hipEventElapsedTime(ctypes.byref(f), evs[a], evs[b]) != 0:
+            raise SystemExit("hipEventElapsedTime failed")
+        return f.value
+
+    stats_ms = np.array([elapsed(4 * i, 4 * i + 1) for i in range(args.steps)])
+    draw_ms = np.array([elapsed(4 * i + 2, 4 * i + 3) for i in range(args.steps)])
+
+    # the same loop through the plain entry point (no events), for comparison
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        call(i)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_plain = start.elapsed_time(stop) / args.steps
+
+    # hot: one input set only (Infinity Cache may serve part of it)
+    start.record()
+    for i in range(args.steps):
+        call(0)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_hot = start.elapsed_time(stop) / args.steps
+
+    stats_avg_s = float(stats_ms.mean()) * 1e-3
+    achieved = bytes_per_call / stats_avg_s / 1e9
+    rows_per_s = B * K / (ms_per_step * 1e-3)
+    call_gbps = bytes_per_call / (ms_per_step * 1e-3) / 1e9
+
+    extra = dict(ms_per_step_plain_entry=round(ms_plain, 5), ms_per_step_hot_one_set=round(ms_hot, 5),
+                 wall_ms_per_step=round(wall / args.steps * 1e3, 5),
+                 stats_kernel_us=dict(mean=round(float(stats_ms.mean()) * 1e3, 3),
+                                      median=round(float(np.median(stats_ms)) * 1e3, 3),
+                                      p90=round(float(np.percentile(stats_ms, 90)) * 1e3, 3)),
+                 draw_kernel_us=dict(mean=round(float(draw_ms.mean()) * 1e3, 3),
+                                     median=round(float(np.median(draw_ms)) * 1e3, 3)),
+                 bytes_per_call=bytes_per_call,
+                 call_hbm_gbps=round(call_gbps, 1),
+                 call_pct_of_peak=round(100 * call_gbps / HBM_PEAK_GBPS, 2))
+
+    if not args.no_secondary:
+        extra.update(secondary(sv, torch, dev, hip, sets, dsets, ws, args))
+
+    for i in range(n_ev):
+        hip.hipEventDestroy(evs[i])
+
+    line = {
+        "metric": METRIC,
+        "value": round(rows_per_s, 1),
+        "unit": "verified draft rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "C3 batched serving: spec_verify_sample, B=64 K=4 V=128256 bf16 "
+                               "T=0.7, 4 rotated input sets",
+                   "B": B, "K": K, "V": V, "temperature": T, "input_sets": len(sets)},
+        "hbm_gbps": round(call_gbps, 1),
+        "pct_of_hbm_peak": round(100 * call_gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "sample_stats_kernel<bf16>",
+                     "bytes_per_launch": bytes_per_call,
+                     "avg_launch_us": round(stats_avg_s * 1e6, 3)},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def secondary(sv, torch, dev, hip, sets, dsets, ws, args):
+    """Greedy verification on C3 and outcome keys on C5 (F=3), events around each call."""
+    res = {}
+    wl0 = sets[0]
+    B, K, V = wl0.B, wl0.K, wl0.V
+    steps = max(20, args.steps // 2)
+    xg = [torch.from_numpy(make_workload(3, r, "greedy").tokens).to(dev) for r in range(len(sets))]
+    outg = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                tau=torch.empty(B, dtype=torch.int32, device=dev),
+                kv_len=torch.empty(B, dtype=torch.int32, device=dev))
+    for i in range(10):
+        s = dsets[i % len(dsets)]
+        sv.spec_verify_greedy(s["t"], xg[i % len(xg)], s["kv"], ws, out=outg)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        s = dsets[i % len(dsets)]
+        sv.spec_verify_greedy(s["t"], xg[i % len(xg)], s["kv"], ws, out=outg)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    gb = B * (K + 1) * V * 2
+    res["greedy_c3"] = dict(ms_per_call=round(ms, 5), rows_per_s=round(B * K / (ms * 1e-3), 1),
+                            hbm_gbps=round(gb / (ms * 1e-3) / 1e9, 1), bytes_per_call=gb)
+
+    log("C5 outcome keys")
+    c5 = [make_workload(5, r) for r in range(8)]
+    d5 = [torch.from_numpy(np.ascontiguousarray(w.draft).view(np.int16)).view(
+        torch.bfloat16).to(dev) for w in c5]
+    F = 3
+    outp = dict(keys=torch.empty((B, K, F), dtype=torch.int32, device=dev),
+                key_prob=torch.empty((B, K, F), dtype=torch.float32, device=dev))
+    for Tp in (1.0, 0.0):
+        for i in range(10):
+            sv.spec_predict_outcomes(d5[i % 8], F, Tp, ws, out=outp)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            sv.spec_predict_outcomes(d5[i % 8], F, Tp, ws, out=outp)
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / steps
+        pb = B * K * V * 2
+        res[f"predict_c5_T{Tp:g}"] = dict(ms_per_call=round(ms, 5),
+                                           keys_per_s=round(B * K * F / (ms * 1e-3), 1),
+                                           hbm_gbps=round(pb / (ms * 1e-3) / 1e9, 1),
+                                           bytes_per_call=pb)
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+/*
+ * spec_verify.h — C ABI of libspecverify.so: the target-side verification step of speculative
+ * decoding (speculative sampling) on an MI355X (gfx950) GPU.
+ *
+ * Sources (page titles and sections):
+ *   [SD]  "speculative decodingとは" (lotook.com), section "speculative decodingはどのような手順で
+ *         動くのか?": stage 2 (one target pass gives a distribution for every draft slot plus one
+ *         more), stage 3 (left-to-right accept/reject; argmax match at temperature zero, a token
+ *         the target likes at least as much always kept, otherwise kept by the probability
+ *         ratio), stage 4 (at the first mismatch m, resample from the residual of both models'
+ *         probabilities; if all K drafts are kept, draw a bonus token from the extra row);
+ *         section "speculative decodingとKV cache、プロンプトキャッシュの関係は?" (both KV caches
+ *         are rewound past the rejected entries).
+ *   [SSD] "Speculative Speculative Decoding (SSD)" (jiwasawa.github.io), section
+ *         "1. Outcome Prediction (The Saguaro Cache)": a verification outcome is (how many drafts
+ *         were kept, which token the target placed); the placed token is predicted from the
+ *         draft's top logits.
+ *   [D3D] "LLMの生成を5倍速くする「D3D」を図で読む" (animemo.app), sections "検証のしくみ①"
+ *         (row k of the target belongs to draft slot k; the row after the last draft is the
+ *         bonus row), "検証のしくみ③" and "検証のまとめ" (keep, discard from the first miss,
+ *         place the target's own token; tau = tokens advanced), "答え:…" (an outcome is the kept
+ *         count and the placed token).
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers on the current HIP device, row-major, contiguous:
+ *       target_logits [B, K+1, V]  row k is the target's distribution for draft slot k,
+ *                                  row K the extra (bonus) row;
+ *       draft_logits  [B, K,   V]  row k is the draft's distribution for slot k;
+ *       draft_tokens  [B, K] int32; uniforms [B, K+1] float32 in [0,1): uniforms[b][k] (k<K)
+ *       decides slot k, uniforms[b][K] drives the residual or bonus draw.
+ *     Logit element type is SPEC_F32 (float) or SPEC_BF16 (bfloat16 bit patterns, 2 bytes);
+ *     logit pointers must be aligned to their element size. Any V >= 2 is accepted.
+ *   - -inf logits are masked tokens (probability 0). NaN or +inf logits, or a row whose logits
+ *     are all -inf, give undefined (but in-bounds, terminating) results.
+ *   - The caller owns every buffer, including the workspace. The library allocates nothing and
+ *     keeps no mutable global state; calls only enqueue work on `stream` and return. Outputs
+ *     are valid after the stream is synchronised. Every element of every non-null output is
+ *     written.
+ *   - Workspace: size from spec_workspace_bytes(B,K,V,F) (one size serves all three entry
+ *     points), 256-byte aligned, zeroed once by spec_workspace_init before its first use. Each
+ *     call leaves it ready for the next one (the completion counters it holds are reset on the
+ *     device). One workspace must not be used by two calls that may run concurrently (two
+ *     streams, or two host threads on one stream without ordering): they would race.
+ *   - Errors found on the host are returned synchronously, before anything is enqueued:
+ *       SPEC_ERR_ARG         null required pointer, B < 1, K < 1 or K > SPEC_MAX_K, V < 2,
+ *                            F outside [1, min(V, SPEC_MAX_F)], misaligned logit pointer,
+ *                            or a launch grid that would exceed 2^31-1 blocks;
+ *       SPEC_ERR_DTYPE       dtype not SPEC_F32 / SPEC_BF16;
+ *       SPEC_ERR_TEMPERATURE sampling with T not finite or T <= 0 (or log2(e)/T not finite);
+ *                            greedy with T != 0; prediction with T < 0 or not finite;
+ *       SPEC_ERR_WORKSPACE   workspace null, smaller than spec_workspace_bytes, or not
+ *                            256-byte aligned;
+ *       SPEC_ERR_HIP         a launch failed (hipGetLastError after enqueueing).
+ *   - Errors in device data are reported per request ("row error"): a draft token outside
+ *     [0,V), or, when sampling, a draft token whose draft logit is -inf (it cannot be a sample
+ *     of the draft), make that request write tau = -1, tokens all -1, kv_out = kv_in, and NaN
+ *     probabilities.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_ABI_VERSION 1
+#define SPEC_MAX_K 64
+#define SPEC_MAX_F 16
+
+/* logit element types */
+#define SPEC_F32 0
+#define SPEC_BF16 1
+
+/* status codes */
+#define SPEC_OK 0
+#define SPEC_ERR_ARG (-1)
+#define SPEC_ERR_DTYPE (-2)
+#define SPEC_ERR_TEMPERATURE (-3)
+#define SPEC_ERR_WORKSPACE (-4)
+#define SPEC_ERR_HIP (-5)
+
+/* Returns SPEC_ABI_VERSION of the built library. */
+int spec_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* spec_status_string(int status);
+
+/* Workspace bytes needed by any entry point for these sizes (F is the largest fan-out that
+ * will be passed to spec_predict_outcomes; pass 1 if prediction is not used). Returns 0 when
+ * the sizes are invalid (same rules as SPEC_ERR_ARG). */
+size_t spec_workspace_bytes(int B, int K, int V, int F);
+
+/* Zeroes the workspace's completion counters on `stream` (one small kernel). Call once after
+ * allocating a workspace. */
+int spec_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Speculative-sampling verification at temperature T > 0 ([SD] stages 3-4; [D3D] 検証のまとめ).
+ *   p_k = softmax(target_logits[b,k,:] / T), q_k = softmax(draft_logits[b,k,:] / T).
+ *   Slots k = 0..K-1 in order: kept iff uniforms[b,k] < r_k, r_k = 1 if p_k(x_k) >= q_k(x_k),
+ *   else p_k(x_k)/q_k(x_k). m = first slot not kept (K if all kept).
+ *   Draw y with u = uniforms[b,K] by inverse CDF (smallest v whose running sum in token order
+ *   exceeds u * total) from w = max(0, p_m - q_m) if m < K, or w = p_K if m = K.
+ * Outputs (device):
+ *   out_tokens [B,K+1] int32   x_0..x_{m-1}, y, then -1 padding
+ *   out_tau    [B]     int32   m + 1 (tokens advanced this round)
+ *   out_kv_len [B]     int32   kv_len_in[b] + tau (nullable; kv_len_in may be NULL = 0)
+ *   out_p, out_q [B,K] float   p_k(x_k), q_k(x_k) for every slot (nullable)
+ * Inputs are read once in one streaming pass; the target and draft rows of slot m are read
+ * again by the draw (only the extra target row when every draft is kept). */
+int spec_verify_sample(const void* target_logits, const void* draft_logits, int dtype,
+                       const int32_t* draft_tokens, const float* uniforms,
+                       const int32_t* kv_len_in, int B, int K, int V, float temperature,
+                       int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len,
+                       float* out_p, float* out_q,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* spec_verify_sample with per-kernel timing, for profiling and the bench. `events` points to
+ * four caller-created hipEvent_t (timing enabled, none NULL, else SPEC_ERR_ARG): the runtime
+ * records events[0]/events[1] at the start/end of the streaming statistics kernel and
+ * events[2]/events[3] at the start/end of the draw kernel (hipExtLaunchKernelGGL). Results are
+ * identical to spec_verify_sample. */
+int spec_verify_sample_timed(const void* target_logits, const void* draft_logits, int dtype,
+                             const int32_t* draft_tokens, const float* uniforms,
+                             const int32_t* kv_len_in, int B, int K, int V, float temperature,
+                             int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len,
+                             float* out_p, float* out_q,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream,
+                             hipEvent_t* events);
+
+/* Greedy verification, temperature must be exactly 0 ([SD] stage 3 at temperature zero;
+ * [D3D] 検証のしくみ③, 検証のまとめ). g_k = argmax_v target_logits[b,k,v] (lowest v on ties);
+ * m = first k with draft_tokens[b,k] != g_k (K if none); y = g_m. Same outputs as
+ * spec_verify_sample without probabilities. Draft logits are not needed and not read. */
+int spec_verify_greedy(const void* target_logits, int dtype, const int32_t* draft_tokens,
+                       const int32_t* kv_len_in, int B, int K, int V, float temperature,
+                       int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Outcome-key prediction ([SSD] "1. Outcome Prediction"; [D3D] "答え:…").
+ * For every request b and slot k < K: out_keys[b,k,0..F-1] = the F token ids with the largest
+ * draft_logits[b,k,:], ordered by logit descending then id ascending; a key (k, t) predicts
+ * "k drafts kept, target places t". out_key_prob[b,k,f] (nullable) = q_k(key) at T > 0; at
+ * T = 0 it is 1 for the first key and 0 for the others. */
+int spec_predict_outcomes(const void* draft_logits, int dtype, int B, int K, int V, int F,
+                          float temperature, int32_t* out_keys, float* out_key_prob,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,217 @@
+"""ctypes binding over libspecverify.so (argument marshalling only).
+
+Every computation runs in the HIP library; this module only turns torch tensors into device
+pointers and the current HIP stream, calls the C entry point of the same name, and raises on a
+non-zero status. There is no fallback: if the library is not built, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
+
+SPEC_F32 = 0
+SPEC_BF16 = 1
+SPEC_MAX_K = 64
+SPEC_MAX_F = 16
+STATUS = {0: "SPEC_OK", -1: "SPEC_ERR_ARG", -2: "SPEC_ERR_DTYPE", -3: "SPEC_ERR_TEMPERATURE",
+          -4: "SPEC_ERR_WORKSPACE", -5: "SPEC_ERR_HIP"}
+
+EXPORTS = ("spec_abi_version", "spec_status_string", "spec_workspace_bytes",
+           "spec_workspace_init", "spec_verify_sample", "spec_verify_sample_timed",
+           "spec_verify_greedy", "spec_predict_outcomes")
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGNATURES = {
+    "spec_abi_version": (_i, []),
+    "spec_status_string": (ctypes.c_char_p, [_i]),
+    "spec_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "spec_workspace_init": (_i, [_vp, _sz, _vp]),
+    "spec_verify_sample": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _f,
+                                _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_sample_timed": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _f,
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "spec_verify_greedy": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _f,
+                                _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_predict_outcomes": (_i, [_vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
+}
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({message})")
+        self.status = status
+
+
+_LIB = None
+
+
+def hip_runtime_paths() -> list[str]:
+    """Paths of the HIP runtime libraries mapped into this process."""
+    with open("/proc/self/maps") as f:
+        return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+
+
+def hip_runtime() -> ctypes.CDLL:
+    """The process's (single) HIP runtime, for events and other plain HIP calls."""
+    load_library()
+    return ctypes.CDLL(hip_runtime_paths()[0])
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once) and declare the C signatures."""
+    global _LIB
+    if _LIB is not None and path == LIB_PATH:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m speculative_decoding_verification_12_amd.build`"
+            " (hipcc, gfx950). There is no CPU fallback.")
+    # torch ships its own HIP runtime. It has to be loaded first so that the library's
+    # dependency on libamdhip64.so.7 binds to that same instance; loading the library first
+    # would map a second runtime whose streams and pointers are foreign to torch's.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(path)
+    runtimes = hip_runtime_paths()
+    if len(runtimes) > 1:
+        raise RuntimeError(f"more than one HIP runtime mapped into the process: {runtimes}")
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path == LIB_PATH:
+        _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().spec_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise SpecVerifyError(fn, status, status_string(status))
+
+
+def workspace_bytes(B: int, K: int, V: int, F: int = 1) -> int:
+    return int(load_library().spec_workspace_bytes(B, K, V, F))
+
+
+# ------------------------------------------------------------------------------ torch marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device:
+        raise ValueError(f"{name}: expected {tuple(shape)} {dtype} on {device}, "
+                         f"got {tuple(t.shape)} {t.dtype} on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def new_workspace(B: int, K: int, V: int, F: int = 1, device="cuda"):
+    """Allocate and initialise a workspace tensor (uint8, 256-byte aligned by the allocator)."""
+    torch = _torch()
+    n = workspace_bytes(B, K, V, F)
+    if n == 0:
+        raise ValueError(f"invalid sizes B={B} K={K} V={V} F={F}")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    _check("spec_workspace_init",
+           load_library().spec_workspace_init(_ptr(ws), n, _stream(ws.device)))
+    return ws
+
+
+def spec_verify_sample(target, draft, draft_tokens, uniforms, kv_len, temperature, workspace,
+                       out=None, events=None):
+    """Speculative-sampling verification. Returns dict(tokens, tau, kv_len, p, q).
+
+    `events` (optional) is a ctypes array of four hipEvent_t handles; the call then goes through
+    spec_verify_sample_timed and the events bracket the two kernels."""
+    torch = _torch()
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    _need(target, "target_logits", (B, K + 1, V), target.dtype, dev)
+    _need(draft, "draft_logits", (B, K, V), target.dtype, dev)
+    _need(draft_tokens, "draft_tokens", (B, K), torch.int32, dev)
+    _need(uniforms, "uniforms", (B, K + 1), torch.float32, dev)
+    if kv_len is not None:
+        _need(kv_len, "kv_len", (B,), torch.int32, dev)
+    if out is None:
+        out = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                   tau=torch.empty(B, dtype=torch.int32, device=dev),
+                   kv_len=torch.empty(B, dtype=torch.int32, device=dev),
+                   p=torch.empty((B, K), dtype=torch.float32, device=dev),
+                   q=torch.empty((B, K), dtype=torch.float32, device=dev))
+    args = (_ptr(target), _ptr(draft), _dtype_code(target), _ptr(draft_tokens), _ptr(uniforms),
+            _ptr(kv_len), B, K, V, float(temperature), _ptr(out["tokens"]), _ptr(out["tau"]),
+            _ptr(out.get("kv_len")), _ptr(out.get("p")), _ptr(out.get("q")), _ptr(workspace),
+            workspace.numel(), _stream(dev))
+    lib = load_library()
+    if events is None:
+        _check("spec_verify_sample", lib.spec_verify_sample(*args))
+    else:
+        _check("spec_verify_sample_timed",
+               lib.spec_verify_sample_timed(*args, ctypes.cast(events, ctypes.c_void_p)))
+    return out
+
+
+def spec_verify_greedy(target, draft_tokens, kv_len, workspace, temperature=0.0, out=None):
+    """Greedy verification. Returns dict(tokens, tau, kv_len)."""
+    torch = _torch()
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    _need(target, "target_logits", (B, K + 1, V), target.dtype, dev)
+    _need(draft_tokens, "draft_tokens", (B, K), torch.int32, dev)
+    if kv_len is not None:
+        _need(kv_len, "kv_len", (B,), torch.int32, dev)
+    if out is None:
+        out = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                   tau=torch.empty(B, dtype=torch.int32, device=dev),
+                   kv_len=torch.empty(B, dtype=torch.int32, device=dev))
+    rc = load_library().spec_verify_greedy(
+        _ptr(target), _dtype_code(target), _ptr(draft_tokens), _ptr(kv_len), B, K, V,
+        float(temperature), _ptr(out["tokens"]), _ptr(out["tau"]), _ptr(out.get("kv_len")),
+        _ptr(workspace), workspace.numel(), _stream(dev))
+    _check("spec_verify_greedy", rc)
+    return out
+
+
+def spec_predict_outcomes(draft, F, temperature, workspace, out=None):
+    """Outcome keys. Returns dict(keys [B,K,F] int32, key_prob [B,K,F] float32)."""
+    torch = _torch()
+    B, K, V = draft.shape
+    dev = draft.device
+    _need(draft, "draft_logits", (B, K, V), draft.dtype, dev)
+    if out is None:
+        out = dict(keys=torch.empty((B, K, F), dtype=torch.int32, device=dev),
+                   key_prob=torch.empty((B, K, F), dtype=torch.float32, device=dev))
+    rc = load_library().spec_predict_outcomes(
+        _ptr(draft), _dtype_code(draft), B, K, V, int(F), float(temperature), _ptr(out["keys"]),
+        _ptr(out.get("key_prob")), _ptr(workspace), workspace.numel(), _stream(dev))
+    _check("spec_predict_outcomes", rc)
+    return out

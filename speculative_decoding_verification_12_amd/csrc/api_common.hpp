@@ -1,0 +1,56 @@
+// Host-side argument checks shared by the C-ABI entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "plan.hpp"
+#include "spec_verify.h"
+
+namespace sv {
+
+inline bool is_aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+inline int elems_per_vec(int dtype) { return dtype == SPEC_BF16 ? 8 : 4; }
+inline size_t elem_bytes(int dtype) { return dtype == SPEC_BF16 ? 2 : 4; }
+
+inline int check_dims(int B, int K, int V) {
+  if (B < 1 || K < 1 || K > SPEC_MAX_K || V < 2) return SPEC_ERR_ARG;
+  return SPEC_OK;
+}
+
+inline int check_dtype(int dtype) {
+  return (dtype == SPEC_F32 || dtype == SPEC_BF16) ? SPEC_OK : SPEC_ERR_DTYPE;
+}
+
+inline int check_logits(const void* p, int dtype) {
+  return (p != nullptr && is_aligned(p, elem_bytes(dtype))) ? SPEC_OK : SPEC_ERR_ARG;
+}
+
+inline int check_workspace(const void* ws, size_t bytes, int B, int K, int V, int F) {
+  if (ws == nullptr || !is_aligned(ws, 256) || bytes < ws_layout(B, K, V, F).total)
+    return SPEC_ERR_WORKSPACE;
+  return SPEC_OK;
+}
+
+inline bool grid_fits(size_t blocks) { return blocks >= 1 && blocks <= 0x7fffffffull; }
+
+// log2(e) / T, the factor that turns a logit into a base-2 exponent at temperature T
+inline float exp2_scale(float T) {
+  return static_cast<float>(1.4426950408889634074 / static_cast<double>(T));
+}
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+template <typename T>
+inline T* ws_ptr(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace sv

@@ -1,0 +1,143 @@
+// Chunk plans and workspace layout, shared by the host launchers and the kernels.
+//
+// A logit row of V elements is cut into chunks of `cv` 16-byte vectors; each chunk is one
+// workgroup's work item. The plan depends only on the sizes and the element size, so every row
+// of a launch has the same number of chunks (a row's own head/tail split can move its vector
+// count down by one, which only shortens its last chunk).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifndef __HIPCC__
+#define SV_HD
+#else
+#define SV_HD __host__ __device__
+#endif
+
+namespace sv {
+
+constexpr int kBlock = 256;            // threads per workgroup, every kernel
+constexpr int kVecPerThread = 4;       // 16-byte vectors a thread holds per pass
+constexpr int kPassVecs = kBlock * kVecPerThread;
+constexpr int kCUs = 256;              // MI355X compute units
+constexpr int kCounterStride = 64;     // words between arrival counters (256 bytes apart)
+
+// Streaming plan of one kernel: every row is cut into `nchunk` chunks of `cv` vectors (the last
+// one shorter); one workgroup per (row, chunk).
+struct KernelPlan {
+  int cv;
+  int nchunk;
+};
+
+SV_HD inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Chunking for `rows` rows of V elements, `epv` elements per 16-byte vector, for a kernel of
+// which `resident` workgroups fit on one CU at a time. Small chunks (one pass of the block,
+// 16 KiB of bf16) balance best when they make many rounds of workgroups; when they would not,
+// the rows are cut into as many equal chunks as fill the GPU once (down to one vector per
+// thread), so no partial second round of workgroups is left running alone and small batches
+// still spread over all CUs. `max_cv` caps the chunk (0 = no cap).
+SV_HD inline KernelPlan plan_rows(int rows, int V, int epv, int resident, int max_cv = 0) {
+  const int nvec = V / epv > 0 ? V / epv : 1;
+  const int cap = kCUs * resident;
+  int nchunk = ceil_div(nvec, kPassVecs);
+  if (static_cast<long long>(rows) * nchunk < 4ll * cap) {
+    const int fill = cap / rows;
+    const int finest = ceil_div(nvec, kBlock);   // one vector per thread
+    nchunk = fill < 1 ? 1 : (fill < finest ? fill : finest);
+  }
+  int cv = ceil_div(ceil_div(nvec, nchunk), kBlock) * kBlock;   // balanced, whole 256-vector steps
+  if (max_cv > 0 && cv > max_cv) cv = max_cv;
+  return KernelPlan{cv, ceil_div(nvec, cv)};
+}
+
+// workgroups per CU at once, from the compiler's resource report for gfx950
+constexpr int kStatsResident = 7;
+constexpr int kDrawResident = 8;
+constexpr int kGreedyResident = 8;
+constexpr int kPredictResident = 4;
+
+SV_HD inline KernelPlan stats_plan(int B, int K, int V, int epv) {
+  return plan_rows(B * (2 * K + 1), V, epv, kStatsResident);
+}
+SV_HD inline KernelPlan draw_plan(int B, int K, int V, int epv) {
+  (void)K;
+  return plan_rows(B, V, epv, kDrawResident);
+}
+SV_HD inline KernelPlan greedy_plan(int B, int K, int V, int epv) {
+  return plan_rows(B * (K + 1), V, epv, kGreedyResident);
+}
+// outcome keys keep a chunk in registers: one pass per chunk
+SV_HD inline KernelPlan predict_plan(int B, int K, int V, int epv) {
+  return plan_rows(B * K, V, epv, kPredictResident, kPassVecs);
+}
+
+// per-request state handed from the first sampling pass to the draw
+struct ReqState {
+  int m;          // first rejected slot (K when all kept), -1 for a row error
+  int pad;
+  float mc_t;     // fl32(M_t * c): reference exponent of the target row used by the draw
+  float inv_t;    // fl32(1 / S_t)
+  float mc_d;     // same for the draft row of slot m (unused when m == K)
+  float inv_d;
+};
+
+struct ArgPart {   // (value, index) partial of an argmax or top-F list
+  float v;
+  int i;
+};
+
+struct WsLayout {
+  size_t cnt_a;      // unsigned[max(B*K, B) * kCounterStride]: per-request or per-row counters
+  size_t cnt_b;      // unsigned[B * kCounterStride]: counters of the residual/bonus draw
+  size_t counters_end;
+  size_t state;      // ReqState[B]
+  size_t part_stats; // 8 B [B*(2K+1)*nchunk]: chunk (max, scaled sum)
+  size_t part_draw;  // 16 B [B*nchunk]: chunk (residual mass, target mass)
+  size_t part_greedy;// 8 B [B*(K+1)*nchunk]: chunk (max, lowest index)
+  size_t part_topf;  // 8 B [B*K*nchunk*F]: chunk top-F lists
+  size_t part_pstat; // 8 B [B*K*nchunk]
+  size_t total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+template <typename PlanFn>
+inline size_t max_chunks(PlanFn fn, int B, int K, int V) {
+  const int a = fn(B, K, V, 4).nchunk, b = fn(B, K, V, 8).nchunk;
+  return static_cast<size_t>(a > b ? a : b);
+}
+
+// Layout covering both element types.
+inline WsLayout ws_layout(int B, int K, int V, int F) {
+  const size_t b = static_cast<size_t>(B), k = static_cast<size_t>(K);
+  const size_t ns = max_chunks(stats_plan, B, K, V);
+  const size_t nd = max_chunks(draw_plan, B, K, V);
+  const size_t ng = max_chunks(greedy_plan, B, K, V);
+  const size_t np = max_chunks(predict_plan, B, K, V);
+  const size_t stride = kCounterStride;
+  WsLayout L;
+  size_t off = 0;
+  L.cnt_a = off;
+  off = align256(off + sizeof(unsigned) * stride * (b * k > b ? b * k : b));
+  L.cnt_b = off;
+  off = align256(off + sizeof(unsigned) * stride * b);
+  L.counters_end = off;
+  L.state = off;
+  off = align256(off + sizeof(ReqState) * b);
+  L.part_stats = off;
+  off = align256(off + 8 * b * (2 * k + 1) * ns);
+  L.part_draw = off;
+  off = align256(off + 16 * b * nd);
+  L.part_greedy = off;
+  off = align256(off + 8 * b * (k + 1) * ng);
+  L.part_topf = off;
+  off = align256(off + 8 * b * k * np * static_cast<size_t>(F));
+  L.part_pstat = off;
+  off = align256(off + 8 * b * k * np);
+  L.total = off;
+  return L;
+}
+
+}  // namespace sv
