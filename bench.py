@@ -50,7 +50,41 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the greedy and outcome-key timings")
+    ap.add_argument("--calib-mib", type=int, default=256,
+                    help="size of one plain device-to-device copy run before timing; under "
+                         "rocprofv3 --pmc its FETCH_SIZE/WRITE_SIZE calibrate the counters")
     return ap.parse_args()
+
+
+# ------------------------------------------------------------------------------ counter traffic
+COUNTERS_MD = os.path.join(ROOT, "profiles", "sample_verify_c3_hbm_counters.md")
+KERNEL_SOURCES = ("verify_sample.hip", "spec_common.hpp", "plan.hpp")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "speculative_decoding_verification_12_amd", "csrc", f),
+                  "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per launch of the statistics kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when that summary
+    was taken on other kernel sources."""
+    try:
+        with open(COUNTERS_MD) as fh:
+            for line in fh:
+                f = line.split()
+                if len(f) == 5 and f[0] == "traffic_bytes_per_launch" and \
+                        f[1] == "sample_stats_kernel" and f[3] == "source_sha256_16":
+                    return int(f[2]) if f[4] == kernel_source_hash() else None
+    except OSError:
+        return None
+    return None
 
 
 # ------------------------------------------------------------------------------ CPU baseline
@@ -127,6 +161,13 @@ def main():
                     u=torch.from_numpy(wl.uniforms).to(dev), kv=torch.from_numpy(wl.kv_len).to(dev))
 
     dsets = [upload(w) for w in sets]
+    if args.calib_mib > 0:   # plain copy of known size (reads and writes calib_mib MiB once)
+        src = torch.empty(args.calib_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     ws = sv.new_workspace(B, K, V, 3)
     out = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
                tau=torch.empty(B, dtype=torch.int32, device=dev),
@@ -168,17 +209,28 @@ def main():
         call(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps, each one spec_verify_sample call (timed variant)
+    # ---- timed region: K steps, each one spec_verify_sample call, events bracketing the loop
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        call(i, events=ev_ptr(4 * i))
+        call(i)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(stop) / args.steps
+
+    # ---- per-kernel durations: the same K steps through spec_verify_sample_timed, whose
+    # kernels are launched with start/stop events (this adds launch overhead between calls, so
+    # the loop's own time is not used for the headline)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        call(i, events=ev_ptr(4 * i))
+    stop.record()
+    torch.cuda.synchronize()
+    ms_timed_entry = start.elapsed_time(stop) / args.steps
 
     def elapsed(a, b):
         f = ctypes.c_float()
@@ -188,15 +240,6 @@ def main():
 
     stats_ms = np.array([elapsed(4 * i, 4 * i + 1) for i in range(args.steps)])
     draw_ms = np.array([elapsed(4 * i + 2, 4 * i + 3) for i in range(args.steps)])
-
-    # the same loop through the plain entry point (no events), for comparison
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(args.steps):
-        call(i)
-    stop.record()
-    torch.cuda.synchronize()
-    ms_plain = start.elapsed_time(stop) / args.steps
 
     # hot: one input set only (Infinity Cache may serve part of it)
     start.record()
@@ -211,7 +254,8 @@ def main():
     rows_per_s = B * K / (ms_per_step * 1e-3)
     call_gbps = bytes_per_call / (ms_per_step * 1e-3) / 1e9
 
-    extra = dict(ms_per_step_plain_entry=round(ms_plain, 5), ms_per_step_hot_one_set=round(ms_hot, 5),
+    extra = dict(ms_per_step_timed_entry=round(ms_timed_entry, 5),
+                 ms_per_step_hot_one_set=round(ms_hot, 5),
                  wall_ms_per_step=round(wall / args.steps * 1e3, 5),
                  stats_kernel_us=dict(mean=round(float(stats_ms.mean()) * 1e3, 3),
                                       median=round(float(np.median(stats_ms)) * 1e3, 3),
@@ -247,7 +291,8 @@ def main():
         "hbm_gbps": round(call_gbps, 1),
         "pct_of_hbm_peak": round(100 * call_gbps / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": counter_traffic(),
                      "kernel": "sample_stats_kernel<bf16>",
                      "bytes_per_launch": bytes_per_call,
                      "avg_launch_us": round(stats_avg_s * 1e6, 3)},

@@ -53,17 +53,21 @@ SV_HD inline KernelPlan plan_rows(int rows, int V, int epv, int resident, int ma
 }
 
 // workgroups per CU at once, from the compiler's resource report for gfx950
-constexpr int kStatsResident = 7;
-constexpr int kDrawResident = 8;
+constexpr int kStatsResident = 8;
 constexpr int kGreedyResident = 8;
 constexpr int kPredictResident = 4;
 
 SV_HD inline KernelPlan stats_plan(int B, int K, int V, int epv) {
   return plan_rows(B * (2 * K + 1), V, epv, kStatsResident);
 }
+// the draw re-reads one row (two when m < K) per request, kDrawVecs adjacent vectors per thread,
+// so its final search rescans one chunk with a single load per vector
+constexpr int kDrawVecs = 4;
 SV_HD inline KernelPlan draw_plan(int B, int K, int V, int epv) {
+  (void)B;
   (void)K;
-  return plan_rows(B, V, epv, kDrawResident);
+  const int nvec = V / epv > 0 ? V / epv : 1;
+  return KernelPlan{kBlock * kDrawVecs, ceil_div(nvec, kBlock * kDrawVecs)};
 }
 SV_HD inline KernelPlan greedy_plan(int B, int K, int V, int epv) {
   return plan_rows(B * (K + 1), V, epv, kGreedyResident);
@@ -73,7 +77,7 @@ SV_HD inline KernelPlan predict_plan(int B, int K, int V, int epv) {
   return plan_rows(B * K, V, epv, kPredictResident, kPassVecs);
 }
 
-// per-request state handed from the first sampling pass to the draw
+// per-request outcome of the slot scan, as the draw needs it
 struct ReqState {
   int m;          // first rejected slot (K when all kept), -1 for a row error
   int pad;
@@ -92,7 +96,7 @@ struct WsLayout {
   size_t cnt_a;      // unsigned[max(B*K, B) * kCounterStride]: per-request or per-row counters
   size_t cnt_b;      // unsigned[B * kCounterStride]: counters of the residual/bonus draw
   size_t counters_end;
-  size_t state;      // ReqState[B]
+  size_t gathered;   // float [B*2K]: target and draft logit of each slot's draft token
   size_t part_stats; // 8 B [B*(2K+1)*nchunk]: chunk (max, scaled sum)
   size_t part_draw;  // 16 B [B*nchunk]: chunk (residual mass, target mass)
   size_t part_greedy;// 8 B [B*(K+1)*nchunk]: chunk (max, lowest index)
@@ -124,8 +128,8 @@ inline WsLayout ws_layout(int B, int K, int V, int F) {
   L.cnt_b = off;
   off = align256(off + sizeof(unsigned) * stride * b);
   L.counters_end = off;
-  L.state = off;
-  off = align256(off + sizeof(ReqState) * b);
+  L.gathered = off;
+  off = align256(off + sizeof(float) * 2 * b * k);
   L.part_stats = off;
   off = align256(off + 8 * b * (2 * k + 1) * ns);
   L.part_draw = off;

@@ -133,6 +133,17 @@ __device__ __forceinline__ int wave_min(int v) {
   return v;
 }
 
+// reductions inside aligned segments of `width` lanes (a power of two <= 64)
+__device__ __forceinline__ float seg_max(float v, int width) {
+  for (int o = width / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ double seg_sum(double v, int width) {
+  for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
 // (value, index) ordered by value descending, then index ascending
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
@@ -169,6 +180,16 @@ __device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
 // small workgroups.
 __device__ __forceinline__ void store_coherent(void* p, uint64_t v) {
   __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_coherent_f32(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
 __device__ __forceinline__ uint64_t load_coherent(const void* p) {

@@ -8,16 +8,20 @@
 // every draft was kept; tau = m + 1 and the KV length advances by tau.
 //
 // Two launches, both HBM-streaming, no matrix cores (nothing here is a contraction):
-//  1. sample_stats_kernel: one workgroup per (request, row, chunk of 16-byte vectors).
-//     Each thread keeps a running max m and a sum of 2^(l*c - fl(m*c)), c = log2(e)/T, with
-//     one hardware exp2 per element; wave butterflies and LDS reduce to the chunk's (M, S).
-//     The last workgroup of a request to finish (device-scope arrival counter) merges its
-//     2K+1 rows in float64, evaluates every slot's log-ratio in float64, finds the first
-//     rejection with a wave ballot, and writes tau, kv, the kept tokens and p_k(x_k), q_k(x_k).
-//  2. sample_draw_kernel: one workgroup per (request, chunk) re-reads row m of the target (and
-//     of the draft when m < K), sums the draw weights per chunk in float64; the request's last
-//     workgroup walks the chunk masses, rescans the one chunk that holds u*Z with a block
-//     prefix sum, and writes the drawn token.
+//  1. sample_stats_kernel: one workgroup per (request, row, chunk of 16-byte vectors). Each
+//     thread keeps a running max m and a sum of 2^(l*c - fl(m*c)), c = log2(e)/T, with one
+//     hardware exp2 per element; wave butterflies and LDS reduce to the chunk's (M, S), written
+//     with a plain store. The workgroup whose chunk holds a slot's draft token also records
+//     that token's logit. No workgroup waits on another: the kernel boundary is the only
+//     synchronisation.
+//  2. sample_draw_kernel: one workgroup per (request, chunk of 1024 vectors). Each first merges
+//     its request's chunk statistics (a few hundred bytes, identical in every workgroup of the
+//     request), evaluates every slot's log-ratio in float64 and finds the first rejection m
+//     with a wave ballot; chunk 0 writes tau, kv, the kept tokens and p_k(x_k), q_k(x_k). Then
+//     it re-reads its chunk of row m of the target (and of the draft when m < K) and sums the
+//     draw weights in float64. The request's last workgroup to arrive (device-scope counter)
+//     finds the chunk that holds u*Z with one wave-wide prefix scan, rescans that chunk with a
+//     block prefix sum and writes the drawn token.
 #include <hip/hip_ext.h>
 
 #include "api_common.hpp"
@@ -115,129 +119,37 @@ __device__ __forceinline__ const TIn* slot_row(const TIn* tgt, const TIn* drf, i
 template <typename TIn>
 __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
     const TIn* __restrict__ tgt, const TIn* __restrict__ drf, const int32_t* __restrict__ xtok,
-    const float* __restrict__ uni, const int32_t* __restrict__ kv_in, int K, int V, float c,
-    int nchunk, int cv, float2* __restrict__ part, unsigned* __restrict__ cnt_base,
-    ReqState* __restrict__ state, int32_t* __restrict__ out_tok, int32_t* __restrict__ out_tau,
-    int32_t* __restrict__ out_kv, float* __restrict__ out_p, float* __restrict__ out_q) {
+    int K, int V, float c, int nchunk, int cv, float2* __restrict__ part,
+    float* __restrict__ gath) {
+  using E = Elem<TIn>;
+  constexpr int N = E::N;
   __shared__ float sm[kWaves], ss[kWaves];
-  __shared__ int s_flag;
-  __shared__ float row_m[2 * SPEC_MAX_K + 1];
-  __shared__ double row_s[2 * SPEC_MAX_K + 1];
 
   const int rows = 2 * K + 1;
   const int ch = blockIdx.x % nchunk;
   const int rb = blockIdx.x / nchunk;   // request-major (request, row) index
   const int r = rb % rows;
   const int b = rb / rows;
-  unsigned* cnt = cnt_base + static_cast<size_t>(b) * kCounterStride;
 
   const TIn* row = slot_row(tgt, drf, b, r, K, V);
   const RowSpan sp = row_span(row, V);
   const ChunkRange cr = chunk_range(sp, ch, nchunk, cv);
+
+  // The workgroup whose chunk holds the slot's draft token also reads that token's logit, so
+  // the merge finds it without another dependent load. Rows 0..K-1 are target slots, K+1..2K
+  // draft slots; row K (the extra target row) has no draft token.
+  const int slot = r < K ? r : r - K - 1;
+  if (r != K && threadIdx.x == 0) {
+    const int x = xtok[static_cast<size_t>(b) * K + slot];
+    const int lo = cr.first ? 0 : sp.head + cr.vbeg * N;
+    const int hi = cr.last ? V : sp.head + cr.vend * N;
+    if (x >= lo && x < hi) gath[static_cast<size_t>(b) * 2 * K + (r < K ? slot : K + slot)] = E::one(row, x);
+  }
+
   float m, s, M, S;
   thread_chunk_stats(row, sp, cr, V, c, m, s);
   block_stats(m, s, c, sm, ss, M, S);
-  if (threadIdx.x == 0) store_coherent(&part[static_cast<size_t>(rb) * nchunk + ch], pack2(M, S));
-  if (!arrive_last(cnt, static_cast<unsigned>(rows * nchunk), &s_flag)) return;
-
-  // ---- last workgroup of request b: merge the chunks of every row in float64
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  for (int rr = w; rr < rows; rr += kWaves) {
-    const float2* pr = part + (static_cast<size_t>(b) * rows + rr) * nchunk;
-    // at most a few chunks per lane: keep them in registers between the two passes
-    constexpr int kHeld = 4;
-    float hm[kHeld], hs[kHeld];
-    float lm = -INFINITY;
-#pragma unroll
-    for (int h = 0; h < kHeld; ++h) {
-      const int j = lane + h * kWave;
-      hm[h] = -INFINITY;
-      hs[h] = 0.f;
-      if (j < nchunk) {
-        const uint64_t q = load_coherent(&pr[j]);
-        hm[h] = lo_float(q);
-        hs[h] = hi_float(q);
-      }
-      lm = fmaxf(lm, hm[h]);
-    }
-    for (int j = lane + kHeld * kWave; j < nchunk; j += kWave)
-      lm = fmaxf(lm, lo_float(load_coherent(&pr[j])));
-    const float Mr = wave_max(lm);
-    const float mc = Mr * c;
-    double ls = 0.0;
-#pragma unroll
-    for (int h = 0; h < kHeld; ++h)
-      if (hm[h] > -INFINITY) {
-        const float qc = hm[h] * c;
-        ls += static_cast<double>(hs[h]) * exp2(static_cast<double>(qc) - static_cast<double>(mc));
-      }
-    for (int j = lane + kHeld * kWave; j < nchunk; j += kWave) {
-      const uint64_t q = load_coherent(&pr[j]);
-      if (lo_float(q) > -INFINITY) {
-        const float qc = lo_float(q) * c;
-        ls += static_cast<double>(hi_float(q)) *
-              exp2(static_cast<double>(qc) - static_cast<double>(mc));
-      }
-    }
-    const double Sr = wave_sum(ls);
-    if (lane == 0) {
-      row_m[rr] = Mr;
-      row_s[rr] = Sr;
-    }
-  }
-  __syncthreads();
-  if (w != 0) return;
-
-  // ---- slot scan: lane k evaluates slot k; the first rejection comes from a ballot
-  const int k = lane;
-  const bool valid = k < K;
-  int xk = -1;
-  bool bad = false, keep = true;
-  double lp = 0.0, lq = 0.0;
-  if (valid) {
-    xk = xtok[static_cast<size_t>(b) * K + k];
-    bad = xk < 0 || xk >= V;
-    if (!bad) {
-      const float lt = Elem<TIn>::one(slot_row(tgt, drf, b, k, K, V), xk);
-      const float ld = Elem<TIn>::one(slot_row(tgt, drf, b, K + 1 + k, K, V), xk);
-      if (ld == -INFINITY) {
-        bad = true;   // a draft token must be a possible sample of the draft
-      } else {
-        const float mct = row_m[k] * c, mcd = row_m[K + 1 + k] * c;
-        lp = kLn2 * (static_cast<double>(lt) * c - static_cast<double>(mct)) - log(row_s[k]);
-        lq = kLn2 * (static_cast<double>(ld) * c - static_cast<double>(mcd)) -
-             log(row_s[K + 1 + k]);
-        // kept iff u < min(1, p/q); p >= q is kept for every u in [0,1)
-        keep = (lp >= lq) || (static_cast<double>(uni[static_cast<size_t>(b) * (K + 1) + k]) <
-                              exp(lp - lq));
-      }
-    }
-  }
-  const bool err = __ballot(bad) != 0ull;
-  const unsigned long long rej = __ballot(valid && !keep);
-  const int mm = rej ? (__ffsll(static_cast<long long>(rej)) - 1) : K;
-
-  if (valid) {
-    const size_t o = static_cast<size_t>(b) * K + k;
-    if (out_p) out_p[o] = err ? NAN : static_cast<float>(exp(lp));
-    if (out_q) out_q[o] = err ? NAN : static_cast<float>(exp(lq));
-  }
-  for (int j = lane; j <= K; j += kWave)   // slot m itself is written by the draw
-    out_tok[static_cast<size_t>(b) * (K + 1) + j] = (!err && j < mm) ? xk : -1;
-  if (lane == 0) {
-    const int kv0 = kv_in ? kv_in[b] : 0;
-    out_tau[b] = err ? -1 : mm + 1;
-    if (out_kv) out_kv[b] = err ? kv0 : kv0 + mm + 1;
-    ReqState st;
-    st.m = err ? -1 : mm;
-    st.pad = 0;
-    st.mc_t = row_m[mm] * c;
-    st.inv_t = static_cast<float>(1.0 / row_s[mm]);
-    st.mc_d = mm < K ? row_m[K + 1 + mm] * c : 0.f;
-    st.inv_d = mm < K ? static_cast<float>(1.0 / row_s[K + 1 + mm]) : 0.f;
-    state[b] = st;
-    reset_counter(cnt);
-  }
+  if (threadIdx.x == 0) part[static_cast<size_t>(rb) * nchunk + ch] = make_float2(M, S);
 }
 
 // ------------------------------------------------------------------------------ draw
@@ -319,22 +231,126 @@ __device__ __forceinline__ void block_scan(double x, double* s_wave, double& inc
   __syncthreads();
 }
 
+// Chunks of at most kBlock * kDrawVecs vectors (see draw_plan).
 template <typename TIn>
 __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
-    const TIn* __restrict__ tgt, const TIn* __restrict__ drf, const float* __restrict__ uni,
-    int K, int V, float c, int nchunk, int cv, const ReqState* __restrict__ state,
-    double2* __restrict__ part, unsigned* __restrict__ cnt_base, int32_t* __restrict__ out_tok) {
+    const TIn* __restrict__ tgt, const TIn* __restrict__ drf, const int32_t* __restrict__ xtok,
+    const float* __restrict__ uni, const int32_t* __restrict__ kv_in, int K, int V, float c,
+    int nchunk_s, const float2* __restrict__ part_s, const float* __restrict__ gath,
+    int nchunk, int cv, double2* __restrict__ part, unsigned* __restrict__ cnt_base,
+    int32_t* __restrict__ out_tok, int32_t* __restrict__ out_tau, int32_t* __restrict__ out_kv,
+    float* __restrict__ out_p, float* __restrict__ out_q) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
   __shared__ double s_a[kWaves], s_b[kWaves];
   __shared__ int s_i[kWaves];
   __shared__ int s_flag, s_cs, s_usep, s_y, s_first;
   __shared__ double s_cum, s_t;
+  __shared__ float row_m[2 * SPEC_MAX_K + 1];
+  __shared__ double row_s[2 * SPEC_MAX_K + 1];
+  __shared__ ReqState s_st;
 
   const int b = blockIdx.x / nchunk;
   const int ch = blockIdx.x % nchunk;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  const ReqState st = state[b];
+  const int rows = 2 * K + 1;
+
+  // ---- merge the statistics pass of request b (every workgroup of b does the same, bit for
+  // bit): row (max, sum) in fp32/fp64, slot log-ratios in fp64, first rejection by ballot
+  {
+    const bool valid = w == 0 && lane < K;
+    int xk = 0;
+    float lt = 0.f, ld = 0.f, uk = 0.f;
+    if (valid) {
+      xk = xtok[static_cast<size_t>(b) * K + lane];
+      uk = uni[static_cast<size_t>(b) * (K + 1) + lane];
+      lt = gath[static_cast<size_t>(b) * 2 * K + lane];
+      ld = gath[static_cast<size_t>(b) * 2 * K + K + lane];
+    }
+    const int kv0 = (ch == 0 && tid == 0 && kv_in) ? kv_in[b] : 0;
+    // Rows are merged in segments of W lanes (W = nchunk_s rounded up to a power of two, at
+    // most 64), 64/W rows per wave, so one pass over the block issues every partial load at
+    // once. Lanes past nchunk_s (or past the last row) carry (-inf, 0).
+    int W = 1;
+    while (W < nchunk_s && W < kWave) W <<= 1;
+    const int per_wave = kWave / W, g = lane / W, i = lane % W;
+    for (int base = 0; base < rows; base += kWaves * per_wave) {
+      const int rr = base + w * per_wave + g;
+      const float2* pr = part_s + (static_cast<size_t>(b) * rows + (rr < rows ? rr : 0)) * nchunk_s;
+      constexpr int kHeld = 4;   // chunks a lane keeps in registers between the two passes
+      float hm[kHeld], hs[kHeld];
+      float lm = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < kHeld; ++h) {
+        const int j = i + h * W;
+        const float2 q = (rr < rows && j < nchunk_s) ? pr[j] : make_float2(-INFINITY, 0.f);
+        hm[h] = q.x;
+        hs[h] = q.y;
+        lm = fmaxf(lm, hm[h]);
+      }
+      if (rr < rows)
+        for (int j = i + kHeld * W; j < nchunk_s; j += W) lm = fmaxf(lm, pr[j].x);
+      const float Mr = seg_max(lm, W);
+      const float mc = Mr * c;
+      double ls = 0.0;
+#pragma unroll
+      for (int h = 0; h < kHeld; ++h)
+        if (hm[h] > -INFINITY) ls += static_cast<double>(hs[h]) * fast_exp2(hm[h] * c - mc);
+      if (rr < rows)
+        for (int j = i + kHeld * W; j < nchunk_s; j += W) {
+          const float2 q = pr[j];
+          if (q.x > -INFINITY) ls += static_cast<double>(q.y) * fast_exp2(q.x * c - mc);
+        }
+      const double Sr = seg_sum(ls, W);
+      if (i == 0 && rr < rows) {
+        row_m[rr] = Mr;
+        row_s[rr] = Sr;
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      // a draft token must be a token the draft could have sampled
+      const bool bad = valid && (xk < 0 || xk >= V || ld == -INFINITY);
+      bool keep = true;
+      double lp = 0.0, lq = 0.0;
+      if (valid && !bad) {
+        const float mct = row_m[lane] * c, mcd = row_m[K + 1 + lane] * c;
+        lp = kLn2 * (static_cast<double>(lt) * c - static_cast<double>(mct)) - log(row_s[lane]);
+        lq = kLn2 * (static_cast<double>(ld) * c - static_cast<double>(mcd)) -
+             log(row_s[K + 1 + lane]);
+        // kept iff u < min(1, p/q); p >= q is kept for every u in [0,1)
+        keep = (lp >= lq) || (static_cast<double>(uk) < exp(lp - lq));
+      }
+      const bool err = __ballot(bad) != 0ull;
+      const unsigned long long rej = __ballot(valid && !keep);
+      const int mm = rej ? (__ffsll(static_cast<long long>(rej)) - 1) : K;
+      if (ch == 0) {   // one workgroup of the request writes everything but the drawn token
+        if (valid) {
+          const size_t o = static_cast<size_t>(b) * K + lane;
+          if (out_p) out_p[o] = err ? NAN : static_cast<float>(exp(lp));
+          if (out_q) out_q[o] = err ? NAN : static_cast<float>(exp(lq));
+        }
+        for (int j = lane; j <= K; j += kWave)
+          if (err || j != mm) out_tok[static_cast<size_t>(b) * (K + 1) + j] = (!err && j < mm) ? xk : -1;
+        if (lane == 0) {
+          out_tau[b] = err ? -1 : mm + 1;
+          if (out_kv) out_kv[b] = err ? kv0 : kv0 + mm + 1;
+        }
+      }
+      if (lane == 0) {
+        ReqState st;
+        st.m = err ? -1 : mm;
+        st.pad = 0;
+        st.mc_t = row_m[mm] * c;
+        st.inv_t = static_cast<float>(1.0 / row_s[mm]);
+        st.mc_d = mm < K ? row_m[K + 1 + mm] * c : 0.f;
+        st.inv_d = mm < K ? static_cast<float>(1.0 / row_s[K + 1 + mm]) : 0.f;
+        s_st = st;
+      }
+    }
+    __syncthreads();
+  }
+  const ReqState st = s_st;
   if (st.m < 0) return;   // row error: nothing to draw (every workgroup of b agrees)
   unsigned* cnt = cnt_base + static_cast<size_t>(b) * kCounterStride;
 
@@ -345,9 +361,17 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
   R.sp = row_span(R.t, V);
   R.d_aligned = row_span(R.d, V).head == R.sp.head;
 
-  // ---- chunk masses: sum of w (draw weights) and of p (fallback weights)
+  // ---- chunk masses: sum of w (draw weights) and of p (fallback weights). Thread t owns the
+  // kDrawVecs adjacent vectors vbeg + t*kDrawVecs + i, plus head (first chunk) or tail (last
+  // chunk) element t.
   {
     const ChunkRange cr = chunk_range(R.sp, ch, nchunk, cv);
+    uint4 qt[kDrawVecs], qd[kDrawVecs];
+#pragma unroll
+    for (int i = 0; i < kDrawVecs; ++i) {
+      const int v = cr.vbeg + tid * kDrawVecs + i;
+      load_pair(R, v, v < cr.vend, qt[i], qd[i]);
+    }
     double rs = 0.0, ps = 0.0;
     float p;
     if (cr.first && tid < R.sp.head) {
@@ -358,30 +382,22 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       rs += weight_one(R, st, c, R.sp.tail + tid, false, p);
       ps += p;
     }
-    for (int base = cr.vbeg; base < cr.vend; base += kPassVecs) {
-      uint4 qt[kVecPerThread], qd[kVecPerThread];
+    float ws = 0.f, pss = 0.f;
 #pragma unroll
-      for (int i = 0; i < kVecPerThread; ++i) {
-        const int v = base + i * kBlock + tid;
-        load_pair(R, v, v < cr.vend, qt[i], qd[i]);
-      }
+    for (int i = 0; i < kDrawVecs; ++i) {
+      const int v = cr.vbeg + tid * kDrawVecs + i;
+      if (v < cr.vend) {
+        float wv[N], pv[N];
+        weight_group(R, st, c, qt[i], qd[i], v, false, wv, pv);
 #pragma unroll
-      for (int i = 0; i < kVecPerThread; ++i) {
-        const int v = base + i * kBlock + tid;
-        if (v < cr.vend) {
-          float wv[N], pv[N];
-          weight_group(R, st, c, qt[i], qd[i], v, false, wv, pv);
-          float ws = 0.f, pss = 0.f;
-#pragma unroll
-          for (int j = 0; j < N; ++j) {
-            ws += wv[j];
-            pss += pv[j];
-          }
-          rs += ws;
-          ps += pss;
+        for (int j = 0; j < N; ++j) {
+          ws += wv[j];
+          pss += pv[j];
         }
       }
     }
+    rs += ws;
+    ps += pss;
     rs = wave_sum(rs);
     ps = wave_sum(ps);
     if (lane == 0) {
@@ -402,48 +418,77 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
   }
   if (!arrive_last(cnt, static_cast<unsigned>(nchunk), &s_flag)) return;
 
-  // ---- last workgroup of request b: find the chunk holding u*Z, then the token inside it
-  const double2* pr = part + static_cast<size_t>(b) * nchunk;
-  auto mass = [&](int j, bool p_mass) {
-    return bits_d(load_coherent(p_mass ? &pr[j].y : &pr[j].x));
-  };
-  if (tid == 0) {
-    double Z = 0.0;
-    for (int j = 0; j < nchunk; ++j) Z += mass(j, false);
-    const int usep = (Z > 0.0) ? 0 : 1;
-    if (usep) {
-      Z = 0.0;
-      for (int j = 0; j < nchunk; ++j) Z += mass(j, true);
+  // ---- last workgroup of request b: find the chunk holding u*Z with one wave-wide scan
+  if (w == 0) {
+    const double u = static_cast<double>(uni[static_cast<size_t>(b) * (K + 1) + K]);
+    const double2* pr = part + static_cast<size_t>(b) * nchunk;
+    const int per = (nchunk + kWave - 1) / kWave;   // lane l owns chunks [l*per, l*per + per)
+    const int j0 = min(lane * per, nchunk), j1 = min(j0 + per, nchunk);
+    double rl = 0.0, pl = 0.0;
+    int lastpos_r = -1, lastpos_p = -1;
+    for (int j = j0; j < j1; ++j) {
+      const double rj = bits_d(load_coherent(&pr[j].x));
+      const double pj = bits_d(load_coherent(&pr[j].y));
+      rl += rj;
+      pl += pj;
+      if (rj > 0.0) lastpos_r = j;
+      if (pj > 0.0) lastpos_p = j;
     }
-    const double t = static_cast<double>(uni[static_cast<size_t>(b) * (K + 1) + K]) * Z;
-    double cum = 0.0;
+    const double ri = wave_inclusive_scan(rl, lane), pi = wave_inclusive_scan(pl, lane);
+    const double rz = __shfl(ri, kWave - 1, kWave);
+    const bool usep = !(rz > 0.0);   // no residual mass left by round-off: draw from p
+    const double incl = usep ? pi : ri;
+    const double Z = usep ? __shfl(pi, kWave - 1, kWave) : rz;
+    const double t = u * Z;
+    double excl = __shfl_up(incl, 1, kWave);
+    if (lane == 0) excl = 0.0;
+    const unsigned long long cross = __ballot(incl > t);
     int cs = -1;
-    for (int j = 0; j < nchunk; ++j) {
-      const double mj = mass(j, usep != 0);
-      if (cum + mj > t) {
-        cs = j;
-        break;
+    double cum = 0.0;
+    if (cross) {
+      const int L = __ffsll(static_cast<long long>(cross)) - 1;
+      if (lane == L) {
+        cum = excl;
+        for (int j = j0; j < j1; ++j) {
+          const double mj = bits_d(load_coherent(usep ? &pr[j].y : &pr[j].x));
+          if (cum + mj > t) {
+            cs = j;
+            break;
+          }
+          cum += mj;
+        }
+        if (cs < 0) cs = usep ? lastpos_p : lastpos_r;   // round-off inside this lane's chunks
+        if (cs < 0) cs = j1 - 1;
       }
-      cum += mj;
+      cs = __shfl(cs, L, kWave);
+      cum = __shfl(cum, L, kWave);
+    } else {   // round-off: the last chunk with positive mass (the chunk scan falls back too)
+      const int lp = wave_max(usep ? lastpos_p : lastpos_r);
+      cs = lp >= 0 ? lp : nchunk - 1;
     }
-    if (cs < 0) {   // round-off: the last chunk with positive mass (chunk scan falls back too)
-      cs = nchunk - 1;
-      for (int j = 0; j < nchunk; ++j)
-        if (mass(j, usep != 0) > 0.0) cs = j;
+    if (lane == 0) {
+      s_cs = cs;
+      s_usep = usep ? 1 : 0;
+      s_cum = cum;
+      s_t = t;
+      s_y = -1;
     }
-    s_cs = cs;
-    s_usep = usep;
-    s_cum = cum;
-    s_t = t;
-    s_y = -1;
   }
   __syncthreads();
+
+  // ---- rescan the chosen chunk in token order (thread t: vectors t*kDrawVecs .. +kDrawVecs-1)
   const bool use_p = s_usep != 0;
   const double t = s_t;
   const ChunkRange cr = chunk_range(R.sp, s_cs, nchunk, cv);
+  uint4 qt[kDrawVecs], qd[kDrawVecs];
+#pragma unroll
+  for (int i = 0; i < kDrawVecs; ++i) {
+    const int v = cr.vbeg + tid * kDrawVecs + i;
+    load_pair(R, v, v < cr.vend, qt[i], qd[i]);
+  }
   int lastpos = -1;   // last token of positive weight this thread saw (round-off fallback)
 
-  if (cr.first && tid == 0) {   // head elements, in token order
+  if (cr.first && tid == 0) {   // head elements come first
     double cum = s_cum;
     float p;
     for (int e = 0; e < R.sp.head; ++e) {
@@ -455,28 +500,30 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     s_cum = cum;
   }
   __syncthreads();
-
   double cum = s_cum;
-  for (int base = cr.vbeg; base < cr.vend; base += kBlock) {
-    if (s_y >= 0) break;   // uniform: read after a barrier
-    const int v = base + tid;
-    const bool has = v < cr.vend;
-    uint4 qt, qd;
-    load_pair(R, v, has, qt, qd);
-    float wv[N], pv[N];
+  if (s_y < 0) {   // uniform: read after a barrier
+    float wv[kDrawVecs][N];
     float vs = 0.f;
-    if (has) {
-      weight_group(R, st, c, qt, qd, v, use_p, wv, pv);
 #pragma unroll
-      for (int j = 0; j < N; ++j) {
-        vs += wv[j];
-        if (wv[j] > 0.f) lastpos = R.sp.head + v * N + j;
+    for (int i = 0; i < kDrawVecs; ++i) {
+      const int v = cr.vbeg + tid * kDrawVecs + i;
+      float pv[N];
+      if (v < cr.vend) {
+        weight_group(R, st, c, qt[i], qd[i], v, use_p, wv[i], pv);
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+          vs += wv[i][j];
+          if (wv[i][j] > 0.f) lastpos = R.sp.head + v * N + j;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < N; ++j) wv[i][j] = 0.f;
       }
     }
     double incl, excl, tot;
     block_scan(static_cast<double>(vs), s_a, incl, excl, tot);
-    const bool cross = has && (cum + incl > t);
-    const unsigned long long bal = __ballot(cross);
+    const bool crossv = cum + incl > t && vs > 0.f;
+    const unsigned long long bal = __ballot(crossv);
     if (lane == 0) s_i[w] = bal ? w * kWave + __ffsll(static_cast<long long>(bal)) - 1 : -1;
     __syncthreads();
     if (tid == 0) {
@@ -486,26 +533,27 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       s_first = f;
     }
     __syncthreads();
-    if (s_first >= 0) {
-      if (tid == s_first) {
-        const double cb = cum + excl;
-        float ps = 0.f;
-        int y = -1, lp = -1;
+    if (s_first >= 0 && tid == s_first) {
+      const double cb = cum + excl;
+      float psum = 0.f;
+      int y = -1, lp = -1;
+#pragma unroll
+      for (int i = 0; i < kDrawVecs; ++i) {
+        const int tok0 = R.sp.head + (cr.vbeg + tid * kDrawVecs + i) * N;
 #pragma unroll
         for (int j = 0; j < N; ++j) {
-          ps += wv[j];
-          if (wv[j] > 0.f) lp = R.sp.head + v * N + j;
-          if (y < 0 && cb + static_cast<double>(ps) > t) y = R.sp.head + v * N + j;
+          psum += wv[i][j];
+          if (wv[i][j] > 0.f) lp = tok0 + j;
+          if (y < 0 && cb + static_cast<double>(psum) > t) y = tok0 + j;
         }
-        s_y = y >= 0 ? y : (lp >= 0 ? lp : R.sp.head + v * N);
       }
-      __syncthreads();
-      break;
+      s_y = y >= 0 ? y : lp;
     }
     cum += tot;
   }
+  __syncthreads();
 
-  if (s_y < 0 && cr.last && tid == 0) {   // tail elements, in token order
+  if (s_y < 0 && cr.last && tid == 0) {   // tail elements come last
     float p;
     for (int e = R.sp.tail; e < V; ++e) {
       const float we = weight_one(R, st, c, e, use_p, p);
@@ -549,31 +597,32 @@ int launch_sample(const void* target, const void* draft, const int32_t* xtok, co
                   hipStream_t stream, hipEvent_t* ev, const SamplePlan& P) {
   const size_t g1 = static_cast<size_t>(B) * (2 * K + 1) * P.stats.nchunk;
   const size_t g2 = static_cast<size_t>(B) * P.draw.nchunk;
-  if (!grid_fits(g1) || !grid_fits(g2)) return SPEC_ERR_ARG;
+  if (!grid_fits(g1) || !grid_fits(g2) || P.draw.cv > kBlock * kDrawVecs) return SPEC_ERR_ARG;
   const WsLayout L = ws_layout(B, K, V, 1);
   const float c = exp2_scale(T);
   const TIn* t = static_cast<const TIn*>(target);
   const TIn* d = static_cast<const TIn*>(draft);
   float2* part1 = ws_ptr<float2>(ws, L.part_stats);
-  unsigned* cnt1 = ws_ptr<unsigned>(ws, L.cnt_a);
-  ReqState* st = ws_ptr<ReqState>(ws, L.state);
+  float* gath = ws_ptr<float>(ws, L.gathered);
   double2* part2 = ws_ptr<double2>(ws, L.part_draw);
   unsigned* cnt2 = ws_ptr<unsigned>(ws, L.cnt_b);
   const dim3 grid1(static_cast<unsigned>(g1)), grid2(static_cast<unsigned>(g2)), block(kBlock);
   const int ns = P.stats.nchunk, cs = P.stats.cv, nd = P.draw.nchunk, cd = P.draw.cv;
   if (ev == nullptr) {
-    hipLaunchKernelGGL(sample_stats_kernel<TIn>, grid1, block, 0, stream, t, d, xtok, uni, kv_in,
-                       K, V, c, ns, cs, part1, cnt1, st, out_tok, out_tau, out_kv, out_p, out_q);
-    hipLaunchKernelGGL(sample_draw_kernel<TIn>, grid2, block, 0, stream, t, d, uni, K, V, c, nd,
-                       cd, static_cast<const ReqState*>(st), part2, cnt2, out_tok);
+    hipLaunchKernelGGL(sample_stats_kernel<TIn>, grid1, block, 0, stream, t, d, xtok, K, V, c, ns,
+                       cs, part1, gath);
+    hipLaunchKernelGGL(sample_draw_kernel<TIn>, grid2, block, 0, stream, t, d, xtok, uni, kv_in,
+                       K, V, c, ns, static_cast<const float2*>(part1),
+                       static_cast<const float*>(gath), nd, cd, part2, cnt2, out_tok, out_tau,
+                       out_kv, out_p, out_q);
   } else {
     // profiling: the runtime records the events at each kernel's start and end
     hipExtLaunchKernelGGL(sample_stats_kernel<TIn>, grid1, block, 0, stream, ev[0], ev[1], 0, t,
-                          d, xtok, uni, kv_in, K, V, c, ns, cs, part1, cnt1, st, out_tok,
-                          out_tau, out_kv, out_p, out_q);
+                          d, xtok, K, V, c, ns, cs, part1, gath);
     hipExtLaunchKernelGGL(sample_draw_kernel<TIn>, grid2, block, 0, stream, ev[2], ev[3], 0, t, d,
-                          uni, K, V, c, nd, cd, static_cast<const ReqState*>(st), part2, cnt2,
-                          out_tok);
+                          xtok, uni, kv_in, K, V, c, ns, static_cast<const float2*>(part1),
+                          static_cast<const float*>(gath), nd, cd, part2, cnt2, out_tok, out_tau,
+                          out_kv, out_p, out_q);
   }
   return launch_status();
 }
