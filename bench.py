@@ -221,7 +221,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(stop) / args.steps
 
-    # ---- per-kernel durations: the same K steps through spec_verify_sample_timed, whose
+    # ---- per-kernel durations: the same K steps through spec_verify_sample_ex, whose
     # kernels are launched with start/stop events (this adds launch overhead between calls, so
     # the loop's own time is not used for the headline)
     torch.cuda.synchronize()

@@ -29,7 +29,7 @@
  *       draft_tokens  [B, K] int32; uniforms [B, K+1] float32 in [0,1): uniforms[b][k] (k<K)
  *       decides slot k, uniforms[b][K] drives the residual or bonus draw.
  *     Logit element type is SPEC_F32 (float) or SPEC_BF16 (bfloat16 bit patterns, 2 bytes);
- *     logit pointers must be aligned to their element size. Any V >= 2 is accepted.
+ *     logit pointers must be aligned to their element size. 2 <= V <= SPEC_MAX_V.
  *   - -inf logits are masked tokens (probability 0). NaN or +inf logits, or a row whose logits
  *     are all -inf, give undefined (but in-bounds, terminating) results.
  *   - The caller owns every buffer, including the workspace. The library allocates nothing and
@@ -39,10 +39,12 @@
  *   - Workspace: size from spec_workspace_bytes(B,K,V,F) (one size serves all three entry
  *     points), 256-byte aligned, zeroed once by spec_workspace_init before its first use. Each
  *     call leaves it ready for the next one (the completion counters it holds are reset on the
- *     device). One workspace must not be used by two calls that may run concurrently (two
+ *     device, and the sampling draw's published-mass words are cleared by the same call's
+ *     streaming pass before the draw reads them). One workspace must not be used by two calls that may run concurrently (two
  *     streams, or two host threads on one stream without ordering): they would race.
  *   - Errors found on the host are returned synchronously, before anything is enqueued:
- *       SPEC_ERR_ARG         null required pointer, B < 1, K < 1 or K > SPEC_MAX_K, V < 2,
+ *       SPEC_ERR_ARG         null required pointer, B < 1, K < 1 or K > SPEC_MAX_K, V < 2
+ *                            or V > SPEC_MAX_V,
  *                            F outside [1, min(V, SPEC_MAX_F)], misaligned logit pointer,
  *                            or a launch grid that would exceed 2^31-1 blocks;
  *       SPEC_ERR_DTYPE       dtype not SPEC_F32 / SPEC_BF16;
@@ -67,9 +69,11 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 1
+#define SPEC_ABI_VERSION 2
 #define SPEC_MAX_K 64
 #define SPEC_MAX_F 16
+#define SPEC_MAX_V 4194304 /* 2^22 */
+#define SPEC_DEFAULT_WAIT_POLLS 16384
 
 /* logit element types */
 #define SPEC_F32 0
@@ -118,18 +122,24 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, int 
                        float* out_p, float* out_q,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* spec_verify_sample with per-kernel timing, for profiling and the bench. `events` points to
- * four caller-created hipEvent_t (timing enabled, none NULL, else SPEC_ERR_ARG): the runtime
- * records events[0]/events[1] at the start/end of the streaming statistics kernel and
- * events[2]/events[3] at the start/end of the draw kernel (hipExtLaunchKernelGGL). Results are
- * identical to spec_verify_sample. */
-int spec_verify_sample_timed(const void* target_logits, const void* draft_logits, int dtype,
-                             const int32_t* draft_tokens, const float* uniforms,
-                             const int32_t* kv_len_in, int B, int K, int V, float temperature,
-                             int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len,
-                             float* out_p, float* out_q,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream,
-                             hipEvent_t* events);
+/* spec_verify_sample with two extra controls, for profiling and testing. Results are identical
+ * to spec_verify_sample, bit for bit, whatever the controls are.
+ *   events     NULL, or four caller-created hipEvent_t (timing enabled, none NULL, else
+ *              SPEC_ERR_ARG): the runtime records events[0]/events[1] at the start/end of the
+ *              streaming statistics kernel and events[2]/events[3] at the start/end of the draw
+ *              kernel (hipExtLaunchKernelGGL).
+ *   wait_polls the draw's workgroups of one request exchange their chunk masses; a workgroup
+ *              re-polls for another's mass at most this many times (a short sleep apart)
+ *              before computing that mass itself. Negative selects SPEC_DEFAULT_WAIT_POLLS
+ *              (what spec_verify_sample uses); 0 makes every workgroup compute each mass it
+ *              does not find already published, which exercises that path. */
+int spec_verify_sample_ex(const void* target_logits, const void* draft_logits, int dtype,
+                          const int32_t* draft_tokens, const float* uniforms,
+                          const int32_t* kv_len_in, int B, int K, int V, float temperature,
+                          int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len,
+                          float* out_p, float* out_q,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream,
+                          hipEvent_t* events, int wait_polls);
 
 /* Greedy verification, temperature must be exactly 0 ([SD] stage 3 at temperature zero;
  * [D3D] 検証のしくみ③, 検証のまとめ). g_k = argmax_v target_logits[b,k,v] (lowest v on ties);

@@ -4,10 +4,11 @@ The work runs in hand-written HIP kernels behind the C ABI of libspecverify.so
 (include/spec_verify.h); this package is the thin Python binding used by tests and the bench.
 Build the library with `python -m speculative_decoding_verification_12_amd.build`.
 """
-from ._binding import (EXPORTS, LIB_PATH, SPEC_BF16, SPEC_F32, SPEC_MAX_F, SPEC_MAX_K, STATUS,
-                       SpecVerifyError, hip_runtime, load_library, new_workspace, spec_predict_outcomes,
+from ._binding import (EXPORTS, LIB_PATH, SPEC_BF16, SPEC_DEFAULT_WAIT_POLLS, SPEC_F32,
+                       SPEC_MAX_F, SPEC_MAX_K, SPEC_MAX_V, STATUS, SpecVerifyError, hip_runtime, load_library, new_workspace, spec_predict_outcomes,
                        spec_verify_greedy, spec_verify_sample, status_string, workspace_bytes)
 
-__all__ = ["EXPORTS", "LIB_PATH", "SPEC_BF16", "SPEC_F32", "SPEC_MAX_F", "SPEC_MAX_K", "STATUS",
+__all__ = ["EXPORTS", "LIB_PATH", "SPEC_BF16", "SPEC_DEFAULT_WAIT_POLLS", "SPEC_F32", "SPEC_MAX_F",
+           "SPEC_MAX_K", "SPEC_MAX_V", "STATUS",
            "SpecVerifyError", "hip_runtime", "load_library", "new_workspace", "spec_predict_outcomes",
            "spec_verify_greedy", "spec_verify_sample", "status_string", "workspace_bytes"]

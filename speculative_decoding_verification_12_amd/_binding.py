@@ -15,11 +15,13 @@ SPEC_F32 = 0
 SPEC_BF16 = 1
 SPEC_MAX_K = 64
 SPEC_MAX_F = 16
+SPEC_MAX_V = 1 << 22
+SPEC_DEFAULT_WAIT_POLLS = 16384
 STATUS = {0: "SPEC_OK", -1: "SPEC_ERR_ARG", -2: "SPEC_ERR_DTYPE", -3: "SPEC_ERR_TEMPERATURE",
           -4: "SPEC_ERR_WORKSPACE", -5: "SPEC_ERR_HIP"}
 
 EXPORTS = ("spec_abi_version", "spec_status_string", "spec_workspace_bytes",
-           "spec_workspace_init", "spec_verify_sample", "spec_verify_sample_timed",
+           "spec_workspace_init", "spec_verify_sample", "spec_verify_sample_ex",
            "spec_verify_greedy", "spec_predict_outcomes")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -30,8 +32,8 @@ _SIGNATURES = {
     "spec_workspace_init": (_i, [_vp, _sz, _vp]),
     "spec_verify_sample": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _f,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "spec_verify_sample_timed": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _f,
-                                      _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "spec_verify_sample_ex": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _f,
+                                   _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _i]),
     "spec_verify_greedy": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _f,
                                 _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_predict_outcomes": (_i, [_vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
@@ -145,11 +147,12 @@ def new_workspace(B: int, K: int, V: int, F: int = 1, device="cuda"):
 
 
 def spec_verify_sample(target, draft, draft_tokens, uniforms, kv_len, temperature, workspace,
-                       out=None, events=None):
+                       out=None, events=None, wait_polls=None):
     """Speculative-sampling verification. Returns dict(tokens, tau, kv_len, p, q).
 
-    `events` (optional) is a ctypes array of four hipEvent_t handles; the call then goes through
-    spec_verify_sample_timed and the events bracket the two kernels."""
+    `events` (optional) is a ctypes array of four hipEvent_t handles that then bracket the two
+    kernels; `wait_polls` (optional) bounds the draw's polling for other workgroups' masses.
+    Either one routes the call through spec_verify_sample_ex."""
     torch = _torch()
     B, K1, V = target.shape
     K = K1 - 1
@@ -171,11 +174,12 @@ def spec_verify_sample(target, draft, draft_tokens, uniforms, kv_len, temperatur
             _ptr(out.get("kv_len")), _ptr(out.get("p")), _ptr(out.get("q")), _ptr(workspace),
             workspace.numel(), _stream(dev))
     lib = load_library()
-    if events is None:
+    if events is None and wait_polls is None:
         _check("spec_verify_sample", lib.spec_verify_sample(*args))
     else:
-        _check("spec_verify_sample_timed",
-               lib.spec_verify_sample_timed(*args, ctypes.cast(events, ctypes.c_void_p)))
+        ev = None if events is None else ctypes.cast(events, ctypes.c_void_p)
+        polls = -1 if wait_polls is None else int(wait_polls)
+        _check("spec_verify_sample_ex", lib.spec_verify_sample_ex(*args, ev, polls))
     return out
 
 

@@ -19,7 +19,7 @@ inline int elems_per_vec(int dtype) { return dtype == SPEC_BF16 ? 8 : 4; }
 inline size_t elem_bytes(int dtype) { return dtype == SPEC_BF16 ? 2 : 4; }
 
 inline int check_dims(int B, int K, int V) {
-  if (B < 1 || K < 1 || K > SPEC_MAX_K || V < 2) return SPEC_ERR_ARG;
+  if (B < 1 || K < 1 || K > SPEC_MAX_K || V < 2 || V > SPEC_MAX_V) return SPEC_ERR_ARG;
   return SPEC_OK;
 }
 

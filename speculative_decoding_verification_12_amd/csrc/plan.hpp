@@ -61,7 +61,7 @@ SV_HD inline KernelPlan stats_plan(int B, int K, int V, int epv) {
   return plan_rows(B * (2 * K + 1), V, epv, kStatsResident);
 }
 // the draw re-reads one row (two when m < K) per request, kDrawVecs adjacent vectors per thread,
-// so its final search rescans one chunk with a single load per vector
+// and keeps them in registers for the final search
 constexpr int kDrawVecs = 4;
 SV_HD inline KernelPlan draw_plan(int B, int K, int V, int epv) {
   (void)B;
@@ -98,7 +98,7 @@ struct WsLayout {
   size_t counters_end;
   size_t gathered;   // float [B*2K]: target and draft logit of each slot's draft token
   size_t part_stats; // 8 B [B*(2K+1)*nchunk]: chunk (max, scaled sum)
-  size_t part_draw;  // 16 B [B*nchunk]: chunk (residual mass, target mass)
+  size_t part_draw;  // 16 B [B*nchunk]: published chunk (residual mass, target mass)
   size_t part_greedy;// 8 B [B*(K+1)*nchunk]: chunk (max, lowest index)
   size_t part_topf;  // 8 B [B*K*nchunk*F]: chunk top-F lists
   size_t part_pstat; // 8 B [B*K*nchunk]

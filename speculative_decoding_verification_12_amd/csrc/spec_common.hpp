@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "plan.hpp"
 
 namespace sv {
@@ -169,6 +171,117 @@ __device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
     if (lane >= o) v += n;
   }
   return v;
+}
+
+// ------------------------------------------------------------------------------ DPP lane moves
+// Data-parallel-primitive moves read another lane's register inside the vector ALU, with no LDS
+// round trip (a ds_bpermute shuffle costs an LDS access per step). GFX9 control encodings; all
+// lanes of the wave must be active where these are used.
+namespace dpp {
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowShr = 0x110;        // row_shr:n is kRowShr + n (n = 1..15)
+constexpr int kWaveShr1 = 0x138;      // wave_shr:1
+constexpr int kRowMirror = 0x140;     // lane i of a row reads lane 15 - i
+constexpr int kRowHalfMirror = 0x141; // lane i of a half-row reads lane 7 - i
+constexpr int kRowBcast15 = 0x142;    // lane 15 of each row to the whole next row
+constexpr int kRowBcast31 = 0x143;    // lane 31 to rows 2 and 3
+}  // namespace dpp
+
+// Lanes outside `row_mask`, and lanes whose source is outside the row (or wave) unless
+// `bound_zero`, keep `old`; with `bound_zero` such sources read as 0.
+template <int ctrl, int row_mask = 0xf, bool bound_zero = false>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(old), static_cast<int>(v), ctrl, row_mask, 0xf, bound_zero));
+}
+
+template <int ctrl, int row_mask = 0xf, bool bound_zero = false>
+__device__ __forceinline__ float dpp_f32(float old, float v) {
+  return __uint_as_float(dpp_u32<ctrl, row_mask, bound_zero>(__float_as_uint(old),
+                                                             __float_as_uint(v)));
+}
+
+template <int ctrl, int row_mask = 0xf, bool bound_zero = false>
+__device__ __forceinline__ double dpp_f64(double old, double v) {
+  const uint64_t o = static_cast<uint64_t>(__double_as_longlong(old));
+  const uint64_t x = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = dpp_u32<ctrl, row_mask, bound_zero>(static_cast<uint32_t>(o),
+                                                          static_cast<uint32_t>(x));
+  const uint32_t hi = dpp_u32<ctrl, row_mask, bound_zero>(static_cast<uint32_t>(o >> 32),
+                                                          static_cast<uint32_t>(x >> 32));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t x = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x)), lane));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x >> 32)), lane));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// Combines the lanes of every aligned group of `width` lanes (1, 2, 4, 8, 16, 32 or 64) with the
+// commutative `op`; every lane of a group gets the group's result, bit for bit, because each
+// step combines a lane with a partner holding the same partial of the other half.
+template <typename T, typename Op>
+__device__ __forceinline__ T group_reduce(T v, int width, Op op) {
+  static_assert(std::is_same<T, double>::value || std::is_same<T, float>::value ||
+                    std::is_same<T, int>::value,
+                "double, float or int");
+  auto mv = [](auto ctrl_tag, T x) -> T {
+    constexpr int ctrl = decltype(ctrl_tag)::value;
+    if constexpr (std::is_same<T, double>::value) return dpp_f64<ctrl>(x, x);
+    else if constexpr (std::is_same<T, float>::value) return dpp_f32<ctrl>(x, x);
+    else return static_cast<T>(dpp_u32<ctrl>(static_cast<uint32_t>(x), static_cast<uint32_t>(x)));
+  };
+  if (width >= 2) v = op(v, mv(std::integral_constant<int, dpp::kQuadXor1>{}, v));
+  if (width >= 4) v = op(v, mv(std::integral_constant<int, dpp::kQuadXor2>{}, v));
+  if (width >= 8) v = op(v, mv(std::integral_constant<int, dpp::kRowHalfMirror>{}, v));
+  if (width >= 16) v = op(v, mv(std::integral_constant<int, dpp::kRowMirror>{}, v));
+  if (width >= 32) {
+    T r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (std::is_same<T, double>::value) r[i] = readlane_f64(v, 16 * i);
+      else if constexpr (std::is_same<T, float>::value) r[i] = readlane_f32(v, 16 * i);
+      else r[i] = static_cast<T>(__builtin_amdgcn_readlane(static_cast<int>(v), 16 * i));
+    }
+    const T lo = op(r[0], r[1]), hi = op(r[2], r[3]);
+    const bool upper = (threadIdx.x & (kWave - 1)) >= 32;
+    v = width >= 64 ? op(lo, hi) : (upper ? hi : lo);
+  }
+  return v;
+}
+
+struct OpAdd {
+  template <typename T> __device__ T operator()(T a, T b) const { return a + b; }
+};
+struct OpMax {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+  __device__ int operator()(int a, int b) const { return max(a, b); }
+};
+
+// Inclusive prefix sum over the 64 lanes in lane order (Hillis-Steele inside each 16-lane row,
+// then the row totals carried across rows).
+__device__ __forceinline__ double wave_scan_incl(double x) {
+  x += dpp_f64<dpp::kRowShr + 1, 0xf, true>(0.0, x);
+  x += dpp_f64<dpp::kRowShr + 2, 0xf, true>(0.0, x);
+  x += dpp_f64<dpp::kRowShr + 4, 0xf, true>(0.0, x);
+  x += dpp_f64<dpp::kRowShr + 8, 0xf, true>(0.0, x);
+  x += dpp_f64<dpp::kRowBcast15, 0xa, false>(0.0, x);
+  x += dpp_f64<dpp::kRowBcast31, 0xc, false>(0.0, x);
+  return x;
+}
+
+// The previous lane's value (0 in lane 0): with an inclusive scan, the exclusive one, bit for bit.
+__device__ __forceinline__ double wave_shift_up1(double x) {
+  return dpp_f64<dpp::kWaveShr1, 0xf, true>(0.0, x);
 }
 
 // ------------------------------------------------------------------------------ arrival

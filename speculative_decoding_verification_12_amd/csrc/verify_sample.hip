@@ -13,15 +13,18 @@
 //     hardware exp2 per element; wave butterflies and LDS reduce to the chunk's (M, S), written
 //     with a plain store. The workgroup whose chunk holds a slot's draft token also records
 //     that token's logit. No workgroup waits on another: the kernel boundary is the only
-//     synchronisation.
+//     synchronisation. The first workgroups also clear the draw's published-mass words.
 //  2. sample_draw_kernel: one workgroup per (request, chunk of 1024 vectors). Each first merges
 //     its request's chunk statistics (a few hundred bytes, identical in every workgroup of the
-//     request), evaluates every slot's log-ratio in float64 and finds the first rejection m
-//     with a wave ballot; chunk 0 writes tau, kv, the kept tokens and p_k(x_k), q_k(x_k). Then
-//     it re-reads its chunk of row m of the target (and of the draft when m < K) and sums the
-//     draw weights in float64. The request's last workgroup to arrive (device-scope counter)
-//     finds the chunk that holds u*Z with one wave-wide prefix scan, rescans that chunk with a
-//     block prefix sum and writes the drawn token.
+//     request), evaluates every slot's acceptance ratio and finds the first rejection m with a
+//     wave ballot; chunk 0 writes tau, kv, the kept tokens and p_k(x_k), q_k(x_k). Then it
+//     re-reads its chunk of row m of the target (and of the draft when m < K), sums the draw
+//     weights per thread and per chunk and publishes the chunk's mass, tagged as written. Every
+//     workgroup of the request gathers all chunk masses, runs the same float64 prefix scan and
+//     so learns which chunk holds u*Z; that chunk's own workgroup finds the thread, then the
+//     token, from the values still in its registers. A workgroup that has polled for a mass too
+//     long computes that chunk's mass itself (bit for bit what its owner publishes), so no
+//     workgroup ever waits on one that has not been scheduled.
 #include <hip/hip_ext.h>
 
 #include "api_common.hpp"
@@ -120,10 +123,14 @@ template <typename TIn>
 __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
     const TIn* __restrict__ tgt, const TIn* __restrict__ drf, const int32_t* __restrict__ xtok,
     int K, int V, float c, int nchunk, int cv, float2* __restrict__ part,
-    float* __restrict__ gath) {
+    float* __restrict__ gath, uint64_t* __restrict__ clear, int nclear) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
   __shared__ float sm[kWaves], ss[kWaves];
+  // the draw kernel that follows finds these words zero (nothing published yet)
+  for (size_t gi = static_cast<size_t>(blockIdx.x) * kBlock + threadIdx.x;
+       gi < static_cast<size_t>(nclear); gi += static_cast<size_t>(gridDim.x) * kBlock)
+    clear[gi] = 0ull;
 
   const int rows = 2 * K + 1;
   const int ch = blockIdx.x % nchunk;
@@ -211,41 +218,137 @@ __device__ __forceinline__ void load_pair(const DrawRows<TIn>& R, int v, bool ha
   qd = (has && R.resid && R.d_aligned) ? dv[v] : neg_inf_vec<TIn>();
 }
 
-// Block-wide inclusive and exclusive prefix sums in thread order. excl of thread t equals incl of
-// thread t-1 bit for bit. `tot` receives the block total.
-__device__ __forceinline__ void block_scan(double x, double* s_wave, double& incl, double& excl,
-                                           double& tot) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  const double wi = wave_inclusive_scan(x, lane);
-  double we = __shfl_up(wi, 1, kWave);
-  if (lane == 0) we = 0.0;
-  if (lane == kWave - 1) s_wave[w] = wi;
-  __syncthreads();
-  double off = 0.0;
-  for (int i = 0; i < w; ++i) off += s_wave[i];
-  double all = 0.0;
-  for (int i = 0; i < kWaves; ++i) all += s_wave[i];
-  incl = off + wi;
-  excl = lane == 0 ? off : off + we;
-  tot = all;
-  __syncthreads();
+// 2^x for a float64 exponent, to about 2e-7 relative: the integer part scales exactly, the
+// fraction goes through the hardware exp2. x = -inf gives 0.
+__device__ __forceinline__ double exp2_wide(double x) {
+  if (!(x > -1074.0)) return 0.0;
+  if (x >= 1024.0) return INFINITY;
+  const double n = floor(x);
+  return ldexp(static_cast<double>(fast_exp2(static_cast<float>(x - n))), static_cast<int>(n));
 }
 
-// Chunks of at most kBlock * kDrawVecs vectors (see draw_plan).
+// The elements a thread of the draw owns, in token order: the scalar head (thread 0 of chunk 0),
+// its kDrawVecs adjacent vectors, then the scalar tail (the thread holding the row's last
+// vector, or the head's owner when the row has no whole vector). Every thread's elements are
+// contiguous in token order, so the thread order of the chunks is token order.
+struct ThreadElems {
+  int nh;      // head elements [0, nh)
+  int v0, nv;  // vectors [v0, v0 + nv)
+  int nt;      // tail elements [tail0, tail0 + nt)
+  int tail0;
+};
+
+__device__ __forceinline__ ThreadElems thread_elems(const RowSpan& sp, int V, int nchunk, int cv,
+                                                    int ch, int th) {
+  const ChunkRange cr = chunk_range(sp, ch, nchunk, cv);
+  ThreadElems e;
+  e.v0 = cr.vbeg + th * kDrawVecs;
+  e.nv = max(0, min(kDrawVecs, cr.vend - e.v0));
+  e.nh = (ch == 0 && th == 0) ? sp.head : 0;
+  int tch = 0, tth = 0;
+  if (sp.nvec > 0) {
+    const int lv = sp.nvec - 1;
+    tch = lv / cv;
+    tth = (lv - tch * cv) / kDrawVecs;
+  }
+  e.nt = (ch == tch && th == tth) ? V - sp.tail : 0;
+  e.tail0 = sp.tail;
+  return e;
+}
+
+// One thread's draw mass ws (sum of w) and target mass ps (sum of p), summed in token order;
+// `qt`/`qd` receive its vectors. Deterministic: the owner and any helper get the same bits.
+template <typename TIn>
+__device__ __forceinline__ void thread_mass(const DrawRows<TIn>& R, const ReqState& st, float c,
+                                            int V, const ThreadElems& el, uint4 (&qt)[kDrawVecs],
+                                            uint4 (&qd)[kDrawVecs], float& ws, float& ps) {
+  constexpr int N = Elem<TIn>::N;
+#pragma unroll
+  for (int i = 0; i < kDrawVecs; ++i) load_pair(R, el.v0 + i, i < el.nv, qt[i], qd[i]);
+  ws = 0.f;
+  ps = 0.f;
+  float p;
+  for (int e = 0; e < el.nh; ++e) {
+    ws += weight_one(R, st, c, e, false, p);
+    ps += p;
+  }
+#pragma unroll
+  for (int i = 0; i < kDrawVecs; ++i) {
+    if (i < el.nv) {
+      float wv[N], pv[N];
+      weight_group(R, st, c, qt[i], qd[i], el.v0 + i, false, wv, pv);
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        ws += wv[j];
+        ps += pv[j];
+      }
+    }
+  }
+  for (int e = 0; e < el.nt; ++e) {
+    ws += weight_one(R, st, c, el.tail0 + e, false, p);
+    ps += p;
+  }
+}
+
+// Chunk masses (R, P) in float64 from the threads' (ws, ps): wave butterflies, then the four
+// wave totals in order. Every thread returns the same bits.
+__device__ __forceinline__ void chunk_mass(float ws, float ps, double (*s_red)[kWaves],
+                                           double& R, double& P) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const double rw = group_reduce(static_cast<double>(ws), kWave, OpAdd{});
+  const double pw = group_reduce(static_cast<double>(ps), kWave, OpAdd{});
+  if (lane == 0) {
+    s_red[0][w] = rw;
+    s_red[1][w] = pw;
+  }
+  __syncthreads();
+  R = 0.0;
+  P = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    R += s_red[0][i];
+    P += s_red[1][i];
+  }
+  __syncthreads();   // s_red is reused
+}
+
+constexpr uint64_t kWrittenBit = 1ull << 63;   // sign bit of a non-negative float64 mass
+
+// Reads a published (R, P) pair, re-polling at most `polls` times; false if it is not there yet.
+__device__ __forceinline__ bool poll_mass(const uint64_t* p, int polls, double& R, double& P) {
+  uint64_t a = load_coherent(p), b = load_coherent(p + 1);
+  while (((a & b) & kWrittenBit) == 0ull) {
+    if (polls-- <= 0) return false;
+    __builtin_amdgcn_s_sleep(2);
+    if ((a & kWrittenBit) == 0ull) a = load_coherent(p);
+    if ((b & kWrittenBit) == 0ull) b = load_coherent(p + 1);
+  }
+  R = bits_d(a & ~kWrittenBit);
+  P = bits_d(b & ~kWrittenBit);
+  return true;
+}
+
+// most draw chunks a row of V <= SPEC_MAX_V elements can have (f32 rows: 4 elements per vector)
+constexpr int kMaxDrawChunks = (SPEC_MAX_V / 4 + kBlock * kDrawVecs - 1) / (kBlock * kDrawVecs);
+
+// Chunks of kBlock * kDrawVecs vectors (see draw_plan). cm holds the published (R, P) of every
+// chunk, [b][ch][2] words, zeroed by the statistics kernel of the same call.
 template <typename TIn>
 __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     const TIn* __restrict__ tgt, const TIn* __restrict__ drf, const int32_t* __restrict__ xtok,
     const float* __restrict__ uni, const int32_t* __restrict__ kv_in, int K, int V, float c,
     int nchunk_s, const float2* __restrict__ part_s, const float* __restrict__ gath,
-    int nchunk, int cv, double2* __restrict__ part, unsigned* __restrict__ cnt_base,
+    int nchunk, int cv, uint64_t* __restrict__ cm, int wait_polls,
     int32_t* __restrict__ out_tok, int32_t* __restrict__ out_tau, int32_t* __restrict__ out_kv,
     float* __restrict__ out_p, float* __restrict__ out_q) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
-  __shared__ double s_a[kWaves], s_b[kWaves];
-  __shared__ int s_i[kWaves];
-  __shared__ int s_flag, s_cs, s_usep, s_y, s_first;
-  __shared__ double s_cum, s_t;
+  __shared__ double s_red[2][kWaves];
+  __shared__ double2 s_cm[kMaxDrawChunks];
+  __shared__ int s_first[kWaves];
+  __shared__ uint32_t s_raw[2][4 * kDrawVecs];   // one thread's target and draft vectors
+  __shared__ int s_cs, s_usep, s_fallback;
+  __shared__ double s_cb, s_t;
   __shared__ float row_m[2 * SPEC_MAX_K + 1];
   __shared__ double row_s[2 * SPEC_MAX_K + 1];
   __shared__ ReqState s_st;
@@ -256,7 +359,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
   const int rows = 2 * K + 1;
 
   // ---- merge the statistics pass of request b (every workgroup of b does the same, bit for
-  // bit): row (max, sum) in fp32/fp64, slot log-ratios in fp64, first rejection by ballot
+  // bit): row (max, sum) in fp32/fp64, slot acceptance ratios, first rejection by ballot
   {
     const bool valid = w == 0 && lane < K;
     int xk = 0;
@@ -268,9 +371,9 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       ld = gath[static_cast<size_t>(b) * 2 * K + K + lane];
     }
     const int kv0 = (ch == 0 && tid == 0 && kv_in) ? kv_in[b] : 0;
-    // Rows are merged in segments of W lanes (W = nchunk_s rounded up to a power of two, at
-    // most 64), 64/W rows per wave, so one pass over the block issues every partial load at
-    // once. Lanes past nchunk_s (or past the last row) carry (-inf, 0).
+    // Rows are merged in groups of W lanes (W = nchunk_s rounded up to a power of two, at most
+    // 64), 64/W rows per wave, so one pass over the block issues every partial load at once.
+    // Lanes past nchunk_s (or past the last row) carry (-inf, 0).
     int W = 1;
     while (W < nchunk_s && W < kWave) W <<= 1;
     const int per_wave = kWave / W, g = lane / W, i = lane % W;
@@ -290,7 +393,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       }
       if (rr < rows)
         for (int j = i + kHeld * W; j < nchunk_s; j += W) lm = fmaxf(lm, pr[j].x);
-      const float Mr = seg_max(lm, W);
+      const float Mr = group_reduce(lm, W, OpMax{});
       const float mc = Mr * c;
       double ls = 0.0;
 #pragma unroll
@@ -301,7 +404,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
           const float2 q = pr[j];
           if (q.x > -INFINITY) ls += static_cast<double>(q.y) * fast_exp2(q.x * c - mc);
         }
-      const double Sr = seg_sum(ls, W);
+      const double Sr = group_reduce(ls, W, OpAdd{});
       if (i == 0 && rr < rows) {
         row_m[rr] = Mr;
         row_s[rr] = Sr;
@@ -312,14 +415,15 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       // a draft token must be a token the draft could have sampled
       const bool bad = valid && (xk < 0 || xk >= V || ld == -INFINITY);
       bool keep = true;
-      double lp = 0.0, lq = 0.0;
+      double pk = 0.0, qk = 0.0;
       if (valid && !bad) {
-        const float mct = row_m[lane] * c, mcd = row_m[K + 1 + lane] * c;
-        lp = kLn2 * (static_cast<double>(lt) * c - static_cast<double>(mct)) - log(row_s[lane]);
-        lq = kLn2 * (static_cast<double>(ld) * c - static_cast<double>(mcd)) -
-             log(row_s[K + 1 + lane]);
-        // kept iff u < min(1, p/q); p >= q is kept for every u in [0,1)
-        keep = (lp >= lq) || (static_cast<double>(uk) < exp(lp - lq));
+        // p_k(x_k) and q_k(x_k): 2^(l*c - fl(M*c)) / S of each row
+        pk = exp2_wide(static_cast<double>(lt) * c - static_cast<double>(row_m[lane] * c)) /
+             row_s[lane];
+        qk = exp2_wide(static_cast<double>(ld) * c - static_cast<double>(row_m[K + 1 + lane] * c)) /
+             row_s[K + 1 + lane];
+        // kept iff u < min(1, p/q): p >= q is kept for every u in [0,1)
+        keep = pk >= qk || static_cast<double>(uk) < pk / qk;
       }
       const bool err = __ballot(bad) != 0ull;
       const unsigned long long rej = __ballot(valid && !keep);
@@ -327,8 +431,8 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       if (ch == 0) {   // one workgroup of the request writes everything but the drawn token
         if (valid) {
           const size_t o = static_cast<size_t>(b) * K + lane;
-          if (out_p) out_p[o] = err ? NAN : static_cast<float>(exp(lp));
-          if (out_q) out_q[o] = err ? NAN : static_cast<float>(exp(lq));
+          if (out_p) out_p[o] = err ? NAN : static_cast<float>(pk);
+          if (out_q) out_q[o] = err ? NAN : static_cast<float>(qk);
         }
         for (int j = lane; j <= K; j += kWave)
           if (err || j != mm) out_tok[static_cast<size_t>(b) * (K + 1) + j] = (!err && j < mm) ? xk : -1;
@@ -352,7 +456,6 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
   }
   const ReqState st = s_st;
   if (st.m < 0) return;   // row error: nothing to draw (every workgroup of b agrees)
-  unsigned* cnt = cnt_base + static_cast<size_t>(b) * kCounterStride;
 
   DrawRows<TIn> R;
   R.resid = st.m < K;
@@ -360,223 +463,177 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
   R.d = R.resid ? drf + (static_cast<size_t>(b) * K + st.m) * static_cast<size_t>(V) : R.t;
   R.sp = row_span(R.t, V);
   R.d_aligned = row_span(R.d, V).head == R.sp.head;
+  uint64_t* cmb = cm + static_cast<size_t>(b) * nchunk * 2;
 
-  // ---- chunk masses: sum of w (draw weights) and of p (fallback weights). Thread t owns the
-  // kDrawVecs adjacent vectors vbeg + t*kDrawVecs + i, plus head (first chunk) or tail (last
-  // chunk) element t.
-  {
-    const ChunkRange cr = chunk_range(R.sp, ch, nchunk, cv);
-    uint4 qt[kDrawVecs], qd[kDrawVecs];
-#pragma unroll
-    for (int i = 0; i < kDrawVecs; ++i) {
-      const int v = cr.vbeg + tid * kDrawVecs + i;
-      load_pair(R, v, v < cr.vend, qt[i], qd[i]);
+  // ---- this chunk's masses, published tagged
+  const ThreadElems el = thread_elems(R.sp, V, nchunk, cv, ch, tid);
+  uint4 qt[kDrawVecs], qd[kDrawVecs];
+  float ws, ps;
+  thread_mass(R, st, c, V, el, qt, qd, ws, ps);
+  double R0, P0;
+  chunk_mass(ws, ps, s_red, R0, P0);
+  if (tid == 0) {
+    store_coherent(&cmb[2 * ch], dbits(R0) | kWrittenBit);
+    store_coherent(&cmb[2 * ch + 1], dbits(P0) | kWrittenBit);
+  }
+
+  // ---- gather every chunk mass of the request into LDS; a chunk not published within the
+  // poll budget is computed here (the same bits its owner publishes)
+  bool missing = false;
+  for (int j = tid; j < nchunk; j += kBlock) {
+    double r = R0, q = P0;
+    if (j != ch && !poll_mass(&cmb[2 * j], wait_polls, r, q)) {
+      r = -1.0;   // marks the entry missing
+      missing = true;
     }
-    double rs = 0.0, ps = 0.0;
-    float p;
-    if (cr.first && tid < R.sp.head) {
-      rs += weight_one(R, st, c, tid, false, p);
-      ps += p;
-    }
-    if (cr.last && tid < V - R.sp.tail) {
-      rs += weight_one(R, st, c, R.sp.tail + tid, false, p);
-      ps += p;
-    }
-    float ws = 0.f, pss = 0.f;
-#pragma unroll
-    for (int i = 0; i < kDrawVecs; ++i) {
-      const int v = cr.vbeg + tid * kDrawVecs + i;
-      if (v < cr.vend) {
-        float wv[N], pv[N];
-        weight_group(R, st, c, qt[i], qd[i], v, false, wv, pv);
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-          ws += wv[j];
-          pss += pv[j];
-        }
-      }
-    }
-    rs += ws;
-    ps += pss;
-    rs = wave_sum(rs);
-    ps = wave_sum(ps);
-    if (lane == 0) {
-      s_a[w] = rs;
-      s_b[w] = ps;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      double R0 = 0.0, P0 = 0.0;
-      for (int i = 0; i < kWaves; ++i) {
-        R0 += s_a[i];
-        P0 += s_b[i];
-      }
-      double2* dst = &part[static_cast<size_t>(b) * nchunk + ch];
-      store_coherent(&dst->x, dbits(R0));
-      store_coherent(&dst->y, dbits(P0));
+    s_cm[j] = make_double2(r, q);
+  }
+  if (__syncthreads_or(missing)) {
+    for (int j = 0; j < nchunk; ++j) {
+      if (!(s_cm[j].x < 0.0)) continue;   // uniform: read after a barrier
+      uint4 ht[kDrawVecs], hd[kDrawVecs];
+      float hw, hp;
+      thread_mass(R, st, c, V, thread_elems(R.sp, V, nchunk, cv, j, tid), ht, hd, hw, hp);
+      double hr, hq;
+      chunk_mass(hw, hp, s_red, hr, hq);
+      if (tid == 0) s_cm[j] = make_double2(hr, hq);
+      __syncthreads();
     }
   }
-  if (!arrive_last(cnt, static_cast<unsigned>(nchunk), &s_flag)) return;
 
-  // ---- last workgroup of request b: find the chunk holding u*Z with one wave-wide scan
+  // ---- wave 0: float64 prefix scan over the chunks (lane l takes a contiguous run of them),
+  // total Z, threshold t = u*Z, and the chunk holding it
   if (w == 0) {
-    const double u = static_cast<double>(uni[static_cast<size_t>(b) * (K + 1) + K]);
-    const double2* pr = part + static_cast<size_t>(b) * nchunk;
-    const int per = (nchunk + kWave - 1) / kWave;   // lane l owns chunks [l*per, l*per + per)
+    const int per = (nchunk + kWave - 1) / kWave;
     const int j0 = min(lane * per, nchunk), j1 = min(j0 + per, nchunk);
     double rl = 0.0, pl = 0.0;
-    int lastpos_r = -1, lastpos_p = -1;
+    int lr = -1, lp = -1;
     for (int j = j0; j < j1; ++j) {
-      const double rj = bits_d(load_coherent(&pr[j].x));
-      const double pj = bits_d(load_coherent(&pr[j].y));
-      rl += rj;
-      pl += pj;
-      if (rj > 0.0) lastpos_r = j;
-      if (pj > 0.0) lastpos_p = j;
+      const double2 m2 = s_cm[j];
+      rl += m2.x;
+      pl += m2.y;
+      if (m2.x > 0.0) lr = j;
+      if (m2.y > 0.0) lp = j;
     }
-    const double ri = wave_inclusive_scan(rl, lane), pi = wave_inclusive_scan(pl, lane);
-    const double rz = __shfl(ri, kWave - 1, kWave);
-    const bool usep = !(rz > 0.0);   // no residual mass left by round-off: draw from p
+    const double ri = wave_scan_incl(rl), pi = wave_scan_incl(pl);
+    const double zr = readlane_f64(ri, kWave - 1), zp = readlane_f64(pi, kWave - 1);
+    const bool usep = !(zr > 0.0);   // no residual mass left by round-off: draw from p
+    const double Z = usep ? zp : zr;
+    const double t = static_cast<double>(uni[static_cast<size_t>(b) * (K + 1) + K]) * Z;
     const double incl = usep ? pi : ri;
-    const double Z = usep ? __shfl(pi, kWave - 1, kWave) : rz;
-    const double t = u * Z;
-    double excl = __shfl_up(incl, 1, kWave);
-    if (lane == 0) excl = 0.0;
+    const double excl = wave_shift_up1(incl);
     const unsigned long long cross = __ballot(incl > t);
-    int cs = -1;
-    double cum = 0.0;
+    const int last_pos = group_reduce(usep ? lp : lr, kWave, OpMax{});
     if (cross) {
       const int L = __ffsll(static_cast<long long>(cross)) - 1;
       if (lane == L) {
-        cum = excl;
+        double cum = excl;
+        int cs = -1, lastp = -1;
         for (int j = j0; j < j1; ++j) {
-          const double mj = bits_d(load_coherent(usep ? &pr[j].y : &pr[j].x));
+          const double mj = usep ? s_cm[j].y : s_cm[j].x;
+          if (mj > 0.0) lastp = j;
           if (cum + mj > t) {
             cs = j;
             break;
           }
           cum += mj;
         }
-        if (cs < 0) cs = usep ? lastpos_p : lastpos_r;   // round-off inside this lane's chunks
-        if (cs < 0) cs = j1 - 1;
+        s_cs = cs >= 0 ? cs : max(lastp, 0);
+        s_fallback = cs >= 0 ? 0 : 1;
+        s_cb = cum;
       }
-      cs = __shfl(cs, L, kWave);
-      cum = __shfl(cum, L, kWave);
-    } else {   // round-off: the last chunk with positive mass (the chunk scan falls back too)
-      const int lp = wave_max(usep ? lastpos_p : lastpos_r);
-      cs = lp >= 0 ? lp : nchunk - 1;
+    } else if (lane == 0) {   // round-off: the last chunk of positive weight
+      s_cs = max(last_pos, 0);
+      s_fallback = 1;
+      s_cb = 0.0;
     }
     if (lane == 0) {
-      s_cs = cs;
       s_usep = usep ? 1 : 0;
-      s_cum = cum;
       s_t = t;
-      s_y = -1;
     }
   }
   __syncthreads();
+  if (s_cs != ch) return;
 
-  // ---- rescan the chosen chunk in token order (thread t: vectors t*kDrawVecs .. +kDrawVecs-1)
+  // ---- the chunk holding u*Z: the thread holding it (block prefix scan of the thread masses),
+  // then the token, from the vectors this workgroup still holds
   const bool use_p = s_usep != 0;
+  const bool fb = s_fallback != 0;
   const double t = s_t;
-  const ChunkRange cr = chunk_range(R.sp, s_cs, nchunk, cv);
-  uint4 qt[kDrawVecs], qd[kDrawVecs];
-#pragma unroll
-  for (int i = 0; i < kDrawVecs; ++i) {
-    const int v = cr.vbeg + tid * kDrawVecs + i;
-    load_pair(R, v, v < cr.vend, qt[i], qd[i]);
-  }
-  int lastpos = -1;   // last token of positive weight this thread saw (round-off fallback)
-
-  if (cr.first && tid == 0) {   // head elements come first
-    double cum = s_cum;
-    float p;
-    for (int e = 0; e < R.sp.head; ++e) {
-      const float we = weight_one(R, st, c, e, use_p, p);
-      if (we > 0.f) lastpos = e;
-      if (s_y < 0 && cum + static_cast<double>(we) > t) s_y = e;
-      cum += static_cast<double>(we);
-    }
-    s_cum = cum;
-  }
+  const float mine = use_p ? ps : ws;
+  const double wi = wave_scan_incl(static_cast<double>(mine));
+  if (lane == kWave - 1) s_red[0][w] = wi;
+  const int lpos = group_reduce(mine > 0.f ? tid : -1, kWave, OpMax{});
+  if (lane == 0) s_first[w] = lpos;
   __syncthreads();
-  double cum = s_cum;
-  if (s_y < 0) {   // uniform: read after a barrier
-    float wv[kDrawVecs][N];
-    float vs = 0.f;
+  double off = s_cb;
+  int last_thr = -1;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < w) off += s_red[0][i];
+    last_thr = max(last_thr, s_first[i]);
+  }
+  const double incl = off + wi;
+  const double excl = off + wave_shift_up1(wi);
+  const unsigned long long cross = fb ? 0ull : __ballot(incl > t);
+  __syncthreads();   // s_first is rewritten
+  if (lane == 0) s_first[w] = cross ? w * kWave + __ffsll(static_cast<long long>(cross)) - 1 : -1;
+  __syncthreads();
+  int first = -1;
+#pragma unroll
+  for (int i = kWaves - 1; i >= 0; --i)
+    if (s_first[i] >= 0) first = s_first[i];
+  const bool walk_fb = first < 0;   // round-off (or fallback): the last thread of positive mass
+  if (walk_fb) first = max(last_thr, 0);
+  if (tid == first) {   // hand this thread's vectors and prefix to wave 0
 #pragma unroll
     for (int i = 0; i < kDrawVecs; ++i) {
-      const int v = cr.vbeg + tid * kDrawVecs + i;
-      float pv[N];
-      if (v < cr.vend) {
-        weight_group(R, st, c, qt[i], qd[i], v, use_p, wv[i], pv);
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-          vs += wv[i][j];
-          if (wv[i][j] > 0.f) lastpos = R.sp.head + v * N + j;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < N; ++j) wv[i][j] = 0.f;
-      }
+      s_raw[0][4 * i] = qt[i].x;
+      s_raw[0][4 * i + 1] = qt[i].y;
+      s_raw[0][4 * i + 2] = qt[i].z;
+      s_raw[0][4 * i + 3] = qt[i].w;
+      s_raw[1][4 * i] = qd[i].x;
+      s_raw[1][4 * i + 1] = qd[i].y;
+      s_raw[1][4 * i + 2] = qd[i].z;
+      s_raw[1][4 * i + 3] = qd[i].w;
     }
-    double incl, excl, tot;
-    block_scan(static_cast<double>(vs), s_a, incl, excl, tot);
-    const bool crossv = cum + incl > t && vs > 0.f;
-    const unsigned long long bal = __ballot(crossv);
-    if (lane == 0) s_i[w] = bal ? w * kWave + __ffsll(static_cast<long long>(bal)) - 1 : -1;
-    __syncthreads();
-    if (tid == 0) {
-      int f = -1;
-      for (int i = kWaves - 1; i >= 0; --i)
-        if (s_i[i] >= 0) f = s_i[i];
-      s_first = f;
-    }
-    __syncthreads();
-    if (s_first >= 0 && tid == s_first) {
-      const double cb = cum + excl;
-      float psum = 0.f;
-      int y = -1, lp = -1;
-#pragma unroll
-      for (int i = 0; i < kDrawVecs; ++i) {
-        const int tok0 = R.sp.head + (cr.vbeg + tid * kDrawVecs + i) * N;
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-          psum += wv[i][j];
-          if (wv[i][j] > 0.f) lp = tok0 + j;
-          if (y < 0 && cb + static_cast<double>(psum) > t) y = tok0 + j;
-        }
-      }
-      s_y = y >= 0 ? y : lp;
-    }
-    cum += tot;
+    s_cb = excl;
   }
   __syncthreads();
 
-  if (s_y < 0 && cr.last && tid == 0) {   // tail elements come last
-    float p;
-    for (int e = R.sp.tail; e < V; ++e) {
-      const float we = weight_one(R, st, c, e, use_p, p);
-      if (we > 0.f) lastpos = e;
-      if (s_y < 0 && cum + static_cast<double>(we) > t) s_y = e;
-      cum += static_cast<double>(we);
+  // ---- wave 0: one element of that thread per lane (at most 7 + 32 + 7 for bf16), in token
+  // order, weights as in its mass, float64 prefix scan, first element past u*Z
+  if (w == 0) {
+    const ThreadElems fe = thread_elems(R.sp, V, nchunk, cv, ch, first);
+    const int nvel = fe.nv * N;
+    const bool has = lane < fe.nh + nvel + fe.nt;
+    int tok = 0;
+    float lt = -INFINITY, ld = -INFINITY;
+    if (has) {
+      if (lane < fe.nh || lane >= fe.nh + nvel) {   // scalar head or tail element
+        tok = lane < fe.nh ? lane : fe.tail0 + (lane - fe.nh - nvel);
+        lt = E::one(R.t, tok);
+        if (R.resid) ld = E::one(R.d, tok);
+      } else {
+        const int k = lane - fe.nh, i = k / N, e = k % N;
+        tok = R.sp.head + (fe.v0 + i) * N + e;
+        lt = E::from_words(&s_raw[0][4 * i], e);
+        if (R.resid) ld = R.d_aligned ? E::from_words(&s_raw[1][4 * i], e) : E::one(R.d, tok);
+      }
     }
-  }
-  __syncthreads();
-  if (s_y < 0) {   // round-off fallback: the last token of positive weight in the chunk
-    const int lp = wave_max(lastpos);
-    if (lane == 0) s_i[w] = lp;
-    __syncthreads();
-    if (tid == 0) {
-      int f = -1;
-      for (int i = 0; i < kWaves; ++i) f = max(f, s_i[i]);
-      s_y = f >= 0 ? f : 0;
+    float we = 0.f;
+    if (has) {
+      const float p = fast_exp2(fmaf(lt, c, -st.mc_t)) * st.inv_t;
+      we = (!R.resid || use_p) ? p : fmaxf(p - fast_exp2(fmaf(ld, c, -st.mc_d)) * st.inv_d, 0.f);
     }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    out_tok[static_cast<size_t>(b) * (K + 1) + st.m] = s_y;
-    reset_counter(cnt);
+    const double cum = s_cb + wave_scan_incl(static_cast<double>(we));
+    const unsigned long long pos = __ballot(we > 0.f);
+    const unsigned long long hit = walk_fb ? 0ull : __ballot(we > 0.f && cum > t);
+    int y;
+    if (hit) y = __shfl(tok, __ffsll(static_cast<long long>(hit)) - 1, kWave);
+    else if (pos) y = __shfl(tok, 63 - __clzll(static_cast<long long>(pos)), kWave);
+    else y = 0;   // no positive weight at all: only for rows without a finite logit
+    if (lane == 0) out_tok[static_cast<size_t>(b) * (K + 1) + st.m] = y;
   }
 }
 
@@ -594,34 +651,37 @@ template <typename TIn>
 int launch_sample(const void* target, const void* draft, const int32_t* xtok, const float* uni,
                   const int32_t* kv_in, int B, int K, int V, float T, int32_t* out_tok,
                   int32_t* out_tau, int32_t* out_kv, float* out_p, float* out_q, void* ws,
-                  hipStream_t stream, hipEvent_t* ev, const SamplePlan& P) {
+                  hipStream_t stream, hipEvent_t* ev, int wait_polls, const SamplePlan& P) {
   const size_t g1 = static_cast<size_t>(B) * (2 * K + 1) * P.stats.nchunk;
   const size_t g2 = static_cast<size_t>(B) * P.draw.nchunk;
-  if (!grid_fits(g1) || !grid_fits(g2) || P.draw.cv > kBlock * kDrawVecs) return SPEC_ERR_ARG;
+  if (!grid_fits(g1) || !grid_fits(g2) || P.draw.cv != kBlock * kDrawVecs ||
+      P.draw.nchunk > kMaxDrawChunks)
+    return SPEC_ERR_ARG;
   const WsLayout L = ws_layout(B, K, V, 1);
   const float c = exp2_scale(T);
   const TIn* t = static_cast<const TIn*>(target);
   const TIn* d = static_cast<const TIn*>(draft);
   float2* part1 = ws_ptr<float2>(ws, L.part_stats);
   float* gath = ws_ptr<float>(ws, L.gathered);
-  double2* part2 = ws_ptr<double2>(ws, L.part_draw);
-  unsigned* cnt2 = ws_ptr<unsigned>(ws, L.cnt_b);
+  uint64_t* cm = ws_ptr<uint64_t>(ws, L.part_draw);
+  const int nclear = static_cast<int>(g2 * 2);
   const dim3 grid1(static_cast<unsigned>(g1)), grid2(static_cast<unsigned>(g2)), block(kBlock);
   const int ns = P.stats.nchunk, cs = P.stats.cv, nd = P.draw.nchunk, cd = P.draw.cv;
+  const int polls = wait_polls < 0 ? SPEC_DEFAULT_WAIT_POLLS : wait_polls;
   if (ev == nullptr) {
     hipLaunchKernelGGL(sample_stats_kernel<TIn>, grid1, block, 0, stream, t, d, xtok, K, V, c, ns,
-                       cs, part1, gath);
+                       cs, part1, gath, cm, nclear);
     hipLaunchKernelGGL(sample_draw_kernel<TIn>, grid2, block, 0, stream, t, d, xtok, uni, kv_in,
                        K, V, c, ns, static_cast<const float2*>(part1),
-                       static_cast<const float*>(gath), nd, cd, part2, cnt2, out_tok, out_tau,
+                       static_cast<const float*>(gath), nd, cd, cm, polls, out_tok, out_tau,
                        out_kv, out_p, out_q);
   } else {
     // profiling: the runtime records the events at each kernel's start and end
     hipExtLaunchKernelGGL(sample_stats_kernel<TIn>, grid1, block, 0, stream, ev[0], ev[1], 0, t,
-                          d, xtok, K, V, c, ns, cs, part1, gath);
+                          d, xtok, K, V, c, ns, cs, part1, gath, cm, nclear);
     hipExtLaunchKernelGGL(sample_draw_kernel<TIn>, grid2, block, 0, stream, ev[2], ev[3], 0, t, d,
                           xtok, uni, kv_in, K, V, c, ns, static_cast<const float2*>(part1),
-                          static_cast<const float*>(gath), nd, cd, part2, cnt2, out_tok, out_tau,
+                          static_cast<const float*>(gath), nd, cd, cm, polls, out_tok, out_tau,
                           out_kv, out_p, out_q);
   }
   return launch_status();
@@ -632,7 +692,7 @@ int verify_sample_entry(const void* target_logits, const void* draft_logits, int
                         const int32_t* kv_len_in, int B, int K, int V, float temperature,
                         int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len, float* out_p,
                         float* out_q, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream, hipEvent_t* events) {
+                        hipStream_t stream, hipEvent_t* events, int wait_polls) {
   int rc = check_dtype(dtype);
   if (rc != SPEC_OK) return rc;
   if ((rc = check_dims(B, K, V)) != SPEC_OK) return rc;
@@ -650,11 +710,12 @@ int verify_sample_entry(const void* target_logits, const void* draft_logits, int
   if (dtype == SPEC_BF16)
     return launch_sample<uint16_t>(target_logits, draft_logits, draft_tokens, uniforms, kv_len_in,
                                    B, K, V, temperature, out_tokens, out_tau, out_kv_len, out_p,
-                                   out_q, workspace, stream, events,
+                                   out_q, workspace, stream, events, wait_polls,
                                    default_sample_plan<uint16_t>(B, K, V));
   return launch_sample<float>(target_logits, draft_logits, draft_tokens, uniforms, kv_len_in, B,
                               K, V, temperature, out_tokens, out_tau, out_kv_len, out_p, out_q,
-                              workspace, stream, events, default_sample_plan<float>(B, K, V));
+                              workspace, stream, events, wait_polls,
+                              default_sample_plan<float>(B, K, V));
 }
 
 }  // namespace
@@ -669,19 +730,18 @@ extern "C" int spec_verify_sample(const void* target_logits, const void* draft_l
   return sv::verify_sample_entry(target_logits, draft_logits, dtype, draft_tokens, uniforms,
                                  kv_len_in, B, K, V, temperature, out_tokens, out_tau,
                                  out_kv_len, out_p, out_q, workspace, workspace_bytes, stream,
-                                 nullptr);
+                                 nullptr, -1);
 }
 
-extern "C" int spec_verify_sample_timed(const void* target_logits, const void* draft_logits,
-                                        int dtype, const int32_t* draft_tokens,
-                                        const float* uniforms, const int32_t* kv_len_in, int B,
-                                        int K, int V, float temperature, int32_t* out_tokens,
-                                        int32_t* out_tau, int32_t* out_kv_len, float* out_p,
-                                        float* out_q, void* workspace, size_t workspace_bytes,
-                                        hipStream_t stream, hipEvent_t* events) {
-  if (events == nullptr) return SPEC_ERR_ARG;
+extern "C" int spec_verify_sample_ex(const void* target_logits, const void* draft_logits,
+                                     int dtype, const int32_t* draft_tokens,
+                                     const float* uniforms, const int32_t* kv_len_in, int B,
+                                     int K, int V, float temperature, int32_t* out_tokens,
+                                     int32_t* out_tau, int32_t* out_kv_len, float* out_p,
+                                     float* out_q, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream, hipEvent_t* events, int wait_polls) {
   return sv::verify_sample_entry(target_logits, draft_logits, dtype, draft_tokens, uniforms,
                                  kv_len_in, B, K, V, temperature, out_tokens, out_tau,
                                  out_kv_len, out_p, out_q, workspace, workspace_bytes, stream,
-                                 events);
+                                 events, wait_polls);
 }

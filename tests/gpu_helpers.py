@@ -53,7 +53,7 @@ def _np(t):
     return t.detach().cpu().numpy()
 
 
-def gpu_sample(wl, dev=None, ws=None):
+def gpu_sample(wl, dev=None, ws=None, wait_polls=None):
     dev = dev or upload(wl)
     B, K = wl.B, wl.K
     ws = ws if ws is not None else sv.new_workspace(B, K, wl.V)
@@ -61,7 +61,7 @@ def gpu_sample(wl, dev=None, ws=None):
                kv_len=poisoned((B,), torch.int32), p=poisoned((B, K), torch.float32),
                q=poisoned((B, K), torch.float32))
     sv.spec_verify_sample(dev["target"], dev["draft"], dev["tokens"], dev["uniforms"], dev["kv"],
-                          float(wl.T), ws, out=out)
+                          float(wl.T), ws, out=out, wait_polls=wait_polls)
     torch.cuda.synchronize()
     return {k: _np(v) for k, v in out.items()}
 

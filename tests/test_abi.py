@@ -45,6 +45,8 @@ def test_constants_match_header(lib):
     assert sv.SPEC_F32 == header_define("SPEC_F32") and sv.SPEC_BF16 == header_define("SPEC_BF16")
     assert sv.SPEC_MAX_K == header_define("SPEC_MAX_K")
     assert sv.SPEC_MAX_F == header_define("SPEC_MAX_F")
+    assert sv.SPEC_MAX_V == header_define("SPEC_MAX_V") == 1 << 22
+    assert sv.SPEC_DEFAULT_WAIT_POLLS == header_define("SPEC_DEFAULT_WAIT_POLLS")
     for code, name in sv.STATUS.items():
         assert header_define(name) == code
 
@@ -62,9 +64,10 @@ def test_workspace_bytes(lib):
     assert lib.spec_workspace_bytes(64, 4, 128256, 16) >= n
     assert lib.spec_workspace_bytes(256, 8, 152064, 1) > lib.spec_workspace_bytes(64, 4, 128256, 1)
     for bad in [(0, 4, 100, 1), (1, 0, 100, 1), (1, 65, 100, 1), (1, 4, 1, 1), (1, 4, 100, 0),
-                (1, 4, 100, 17), (1, 4, 3, 4)]:
+                (1, 4, 100, 17), (1, 4, 3, 4), (1, 4, sv.SPEC_MAX_V + 1, 1)]:
         assert lib.spec_workspace_bytes(*bad) == 0, bad
     assert lib.spec_workspace_bytes(1, 64, 2, 2) > 0
+    assert lib.spec_workspace_bytes(1, 4, sv.SPEC_MAX_V, 1) > 0
 
 
 FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: every call fails validation first
@@ -87,7 +90,7 @@ def test_sample_validation(lib):
     assert sample_call(lib, dtype=7) == code["SPEC_ERR_DTYPE"]
     for kw in [dict(B=0), dict(K=0), dict(K=65), dict(V=1), dict(t=NULL), dict(d=NULL),
                dict(x=NULL), dict(u=NULL), dict(tok=NULL), dict(tau=NULL), dict(t=FAKE_ODD),
-               dict(d=FAKE_ODD, dtype=0)]:
+               dict(d=FAKE_ODD, dtype=0), dict(V=sv.SPEC_MAX_V + 1)]:
         assert sample_call(lib, **kw) == code["SPEC_ERR_ARG"], kw
     for T in [0.0, -1.0, float("nan"), float("inf"), 1e-45]:
         assert sample_call(lib, T=T) == code["SPEC_ERR_TEMPERATURE"], T
@@ -95,6 +98,29 @@ def test_sample_validation(lib):
     assert sample_call(lib, ws=NULL, wsb=need) == code["SPEC_ERR_WORKSPACE"]
     assert sample_call(lib, wsb=need - 1) == code["SPEC_ERR_WORKSPACE"]
     assert sample_call(lib, ws=ctypes.c_void_p(0x10010), wsb=need) == code["SPEC_ERR_WORKSPACE"]
+
+
+def test_sample_ex_validation(lib):
+    code = {v: k for k, v in sv.STATUS.items()}
+    need = lib.spec_workspace_bytes(2, 4, 1000, 1)
+
+    def call(events, polls, **kw):
+        a = dict(t=FAKE, d=FAKE, dtype=1, x=FAKE, u=FAKE, kv=NULL, B=2, K=4, V=1000, T=1.0,
+                 tok=FAKE, tau=FAKE, kvo=NULL, p=NULL, q=NULL, ws=FAKE, wsb=0, s=NULL)
+        a.update(kw)
+        return lib.spec_verify_sample_ex(a["t"], a["d"], a["dtype"], a["x"], a["u"], a["kv"],
+                                         a["B"], a["K"], a["V"], a["T"], a["tok"], a["tau"],
+                                         a["kvo"], a["p"], a["q"], a["ws"], a["wsb"], a["s"],
+                                         events, polls)
+    # the same checks as spec_verify_sample, in the same order
+    assert call(NULL, -1, dtype=7) == code["SPEC_ERR_DTYPE"]
+    assert call(NULL, 0, K=65) == code["SPEC_ERR_ARG"]
+    assert call(NULL, 5, T=0.0) == code["SPEC_ERR_TEMPERATURE"]
+    assert call(NULL, -1) == code["SPEC_ERR_WORKSPACE"]
+    # an events array with a NULL handle is rejected once everything else is valid
+    events = (ctypes.c_void_p * 4)(1, 2, None, 4)
+    ws = ctypes.c_void_p(0x100000)   # 256-byte aligned, never dereferenced
+    assert call(ctypes.cast(events, ctypes.c_void_p), -1, ws=ws, wsb=need) == code["SPEC_ERR_ARG"]
 
 
 def test_greedy_validation(lib):

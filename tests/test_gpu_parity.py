@@ -133,6 +133,27 @@ def test_determinism_and_shared_workspace():
     assert g["tau"].min() >= 1
 
 
+@pytest.mark.parametrize("cid,B,V,rnd", [(3, 64, None, 21), (3, 8, 40000, 22), (1, 8, 1003, 23),
+                                         (4, 16, None, 24)])
+def test_draw_help_path_bit_identical(cid, B, V, rnd):
+    """wait_polls=0: every draw workgroup computes each chunk mass it does not find already
+    published, the path a workgroup takes when a partner of its request is late. The result
+    must equal the default path's bit for bit (and the oracle's). The C4 recipe has requests
+    whose draft rows equal the target rows, so the fallback to p is covered too."""
+    kw = dict(B=B) if V is None else dict(B=B, V=V)
+    wl = make_workload(cid, rnd, **kw)
+    dev = upload(wl)
+    ws = sv.new_workspace(wl.B, wl.K, wl.V)
+    announce(f"help path C{cid} B={wl.B} V={wl.V}")
+    a = gpu_sample(wl, dev=dev, ws=ws)
+    h = gpu_sample(wl, dev=dev, ws=ws, wait_polls=0)
+    b = gpu_sample(wl, dev=dev, ws=ws, wait_polls=1)
+    for k in a:
+        assert np.array_equal(a[k].view(np.int32), h[k].view(np.int32)), k
+        assert np.array_equal(a[k].view(np.int32), b[k].view(np.int32)), k
+    compare_sample(wl, h, requests=range(min(wl.B, 16)))
+
+
 # ------------------------------------------------------------------------------ the five configs
 def _rounds_sample(cid, rounds, mode):
     tot = flag = flag_bad = 0
