@@ -55,7 +55,7 @@ SV_HD inline KernelPlan plan_rows(int rows, int V, int epv, int resident, int ma
 // workgroups per CU at once, from the compiler's resource report for gfx950
 constexpr int kStatsResident = 8;
 constexpr int kGreedyResident = 8;
-constexpr int kPredictResident = 4;
+constexpr int kPredictResident = 8;
 
 SV_HD inline KernelPlan stats_plan(int B, int K, int V, int epv) {
   return plan_rows(B * (2 * K + 1), V, epv, kStatsResident);
@@ -72,9 +72,13 @@ SV_HD inline KernelPlan draw_plan(int B, int K, int V, int epv) {
 SV_HD inline KernelPlan greedy_plan(int B, int K, int V, int epv) {
   return plan_rows(B * (K + 1), V, epv, kGreedyResident);
 }
-// outcome keys keep a chunk in registers: one pass per chunk
+// outcome keys: a lane issues all its loads of a chunk at once (kPredictPasses rounds of
+// kVecPerThread vectors); each wave of a chunk publishes its own candidates and statistics for
+// its slot's merge
+constexpr int kPredictPasses = 2;
+constexpr int kPredictVecs = kPassVecs * kPredictPasses;
 SV_HD inline KernelPlan predict_plan(int B, int K, int V, int epv) {
-  return plan_rows(B * K, V, epv, kPredictResident, kPassVecs);
+  return plan_rows(B * K, V, epv, kPredictResident, kPredictVecs);
 }
 
 // per-request outcome of the slot scan, as the draw needs it
@@ -100,8 +104,9 @@ struct WsLayout {
   size_t part_stats; // 8 B [B*(2K+1)*nchunk]: chunk (max, scaled sum)
   size_t part_draw;  // 16 B [B*nchunk]: published chunk (residual mass, target mass)
   size_t part_greedy;// 8 B [B*(K+1)*nchunk]: chunk (max, lowest index)
-  size_t part_topf;  // 8 B [B*K*nchunk*F]: chunk top-F lists
-  size_t part_pstat; // 8 B [B*K*nchunk]
+  size_t part_topf;  // 8 B [B*K*nchunk*4*kWaveSlots]: each wave's candidate list
+  size_t part_pcnt;  // 4 B [B*K*nchunk*4]: entries in each wave's list
+  size_t part_pstat; // 8 B [B*K*nchunk*4]: each wave's (max, scaled sum)
   size_t total;
 };
 
@@ -137,9 +142,11 @@ inline WsLayout ws_layout(int B, int K, int V, int F) {
   L.part_greedy = off;
   off = align256(off + 8 * b * (k + 1) * ng);
   L.part_topf = off;
-  off = align256(off + 8 * b * k * np * static_cast<size_t>(F));
+  off = align256(off + 8 * b * k * np * 4 * 16);
+  L.part_pcnt = off;
+  off = align256(off + 4 * b * k * np * 4);
   L.part_pstat = off;
-  off = align256(off + 8 * b * k * np);
+  off = align256(off + 8 * b * k * np * 4);
   L.total = off;
   return L;
 }

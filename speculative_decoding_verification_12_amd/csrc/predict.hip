@@ -7,64 +7,57 @@
 // token)). For every draft slot k the F tokens with the largest draft logits, ordered by logit
 // descending then id ascending, are the keys (k, t); at T > 0 each key also gets q_k(t).
 //
-// One launch: a workgroup per (request, slot, chunk of at most 1024 16-byte vectors). Each thread holds
-// its 8..34 elements in registers for one pass. Exact top-F of the chunk without sorting it:
-//   1. every wave picks its F largest lane maxima; theta = the largest of the waves' F-th values.
-//      Some wave then holds F elements >= theta, so every element of the chunk's top F is
-//      >= theta and lives in a lane whose maximum is >= theta;
-//   2. only those candidate lanes (a handful) copy their elements to LDS;
-//   3. one wave selects the top F among the candidates by F rounds of (value, id) argmax, each
-//      round excluding everything at or before the previous pick in that order.
-// At T > 0 the same pass also keeps the online (max, scaled sum) for the key probabilities. The
-// slot's last workgroup to arrive merges the chunks' lists and statistics.
+// One launch: a workgroup of four independent waves per (request, slot, chunk of at most
+// kPredictVecs 16-byte vectors). Lane t of wave w reads vectors vbeg + p*1024 + i*256 + 64w + t
+// (pass p < kPredictPasses, i < 4), all issued at once, plus one head and one tail element.
+// Each wave works on its own, with no LDS and no barriers:
+//   1. the lane maximum, and at T > 0 the lane's online sum of 2^(l*c - fl(m*c)) against its
+//      running max m (one exp per element), reduced to the wave's (max, sum);
+//   2. theta: the wave's F-th largest lane maximum, ties counted. F lanes hold an element
+//      >= theta, so every element of the wave's top F is >= theta, and only lanes whose maximum
+//      reaches theta can hold one: usually a handful;
+//   3. those lanes' elements are read again (cache hits), one element per lane of the wave; the
+//      elements >= theta are numbered by ballot and published as the wave's candidate list.
+//      More than kWaveSlots of them (ties at theta) and the wave publishes its exact top F
+//      instead, merging the qualifying lanes' elements one lane at a time by F rounds of
+//      (value, id) argmax.
+// The wave counts itself in on the slot's counter; the slot's last wave selects the F best of all
+// published lists by F rounds of argmax, each excluding everything at or before the previous
+// pick in the order (value desc, id asc), and writes the keys and q_k(key).
 #include "api_common.hpp"
 #include "spec_common.hpp"
 
 namespace sv {
 namespace {
 
-constexpr int kCandSlots = 16;   // candidate lanes copied to LDS per batch
 constexpr int kSentinelId = 0x7fffffff;
+constexpr int kWaveSlots = 16;  // candidates a wave publishes before falling back to its top F
+constexpr int kListSlots = 16;  // entries of a wave's list: kWaveSlots, or F <= SPEC_MAX_F
 
 // after (pv, pi) in the order (value desc, id asc)
 __device__ __forceinline__ bool after(float v, int i, float pv, int pi) {
   return v < pv || (v == pv && i > pi);
 }
 
-template <int n>
-__device__ __forceinline__ void absorb_stats(const float (&v)[n], float c, float& m, float& s) {
-  float bm = v[0];
-#pragma unroll
-  for (int j = 1; j < n; ++j) bm = fmaxf(bm, v[j]);
-  if (bm > m) {
-    s *= fast_exp2(m * c - bm * c);
-    m = bm;
-  }
-  if (m > -INFINITY) {
-    const float mc = m * c;
-#pragma unroll
-    for (int j = 0; j < n; ++j) s += fast_exp2(fmaf(v[j], c, -mc));
-  }
+// index of the n-th (0-based) set bit of a uniform mask, -1 if there are fewer
+__device__ __forceinline__ int nth_bit(unsigned long long m, int n) {
+  for (int i = 0; i < n && m != 0ull; ++i) m &= m - 1ull;
+  return m != 0ull ? __ffsll(static_cast<long long>(m)) - 1 : -1;
 }
 
 template <typename TIn>
-__global__ __launch_bounds__(kBlock) void predict_kernel(
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void predict_kernel(
     const TIn* __restrict__ drf, int K, int V, int F, float c, int nchunk, int cv,
-    ArgPart* __restrict__ part, float2* __restrict__ pstat, unsigned* __restrict__ cnt_base,
-    int32_t* __restrict__ out_keys, float* __restrict__ out_prob) {
+    ArgPart* __restrict__ part, int* __restrict__ pcnt, float2* __restrict__ pstat,
+    unsigned* __restrict__ cnt_base, int32_t* __restrict__ out_keys,
+    float* __restrict__ out_prob) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
-  constexpr int kPer = kVecPerThread * N + 2;                         // elements a lane holds
-  constexpr int kSel = (kCandSlots * kPer + kWave - 1) / kWave;       // per selecting lane
-  __shared__ uint4 c_vec[kCandSlots][kVecPerThread];
-  __shared__ float c_ext[kCandSlots][2];
-  __shared__ int c_tid[kCandSlots];
-  __shared__ float l_v[SPEC_MAX_F];
-  __shared__ int l_i[SPEC_MAX_F];
-  __shared__ float s_theta[kWaves];
-  __shared__ int s_cnt[kWaves];
-  __shared__ float sm[kWaves], ss[kWaves];
-  __shared__ int s_flag;
+  constexpr int kVecs = kPredictPasses * kVecPerThread;   // vectors a lane reads
+  constexpr int kLaneElems = kVecs * N;                    // their elements (64 or 32)
+  constexpr int kGroups = kWave / kLaneElems;              // qualifying lanes per re-read (1 or 2)
+  static_assert(kWave % kLaneElems == 0, "a lane's elements fit the wave");
+  static_assert(SPEC_MAX_F <= kListSlots && kWaveSlots <= kListSlots, "list sizes");
 
   const int ch = blockIdx.x % nchunk;
   const int rk = blockIdx.x / nchunk;   // b * K + k
@@ -72,207 +65,251 @@ __global__ __launch_bounds__(kBlock) void predict_kernel(
   unsigned* cnt = cnt_base + static_cast<size_t>(rk) * kCounterStride;
   const TIn* row = drf + static_cast<size_t>(rk) * static_cast<size_t>(V);
   const RowSpan sp = row_span(row, V);
-  const ChunkRange cr = chunk_range(sp, ch, nchunk, cv);   // cv <= one pass (kPassVecs)
+  const ChunkRange cr = chunk_range(sp, ch, nchunk, cv);   // cv <= kPredictVecs
+  // vector v (0..kVecs-1) of lane tid
+  auto vec_index = [&](int v, int t) { return cr.vbeg + v * kBlock + t; };
 
-  // ---- load the lane's elements (one pass; padding is -inf)
-  uint4 q[kVecPerThread];
+  // ---- the lane's elements, all loads in flight at once (padding is -inf)
+  uint4 q[kVecs];
   const uint4* vrow = reinterpret_cast<const uint4*>(row + sp.head);
 #pragma unroll
-  for (int i = 0; i < kVecPerThread; ++i) {
-    const int vi = cr.vbeg + i * kBlock + tid;
-    q[i] = vi < cr.vend ? vrow[vi] : neg_inf_vec<TIn>();
+  for (int v = 0; v < kVecs; ++v) {
+    const int vi = vec_index(v, tid);
+    q[v] = vi < cr.vend ? vrow[vi] : neg_inf_vec<TIn>();
   }
   const bool has_head = cr.first && tid < sp.head;
   const bool has_tail = cr.last && tid < V - sp.tail;
-  float ext[2];
-  ext[0] = has_head ? E::one(row, tid) : -INFINITY;
-  ext[1] = has_tail ? E::one(row, sp.tail + tid) : -INFINITY;
+  const float eh = has_head ? E::one(row, tid) : -INFINITY;
+  const float et = has_tail ? E::one(row, sp.tail + tid) : -INFINITY;
   const bool has = has_head || has_tail || (cr.vbeg + tid < cr.vend);
 
-  float v[kVecPerThread * N];
+  // lane maximum, and at T > 0 the online sum of 2^(l*c - fl(m*c)) against the running max m
+  float tm = fmaxf(eh, et), s = 0.f;
+  if (c > 0.f && tm > -INFINITY) {
+    const float mc = tm * c;
+    s = fast_exp2(fmaf(eh, c, -mc)) + fast_exp2(fmaf(et, c, -mc));
+  }
 #pragma unroll
-  for (int i = 0; i < kVecPerThread; ++i) {
+  for (int v = 0; v < kVecs; ++v) {
     float t[N];
-    E::unpack(q[i], t);
+    E::unpack(q[v], t);
+    float bm = t[0];
 #pragma unroll
-    for (int j = 0; j < N; ++j) v[i * N + j] = t[j];
+    for (int j = 1; j < N; ++j) bm = fmaxf(bm, t[j]);
+    if (c > 0.f) {
+      if (bm > tm) {
+        s *= fast_exp2(tm * c - bm * c);   // s is 0 while tm is -inf
+        tm = bm;
+      }
+      if (tm > -INFINITY) {
+        const float mc = tm * c;
+#pragma unroll
+        for (int j = 0; j < N; ++j) s += fast_exp2(fmaf(t[j], c, -mc));
+      }
+    } else {
+      tm = fmaxf(tm, bm);
+    }
   }
-  float tm = fmaxf(ext[0], ext[1]);
-#pragma unroll
-  for (int j = 0; j < kVecPerThread * N; ++j) tm = fmaxf(tm, v[j]);
-
-  // ---- statistics for q_k(key) at T > 0
-  float M = -INFINITY, S = 0.f;
-  if (c > 0.f) {
-    float m = -INFINITY, s = 0.f;
-    absorb_stats(ext, c, m, s);
-    absorb_stats(v, c, m, s);
-    const float wm = wave_max(m);
-    const float sc = (m > -INFINITY) ? s * fast_exp2(m * c - wm * c) : 0.f;
+  const size_t pw = (static_cast<size_t>(rk) * nchunk + ch) * kWaves + w;   // this wave's list
+  if (c > 0.f) {   // the wave's (max, scaled sum) for q_k(key)
+    const float wm = wave_max(tm);
+    const float sc = (tm > -INFINITY) ? s * fast_exp2(tm * c - wm * c) : 0.f;
     const float wsum = wave_sum(sc);
-    if (lane == 0) {
-      sm[w] = wm;
-      ss[w] = wsum;
-    }
+    if (lane == 0) store_coherent(&pstat[pw], pack2(wm, wsum));
   }
 
-  // ---- theta: each wave's F-th largest lane maximum (lanes without elements never count)
+  // ---- theta: the wave's F-th largest lane maximum, ties counted (-inf when fewer than F
+  // lanes hold elements)
+  float theta = -INFINITY;
   {
-    float kv = has ? tm : -INFINITY;
-    int ki = has ? lane : kSentinelId;
-    float th = -INFINITY;
-    int thi = kSentinelId;
-    for (int f = 0; f < F; ++f) {
-      float bv = kv;
-      int bi = ki;
-      wave_argmax(bv, bi);
-      th = bv;
-      thi = bi;
-      if (bi == lane) {   // the winning lane leaves the race
-        kv = -INFINITY;
-        ki = kSentinelId;
+    float cur = has ? tm : -INFINITY;
+    bool in = has;
+    int need = F;
+    while (need > 0) {   // uniform: every quantity below is wave-wide
+      if (__ballot(in) == 0ull) {
+        theta = -INFINITY;
+        break;
       }
+      const float mx = wave_max(in ? cur : -INFINITY);
+      const bool at = in && cur == mx;
+      need -= __popcll(__ballot(at));
+      theta = mx;
+      if (at) in = false;
     }
-    if (lane == 0) s_theta[w] = (thi == kSentinelId) ? -INFINITY : th;
-  }
-  __syncthreads();
-  float theta = s_theta[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) theta = fmaxf(theta, s_theta[i]);
-
-  if (c > 0.f && tid == 0) {
-    M = sm[0];
-    for (int i = 1; i < kWaves; ++i) M = fmaxf(M, sm[i]);
-    for (int i = 0; i < kWaves; ++i)
-      if (sm[i] > -INFINITY) S += ss[i] * fast_exp2(sm[i] * c - M * c);
   }
 
-  // ---- candidate lanes and their rank in (wave, lane) order
-  const bool cand = has && tm >= theta;
-  const unsigned long long bal = __ballot(cand);
-  if (lane == 0) s_cnt[w] = __popcll(bal);
-  if (tid < SPEC_MAX_F) {
-    l_v[tid] = -INFINITY;
-    l_i[tid] = kSentinelId;
+  // ---- candidates: elements >= theta of the qualifying lanes, numbered by ballot. Lane j reads
+  // element j % kLaneElems of the (j / kLaneElems)-th qualifying lane of a batch.
+  ArgPart* list = part + pw * kListSlots;
+  int count = 0;   // uniform
+  auto publish = [&](bool cand, float v, int id) {
+    const unsigned long long bal = __ballot(cand);
+    const int slot = count + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                 static_cast<uint32_t>(bal >> 32),
+                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u)));
+    if (cand && slot < kWaveSlots) store_coherent(&list[slot], pack2(v, id));
+    count += __popcll(bal);
+  };
+  const int g = lane / kLaneElems, e = lane % kLaneElems;
+  const int ev_ = e / N, el = e % N;   // the element this lane reads: vector ev_, element el
+  // the qualifying lane L's element read by this lane: (in range, value, id)
+  auto reread = [&](int L, bool& ok, float& v, int& id) {
+    const int vi = vec_index(ev_, w * kWave + L);
+    ok = L >= 0 && vi < cr.vend;
+    id = sp.head + vi * N + el;
+    v = ok ? E::one(row, id) : -INFINITY;
+  };
+  const unsigned long long qual0 = __ballot(has && tm >= theta);
+  publish(has_head && eh >= theta, eh, tid);
+  unsigned long long qual = qual0;
+  while (qual != 0ull) {   // uniform; kGroups qualifying lanes per read
+    bool ok;
+    float v;
+    int id;
+    reread(nth_bit(qual, g), ok, v, id);
+    publish(ok && v >= theta, v, id);
+    for (int r = 0; r < kGroups && qual != 0ull; ++r) qual &= qual - 1ull;
   }
-  __syncthreads();
-  int rank = __popcll(bal & ((1ull << lane) - 1ull));
-  int ncand = 0;
-  for (int i = 0; i < kWaves; ++i) {
-    if (i < w) rank += s_cnt[i];
-    ncand += s_cnt[i];
-  }
+  publish(has_tail && et >= theta, et, sp.tail + tid);
 
-  for (int b0 = 0; b0 < ncand; b0 += kCandSlots) {
-    if (cand && rank >= b0 && rank < b0 + kCandSlots) {
-      const int sl = rank - b0;
-#pragma unroll
-      for (int i = 0; i < kVecPerThread; ++i) c_vec[sl][i] = q[i];
-      c_ext[sl][0] = ext[0];
-      c_ext[sl][1] = ext[1];
-      c_tid[sl] = tid;
-    }
-    __syncthreads();
-    if (w == 0) {
-      const int nslot = min(kCandSlots, ncand - b0);
-      // decode this lane's share of the candidate elements once
-      float ev[kSel + 1];
-      int ei[kSel + 1];
-#pragma unroll
-      for (int s = 0; s < kSel; ++s) {
-        const int e = lane + s * kWave;
-        const int sl = e / kPer, wi = e % kPer;
-        float val = -INFINITY;
-        int id = kSentinelId;
-        if (sl < nslot) {
-          const int ct = c_tid[sl];
-          if (wi < kVecPerThread * N) {
-            const int i = wi / N, j = wi % N;
-            const int vi = cr.vbeg + i * kBlock + ct;
-            if (vi < cr.vend) {
-              val = E::from_words(reinterpret_cast<const uint32_t*>(&c_vec[sl][i]), j);
-              id = sp.head + vi * N + j;
-            }
-          } else if (wi == kVecPerThread * N) {
-            if (cr.first && ct < sp.head) {
-              val = c_ext[sl][0];
-              id = ct;
-            }
-          } else if (cr.last && ct < V - sp.tail) {
-            val = c_ext[sl][1];
-            id = sp.tail + ct;
-          }
-        }
-        ev[s] = val;
-        ei[s] = id;
-      }
-      // the running list from earlier batches competes too
-      ev[kSel] = lane < F ? l_v[lane] : -INFINITY;
-      ei[kSel] = lane < F ? l_i[lane] : kSentinelId;
-      float pv = INFINITY;
-      int pi = -1;
+  if (count > kWaveSlots) {
+    // ---- ties at theta: the wave's exact top F, kept in lanes 0..F-1 and merged with each
+    // qualifying lane's elements (and the head/tail elements) by F rounds of argmax
+    float my_v = -INFINITY;
+    int my_i = kSentinelId;
+    auto merge_in = [&](float v, int id) {   // v, id: this lane's contender (or -inf)
+      float pv = INFINITY, nv = -INFINITY;
+      int pi = -1, ni = kSentinelId;
+      const float hv = lane < F ? my_v : -INFINITY;
+      const int hi = lane < F ? my_i : kSentinelId;
       for (int f = 0; f < F; ++f) {
         float bv = -INFINITY;
         int bi = kSentinelId;
-#pragma unroll
-        for (int s = 0; s <= kSel; ++s)
-          if (after(ev[s], ei[s], pv, pi) && better(ev[s], ei[s], bv, bi)) {
-            bv = ev[s];
-            bi = ei[s];
-          }
+        if (after(v, id, pv, pi) && better(v, id, bv, bi)) {
+          bv = v;
+          bi = id;
+        }
+        if (after(hv, hi, pv, pi) && better(hv, hi, bv, bi)) {
+          bv = hv;
+          bi = hi;
+        }
         wave_argmax(bv, bi);
         pv = bv;
         pi = bi;
-        if (lane == 0) {
-          l_v[f] = bv;
-          l_i[f] = bi;
+        if (lane == f) {
+          nv = bv;
+          ni = bi;
         }
       }
+      my_v = nv;
+      my_i = ni;
+    };
+    merge_in(has_head && eh >= theta ? eh : -INFINITY, has_head && eh >= theta ? tid : kSentinelId);
+    merge_in(has_tail && et >= theta ? et : -INFINITY,
+             has_tail && et >= theta ? sp.tail + tid : kSentinelId);
+    for (unsigned long long qm = qual0; qm != 0ull;) {   // uniform
+      bool ok;
+      float v;
+      int id;
+      reread(nth_bit(qm, g), ok, v, id);
+      const bool cand = ok && v >= theta;
+      merge_in(cand ? v : -INFINITY, cand ? id : kSentinelId);
+      for (int r = 0; r < kGroups && qm != 0ull; ++r) qm &= qm - 1ull;
     }
-    __syncthreads();
+    if (lane < F) store_coherent(&list[lane], pack2(my_v, my_i));
+    count = F;
   }
+  if (lane == 0) store_coherent_u32(&pcnt[pw], static_cast<uint32_t>(count));
 
-  // ---- publish the chunk's list and statistics
-  const size_t pc = static_cast<size_t>(rk) * nchunk + ch;
-  if (tid < F) store_coherent(&part[pc * F + tid], pack2(l_v[tid], l_i[tid]));
-  if (tid == 0 && c > 0.f) store_coherent(&pstat[pc], pack2(M, S));
-  if (!arrive_last(cnt, static_cast<unsigned>(nchunk), &s_flag)) return;
+  // ---- count this wave in; the slot's last wave merges
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's stores are at the coherence point
+  unsigned prev = 0;
+  if (lane == 0)
+    prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  const int nl = nchunk * kWaves;   // lists of this slot
+  if (prev != static_cast<unsigned>(nl) - 1u) return;
 
-  // ---- last workgroup of the slot: merge the chunks' lists
-  if (w != 0) return;
-  const ArgPart* pr = part + static_cast<size_t>(rk) * nchunk * F;
-  const int total = nchunk * F;
-  float pv = INFINITY;
-  int pi = -1;
+  const size_t p0 = static_cast<size_t>(rk) * nchunk * kWaves;
   float Mr = -INFINITY;
   double Sr = 0.0;
   if (c > 0.f) {
-    const float2* ps = pstat + static_cast<size_t>(rk) * nchunk;
+    constexpr int kHeldStats = 4;   // wave statistics a lane keeps between the two passes
+    float hm[kHeldStats], hs[kHeldStats];
     float lm = -INFINITY;
-    for (int j = lane; j < nchunk; j += kWave) lm = fmaxf(lm, lo_float(load_coherent(&ps[j])));
+#pragma unroll
+    for (int h = 0; h < kHeldStats; ++h) {
+      const int j = lane + h * kWave;
+      const uint64_t st = j < nl ? load_coherent(&pstat[p0 + j]) : pack2(-INFINITY, 0.f);
+      hm[h] = lo_float(st);
+      hs[h] = hi_float(st);
+      lm = fmaxf(lm, hm[h]);
+    }
+    for (int j = lane + kHeldStats * kWave; j < nl; j += kWave)
+      lm = fmaxf(lm, lo_float(load_coherent(&pstat[p0 + j])));
     Mr = wave_max(lm);
     const float mc = Mr * c;
     double ls = 0.0;
-    for (int j = lane; j < nchunk; j += kWave) {
-      const uint64_t st = load_coherent(&ps[j]);
-      if (lo_float(st) > -INFINITY) {
-        const float qc = lo_float(st) * c;
-        ls += static_cast<double>(hi_float(st)) *
-              exp2(static_cast<double>(qc) - static_cast<double>(mc));
-      }
+#pragma unroll
+    for (int h = 0; h < kHeldStats; ++h)
+      if (hm[h] > -INFINITY) ls += static_cast<double>(hs[h]) * fast_exp2(hm[h] * c - mc);
+    for (int j = lane + kHeldStats * kWave; j < nl; j += kWave) {
+      const uint64_t st = load_coherent(&pstat[p0 + j]);
+      if (lo_float(st) > -INFINITY)
+        ls += static_cast<double>(hi_float(st)) * fast_exp2(lo_float(st) * c - mc);
     }
     Sr = wave_sum(ls);
   }
+
+  // The slot's lists are adjacent: nl lists of kListSlots entries. Entry g (list g / kListSlots,
+  // position g % kListSlots) is valid below its list's count. Lane l holds entries l + 64h for
+  // h < kHeld in registers (coalesced reads); a slot with more lists re-reads the rest every round.
+  constexpr int kHeld = 8;
+  const int total = nl * kListSlots;
+  const ArgPart* lists = part + p0 * kListSlots;
+  const int my_cnt = lane < nl ? min(static_cast<int>(load_coherent_u32(&pcnt[p0 + lane])), kListSlots)
+                               : 0;   // lane l: count of list l (l < 64)
+  float ev[kHeld];
+  int ei[kHeld];
+#pragma unroll
+  for (int h = 0; h < kHeld; ++h) {
+    const int gi = lane + h * kWave;
+    const uint64_t a = gi < total ? load_coherent(&lists[gi]) : pack2(-INFINITY, kSentinelId);
+    ev[h] = lo_float(a);
+    ei[h] = hi_int(a);
+  }
+#pragma unroll
+  for (int h = 0; h < kHeld; ++h) {   // lists 0..63 are covered by the counts in the lanes
+    const int gi = lane + h * kWave;
+    const int j = gi / kListSlots;
+    const int cj = __shfl(my_cnt, j < kWave ? j : 0, kWave);
+    if (!(gi < total && j < kWave && gi % kListSlots < cj)) {
+      ev[h] = -INFINITY;
+      ei[h] = kSentinelId;
+    }
+  }
+  const bool more = total > kHeld * kWave;   // uniform
+  float pv = INFINITY;
+  int pi = -1;
   for (int f = 0; f < F; ++f) {
     float bv = -INFINITY;
     int bi = kSentinelId;
-    for (int j = lane; j < total; j += kWave) {
-      const uint64_t a = load_coherent(&pr[j]);
-      const float av = lo_float(a);
-      const int ai = hi_int(a);
-      if (after(av, ai, pv, pi) && better(av, ai, bv, bi)) {
-        bv = av;
-        bi = ai;
+    auto consider = [&](float v, int id) {
+      if (after(v, id, pv, pi) && better(v, id, bv, bi)) {
+        bv = v;
+        bi = id;
+      }
+    };
+#pragma unroll
+    for (int h = 0; h < kHeld; ++h) consider(ev[h], ei[h]);
+    if (more) {   // entries beyond the registers (and lists past the 64th, with their counts)
+      for (int gi = lane + kHeld * kWave; gi < total; gi += kWave) {
+        const int j = gi / kListSlots;
+        const int cj = min(static_cast<int>(load_coherent_u32(&pcnt[p0 + j])), kListSlots);
+        if (gi % kListSlots < cj) {
+          const uint64_t a = load_coherent(&lists[gi]);
+          consider(lo_float(a), hi_int(a));
+        }
       }
     }
     wave_argmax(bv, bi);
@@ -283,13 +320,11 @@ __global__ __launch_bounds__(kBlock) void predict_kernel(
       out_keys[o] = bi;
       if (out_prob) {
         float pr_f;
-        if (c > 0.f) {
-          const float mc = Mr * c;
+        if (c > 0.f)
           pr_f = static_cast<float>(
-              exp(kLn2 * (static_cast<double>(bv) * c - static_cast<double>(mc))) / Sr);
-        } else {
+              exp2_wide(static_cast<double>(bv) * c - static_cast<double>(Mr * c)) / Sr);
+        else
           pr_f = f == 0 ? 1.f : 0.f;
-        }
         out_prob[o] = pr_f;
       }
     }
@@ -300,14 +335,15 @@ __global__ __launch_bounds__(kBlock) void predict_kernel(
 template <typename TIn>
 int launch_predict(const void* draft, int B, int K, int V, int F, float T, int32_t* out_keys,
                    float* out_prob, void* ws, hipStream_t stream, const KernelPlan& P) {
-  if (P.cv > kPassVecs) return SPEC_ERR_ARG;   // a chunk must fit one register-resident pass
+  if (P.cv > kPredictVecs) return SPEC_ERR_ARG;   // a chunk is one round of loads per lane
   const size_t g = static_cast<size_t>(B) * K * P.nchunk;
   if (!grid_fits(g)) return SPEC_ERR_ARG;
   const WsLayout L = ws_layout(B, K, V, F);
   const float c = T > 0.f ? exp2_scale(T) : 0.f;
   hipLaunchKernelGGL(predict_kernel<TIn>, dim3(static_cast<unsigned>(g)), dim3(kBlock), 0, stream,
                      static_cast<const TIn*>(draft), K, V, F, c, P.nchunk, P.cv,
-                     ws_ptr<ArgPart>(ws, L.part_topf), ws_ptr<float2>(ws, L.part_pstat),
+                     ws_ptr<ArgPart>(ws, L.part_topf), ws_ptr<int>(ws, L.part_pcnt),
+                     ws_ptr<float2>(ws, L.part_pstat),
                      ws_ptr<unsigned>(ws, L.cnt_a), out_keys, out_prob);
   return launch_status();
 }

@@ -102,77 +102,6 @@ __device__ __forceinline__ ChunkRange chunk_range(const RowSpan& sp, int ch, int
   return c;
 }
 
-// ------------------------------------------------------------------------------ wave reductions
-// xor-butterfly reductions: every lane ends with the same value, combined in a fixed order, so
-// results are deterministic run to run.
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-__device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
-__device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
-// reductions inside aligned segments of `width` lanes (a power of two <= 64)
-__device__ __forceinline__ float seg_max(float v, int width) {
-  for (int o = width / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
-__device__ __forceinline__ double seg_sum(double v, int width) {
-  for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-// (value, index) ordered by value descending, then index ascending
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
-}
-
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o, kWave);
-    const int oi = __shfl_xor(i, o, kWave);
-    if (better(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
-    }
-  }
-}
-
-// inclusive prefix sum over the 64 lanes in lane order
-__device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double n = __shfl_up(v, o, kWave);
-    if (lane >= o) v += n;
-  }
-  return v;
-}
-
 // ------------------------------------------------------------------------------ DPP lane moves
 // Data-parallel-primitive moves read another lane's register inside the vector ALU, with no LDS
 // round trip (a ds_bpermute shuffle costs an LDS access per step). GFX9 control encodings; all
@@ -284,6 +213,70 @@ __device__ __forceinline__ double wave_shift_up1(double x) {
   return dpp_f64<dpp::kWaveShr1, 0xf, true>(0.0, x);
 }
 
+// ------------------------------------------------------------------------------ wave reductions
+// Whole-wave reductions on DPP moves: every lane ends with the same value, combined in a fixed
+// order, so results are deterministic run to run.
+__device__ __forceinline__ float wave_max(float v) { return group_reduce(v, kWave, OpMax{}); }
+__device__ __forceinline__ float wave_sum(float v) { return group_reduce(v, kWave, OpAdd{}); }
+__device__ __forceinline__ double wave_sum(double v) { return group_reduce(v, kWave, OpAdd{}); }
+__device__ __forceinline__ int wave_max(int v) { return group_reduce(v, kWave, OpMax{}); }
+
+// (value, index) ordered by value descending, then index ascending
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// Wave-wide best (value, index) in that order; every lane gets it. Indices must be distinct
+// among lanes with equal values (or the pairs equal), which makes the order total.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  auto step = [&](auto ctrl_tag) {
+    constexpr int ctrl = decltype(ctrl_tag)::value;
+    const float ov = dpp_f32<ctrl>(v, v);
+    const int oi = static_cast<int>(dpp_u32<ctrl>(static_cast<uint32_t>(i), static_cast<uint32_t>(i)));
+    if (better(ov, oi, v, i)) {
+      v = ov;
+      i = oi;
+    }
+  };
+  step(std::integral_constant<int, dpp::kQuadXor1>{});
+  step(std::integral_constant<int, dpp::kQuadXor2>{});
+  step(std::integral_constant<int, dpp::kRowHalfMirror>{});
+  step(std::integral_constant<int, dpp::kRowMirror>{});
+  float bv = readlane_f32(v, 0);
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float rv = readlane_f32(v, 16 * r);
+    const int ri = __builtin_amdgcn_readlane(i, 16 * r);
+    if (better(rv, ri, bv, bi)) {
+      bv = rv;
+      bi = ri;
+    }
+  }
+  v = bv;
+  i = bi;
+}
+
+// Inclusive prefix sum of ints over the 64 lanes in lane order.
+__device__ __forceinline__ int wave_scan_incl(int x) {
+  x += static_cast<int>(dpp_u32<dpp::kRowShr + 1, 0xf, true>(0u, static_cast<uint32_t>(x)));
+  x += static_cast<int>(dpp_u32<dpp::kRowShr + 2, 0xf, true>(0u, static_cast<uint32_t>(x)));
+  x += static_cast<int>(dpp_u32<dpp::kRowShr + 4, 0xf, true>(0u, static_cast<uint32_t>(x)));
+  x += static_cast<int>(dpp_u32<dpp::kRowShr + 8, 0xf, true>(0u, static_cast<uint32_t>(x)));
+  x += static_cast<int>(dpp_u32<dpp::kRowBcast15, 0xa, false>(0u, static_cast<uint32_t>(x)));
+  x += static_cast<int>(dpp_u32<dpp::kRowBcast31, 0xc, false>(0u, static_cast<uint32_t>(x)));
+  return x;
+}
+
+// 2^x for a float64 exponent, to about 2e-7 relative: the integer part scales exactly, the
+// fraction goes through the hardware exp2. x = -inf gives 0.
+__device__ __forceinline__ double exp2_wide(double x) {
+  if (!(x > -1074.0)) return 0.0;
+  if (x >= 1024.0) return INFINITY;
+  const double n = floor(x);
+  return ldexp(static_cast<double>(fast_exp2(static_cast<float>(x - n))), static_cast<int>(n));
+}
+
 // ------------------------------------------------------------------------------ arrival
 // Workgroups of one group (a request or a row) publish partial results and count themselves in;
 // the last to arrive merges them. The eight XCDs have separate L2 caches, so the partials are
@@ -298,6 +291,15 @@ __device__ __forceinline__ void store_coherent(void* p, uint64_t v) {
 __device__ __forceinline__ void store_coherent(float* p, float v) {
   __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_coherent_u32(void* p, uint32_t v) {
+  __hip_atomic_store(static_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t load_coherent_u32(const void* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(static_cast<const uint32_t*>(p)),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ float load_coherent_f32(const float* p) {

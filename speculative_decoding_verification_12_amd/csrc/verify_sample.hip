@@ -218,15 +218,6 @@ __device__ __forceinline__ void load_pair(const DrawRows<TIn>& R, int v, bool ha
   qd = (has && R.resid && R.d_aligned) ? dv[v] : neg_inf_vec<TIn>();
 }
 
-// 2^x for a float64 exponent, to about 2e-7 relative: the integer part scales exactly, the
-// fraction goes through the hardware exp2. x = -inf gives 0.
-__device__ __forceinline__ double exp2_wide(double x) {
-  if (!(x > -1074.0)) return 0.0;
-  if (x >= 1024.0) return INFINITY;
-  const double n = floor(x);
-  return ldexp(static_cast<double>(fast_exp2(static_cast<float>(x - n))), static_cast<int>(n));
-}
-
 // The elements a thread of the draw owns, in token order: the scalar head (thread 0 of chunk 0),
 // its kDrawVecs adjacent vectors, then the scalar tail (the thread holding the row's last
 // vector, or the head's owner when the row has no whole vector). Every thread's elements are

@@ -41,6 +41,19 @@ def test_tiny_random_sample_greedy_predict(dtype):
                 compare_predict(wl, gpu_predict(wl, F, TT), F, TT)
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 40000), ("f32", 40001), ("bf16", 1_000_003)])
+def test_predict_massive_ties(dtype, V):
+    """Logits on a coarse grid: thousands of tokens share the top value, so every chunk has far
+    more candidates than it can publish and selects its own top F first (in rounds of staged
+    candidates), and at V ~ 1e6 the merge holds more entries than a lane keeps in registers.
+    Keys must still be the lowest ids among the equal top logits, exactly."""
+    wl = make_tiny_random(7, B=2, K=2, V=V, T=1.0, dtype=dtype, ties=True)
+    for F in (1, 3, 16):
+        for T in (0.0, 1.0):
+            announce(f"predict ties dtype={dtype} V={V} F={F} T={T}")
+            compare_predict(wl, gpu_predict(wl, F, T), F, T)
+
+
 @pytest.mark.parametrize("V", [2, 7, 8, 9, 1000, 1001, 4097, 8191, 8192, 8193, 16389, 32064])
 @pytest.mark.parametrize("K", [1, 4, 7])
 def test_shape_sweep_c3_recipe_bf16(V, K):
