@@ -6,8 +6,9 @@ no code with the HIP library (no kernels, headers, tables or helpers); the seede
 generators in `synthetic/` are the only code both sides use.
 
 Modules
-  reference  vectorised NumPy oracle in float64 (greedy, sampling, outcome prediction,
-             hit check, decision margins and near-tie flags)
+  reference  vectorised NumPy oracle in float64 (greedy, sampling, outcome prediction with a
+             uniform or per-slot fan-out, hit check and prepared-continuation lookup, draft
+             budget, decision margins and near-tie flags)
   naive      the same rules as literal pure-Python loops (math.exp, running sums), used only to
              cross-check `reference` on tiny inputs
 
@@ -20,15 +21,18 @@ Sources (page titles and sections):
          "1. Outcome Prediction (The Saguaro Cache)".
   [D3D]  "LLMの生成を5倍速くする「D3D」を図で読む" (animemo.app): sections "検証のしくみ①",
          "検証のしくみ③", "検証のまとめ", "答え:ありうる結果すべてに、先回りして下書きする",
-         "ヒット", "ミス".
+         "パック", "ヒット", "ミス" and the table under "用意を増やせばいい、わけではない".
 
 Pin status: every function is pinned by a CPU test except the parts the pages give no formula
 for (Saguaro's fan-out optimiser and Saguaro sampling), which are not implemented here.
 """
 from .reference import (NEAR_TIE, decode_logits, softmax, residual_weights, inverse_cdf,
                         verify_sample_request, verify_greedy_request, predict_request,
-                        verify_sample, verify_greedy, predict_outcomes, outcome_hit)
+                        verify_sample, verify_greedy, predict_outcomes, outcome_hit,
+                        fanout_offsets, predict_fanout_request, predict_fanout, outcome_slot,
+                        fanout_budget)
 
 __all__ = ["NEAR_TIE", "decode_logits", "softmax", "residual_weights", "inverse_cdf",
            "verify_sample_request", "verify_greedy_request", "predict_request", "verify_sample",
-           "verify_greedy", "predict_outcomes", "outcome_hit"]
+           "verify_greedy", "predict_outcomes", "outcome_hit", "fanout_offsets",
+           "predict_fanout_request", "predict_fanout", "outcome_slot", "fanout_budget"]

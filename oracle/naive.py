@@ -123,3 +123,45 @@ def naive_predict(d_rows, F, T):
         else:
             probs.append([1.0] + [0.0] * (F - 1))
     return keys, probs
+
+
+def naive_predict_fanout(d_rows, x, fanout, T):
+    """Per-slot fan-out by repeated selection, skipping the draft token when x is given."""
+    d_rows = _as_float_rows(d_rows)
+    keys, probs = [], []
+    for k, F in enumerate(fanout):
+        row = d_rows[k]
+        chosen = []
+        for _ in range(F):
+            best = None
+            for v in range(len(row)):
+                if v in chosen or (x is not None and v == int(x[k])):
+                    continue
+                if best is None or row[v] > row[best]:
+                    best = v
+            chosen.append(best)
+        keys.extend(chosen)
+        if T > 0:
+            p = naive_softmax(row, float(T))
+            probs.extend(p[v] for v in chosen)
+        else:
+            top = 0
+            for v in range(1, len(row)):
+                if row[v] > row[top]:
+                    top = v
+            probs.extend(1.0 if v == top else 0.0 for v in chosen)
+    return keys, probs
+
+
+def naive_outcome_slot(keys, fanout, K, m, y, all_accept=True):
+    start = 0
+    for k, F in enumerate(fanout):
+        if k == m:
+            for j in range(F):
+                if keys[start + j] == y:
+                    return start + j
+            return -1
+        start += F
+    if m == K and all_accept:
+        return start
+    return -1

@@ -191,6 +191,72 @@ def outcome_hit(keys_row: np.ndarray, m: int, y: int, K: int, positions: int = N
 
 
 # ----------------------------------------------------------------------------------------------
+# per-slot fan-out: prepared outcomes in the manner of D3D
+def fanout_offsets(fanout) -> np.ndarray:
+    """Key offsets of a per-slot fan-out: slot k's keys occupy [off[k], off[k+1])."""
+    off = np.zeros(len(fanout) + 1, np.int64)
+    off[1:] = np.cumsum(np.asarray(fanout, np.int64))
+    return off
+
+
+def predict_fanout_request(d_rows: np.ndarray, x, fanout, T: float):
+    """Keys of one request under a per-slot fan-out ([D3D] section "答え:…": for each of the
+    first P slots the drafter prepares candidates for the token the target would place were that
+    slot the first rejection, namely its own 2nd and 3rd choices, i.e. its top choices other than
+    the draft token; [SSD] section "1. Outcome Prediction": how many candidates each position
+    gets is the fan-out).
+
+    fanout[k] = F_k >= 0 for slots k < P = len(fanout). Slot k's keys are the F_k tokens with the
+    largest draft logits, ordered by logit descending then id ascending, skipping the draft token
+    x[k] when x is given (x = None: no exclusion). key_prob = q_k(key) at T > 0; at T = 0 it is 1
+    for the row's argmax token (lowest id among equal maxima) and 0 for any other key.
+    Returns keys [S] and key_prob [S], S = sum F_k, slot k at [off[k], off[k+1]).
+    """
+    off = fanout_offsets(fanout)
+    keys = np.full(int(off[-1]), -1, np.int64)
+    prob = np.zeros(int(off[-1]))
+    for k, F in enumerate(fanout):
+        order = np.argsort(-d_rows[k], kind="stable")
+        if x is not None:
+            order = order[order != int(x[k])]
+        sel = order[:int(F)]
+        keys[off[k]:off[k + 1]] = sel
+        if T > 0:
+            prob[off[k]:off[k + 1]] = softmax(d_rows[k], T)[sel]
+        else:
+            prob[off[k]:off[k + 1]] = (sel == int(np.argmax(d_rows[k]))).astype(np.float64)
+    return keys, prob
+
+
+def outcome_slot(keys_req, fanout, K: int, m: int, y: int, all_accept: bool = True) -> int:
+    """The prepared continuation a verification outcome selects, or -1 for a miss ([D3D]
+    sections "答え:…", "ヒット" and "ミス").
+
+    The outcome is m drafts kept and token y placed at slot m. A rejection at a prepared slot
+    (m < P) whose placed token is one of that slot's keys selects that key's continuation, index
+    off[m] + (position of y among the slot's keys). Every draft kept (m = K) selects the single
+    continuation prepared for that case, index S = sum F_k, when one was prepared. Anything else
+    (a placed token outside the candidates, a rejection beyond the prepared slots, a row error)
+    is a miss.
+    """
+    P = len(fanout)
+    off = fanout_offsets(fanout)
+    if m == K:
+        return int(off[-1]) if all_accept else -1
+    if m < 0 or m >= P:
+        return -1
+    hits = np.nonzero(np.asarray(keys_req[off[m]:off[m + 1]]) == int(y))[0]
+    return int(off[m] + hits[0]) if hits.size else -1
+
+
+def fanout_budget(fanout, block: int) -> int:
+    """Tokens the drafter prepares per round ([D3D] sections "パック" and the table under
+    "用意を増やせばいい、わけではない"): one block for every candidate, one for the all-accept
+    continuation and the block being verified, (sum F_k + 2) * block."""
+    return (int(np.sum(np.asarray(fanout, np.int64))) + 2) * int(block)
+
+
+# ----------------------------------------------------------------------------------------------
 # batches
 def _request_slices(n: int, requests):
     return range(n) if requests is None else requests
@@ -218,6 +284,16 @@ def verify_greedy(target, dtype, tokens, kv_len, requests=None):
 def predict_outcomes(draft, dtype, F, T, requests=None):
     idx = list(_request_slices(draft.shape[0], requests))
     out = [predict_request(decode_logits(draft[b], dtype), F, float(np.float32(T))) for b in idx]
+    return dict(requests=np.array(idx), keys=np.stack([o[0] for o in out]),
+                key_prob=np.stack([o[1] for o in out]))
+
+
+def predict_fanout(draft, dtype, tokens, fanout, T, requests=None):
+    """Batch wrapper of predict_fanout_request; tokens None disables the draft-token exclusion."""
+    idx = list(_request_slices(draft.shape[0], requests))
+    out = [predict_fanout_request(decode_logits(draft[b], dtype),
+                                  None if tokens is None else tokens[b], fanout,
+                                  float(np.float32(T))) for b in idx]
     return dict(requests=np.array(idx), keys=np.stack([o[0] for o in out]),
                 key_prob=np.stack([o[1] for o in out]))
 
