@@ -350,6 +350,40 @@ def secondary(sv, torch, dev, hip, sets, dsets, ws, args):
                                            keys_per_s=round(B * K * F / (ms * 1e-3), 1),
                                            hbm_gbps=round(pb / (ms * 1e-3) / 1e9, 1),
                                            bytes_per_call=pb)
+
+    # per-slot fan-out with the draft token skipped (two candidates per slot, the D3D page's
+    # setting), then the lookup of each outcome's prepared continuation
+    log("C5 fan-out keys and outcome lookup")
+    x5 = [torch.from_numpy(w.tokens).to(dev) for w in c5]
+    fan = [2] * K
+    S = sum(fan)
+    outf = dict(keys=torch.empty((B, S), dtype=torch.int32, device=dev),
+                key_prob=torch.empty((B, S), dtype=torch.float32, device=dev))
+    for i in range(10):
+        sv.spec_predict_fanout(d5[i % 8], fan, 1.0, ws, draft_tokens=x5[i % 8], out=outf)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        sv.spec_predict_fanout(d5[i % 8], fan, 1.0, ws, draft_tokens=x5[i % 8], out=outf)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    pb = B * K * V * 2
+    res["fanout_c5_T1"] = dict(fanout=fan, draft_token_skipped=True, ms_per_call=round(ms, 5),
+                               keys_per_s=round(B * S / (ms * 1e-3), 1),
+                               hbm_gbps=round(pb / (ms * 1e-3) / 1e9, 1), bytes_per_call=pb)
+    slot = torch.empty(B, dtype=torch.int32, device=dev)
+    for i in range(10):
+        sv.spec_outcome_lookup(outg["tau"], outg["tokens"], outf["keys"], fan, True, out=slot)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        sv.spec_outcome_lookup(outg["tau"], outg["tokens"], outf["keys"], fan, True, out=slot)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    res["outcome_lookup"] = dict(ms_per_call=round(ms, 5),
+                                 outcomes_per_s=round(B / (ms * 1e-3), 1))
     return res
 
 

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 2
+#define SPEC_ABI_VERSION 3
 #define SPEC_MAX_K 64
 #define SPEC_MAX_F 16
 #define SPEC_MAX_V 4194304 /* 2^22 */
@@ -158,6 +158,46 @@ int spec_verify_greedy(const void* target_logits, int dtype, const int32_t* draf
 int spec_predict_outcomes(const void* draft_logits, int dtype, int B, int K, int V, int F,
                           float temperature, int32_t* out_keys, float* out_key_prob,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Outcome keys with a per-slot fan-out ([D3D] "答え:…": for each of the first P draft positions
+ * the drafter prepares candidates for the token the target would place were that position the
+ * first rejection, its own 2nd and 3rd choices in the page's setting; [SSD] section 1: how many
+ * candidates each position gets is the fan-out).
+ *   fanout     HOST array of P ints, 1 <= P <= K: F_k >= 0 keys for slot k (at least one key in
+ *              total). F_k <= SPEC_MAX_F, or SPEC_MAX_F - 1 when draft_tokens is given; the F_k
+ *              (+1 when draft_tokens is given) must not exceed V.
+ *   draft_tokens [B,K] int32 (nullable): when given, slot k skips the draft token x_k. After a
+ *              rejection at slot k the target never places x_k (its residual weight is zero;
+ *              at temperature zero the placed token differs from x_k by definition), so the
+ *              slot's keys are the best tokens that can actually be placed; with greedy drafts
+ *              they are the drafter's 2nd, 3rd, ... choices.
+ * Slot k's keys are the F_k tokens with the largest draft_logits[b,k,:] (x_k skipped as above),
+ * ordered by logit descending then id ascending, written at out_keys[b, off_k .. off_k+F_k),
+ * off_k = F_0 + ... + F_{k-1}; out_keys is [B,S] int32 with S = F_0 + ... + F_{P-1}.
+ * out_key_prob [B,S] (nullable) = q_k(key) at T > 0; at T = 0, 1 for the row's argmax token
+ * (lowest id among equal maxima) and 0 for any other key. Only rows k < P with F_k > 0 are read.
+ * The workspace is sized by spec_workspace_bytes(B, K, V, F) for any F. Errors as for
+ * spec_predict_outcomes (SPEC_ERR_ARG also for P or fan-outs out of range, or S = 0). */
+int spec_predict_fanout(const void* draft_logits, int dtype, const int32_t* draft_tokens, int B,
+                        int K, int V, int P, const int32_t* fanout, float temperature,
+                        int32_t* out_keys, float* out_key_prob, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* The prepared continuation each verification outcome selects ([D3D] sections "ヒット" and
+ * "ミス": a placed token among the prepared candidates is a hit; a placed token outside them, or
+ * a rejection beyond the prepared positions, is a miss; section "答え:…": one more continuation
+ * is prepared for the case where every draft is kept).
+ *   tau [B], tokens [B,K+1] int32 (device): outputs of spec_verify_sample or spec_verify_greedy;
+ *   keys [B,S] int32 (device): out_keys of spec_predict_fanout with the same P and fanout (HOST
+ *   array, same rules); all_accept: nonzero when a continuation for "every draft kept" exists.
+ * out_slot [B] int32 (device): off_m + j when the request kept m = tau-1 < P drafts and placed
+ * keys[b, off_m + j]; S when it kept all K drafts (tau = K+1) and all_accept is nonzero; -1
+ * otherwise (a miss, or a row error tau = -1). One thread per request; no workspace.
+ * Errors: SPEC_ERR_ARG for null pointers, B < 1, K out of [1, SPEC_MAX_K], P out of [1, K] or a
+ * fan-out out of [0, SPEC_MAX_F] (or S = 0); SPEC_ERR_HIP for a failed launch. */
+int spec_outcome_lookup(const int32_t* tau, const int32_t* tokens, const int32_t* keys, int B,
+                        int K, int P, const int32_t* fanout, int all_accept, int32_t* out_slot,
+                        hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,8 @@ STATUS = {0: "SPEC_OK", -1: "SPEC_ERR_ARG", -2: "SPEC_ERR_DTYPE", -3: "SPEC_ERR_
 
 EXPORTS = ("spec_abi_version", "spec_status_string", "spec_workspace_bytes",
            "spec_workspace_init", "spec_verify_sample", "spec_verify_sample_ex",
-           "spec_verify_greedy", "spec_predict_outcomes")
+           "spec_verify_greedy", "spec_predict_outcomes", "spec_predict_fanout",
+           "spec_outcome_lookup")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGNATURES = {
@@ -37,6 +38,9 @@ _SIGNATURES = {
     "spec_verify_greedy": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _f,
                                 _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_predict_outcomes": (_i, [_vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
+    "spec_predict_fanout": (_i, [_vp, _i, _vp, _i, _i, _i, _i, _vp, _f, _vp, _vp, _vp, _sz,
+                                 _vp]),
+    "spec_outcome_lookup": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp]),
 }
 
 
@@ -218,4 +222,48 @@ def spec_predict_outcomes(draft, F, temperature, workspace, out=None):
         _ptr(draft), _dtype_code(draft), B, K, V, int(F), float(temperature), _ptr(out["keys"]),
         _ptr(out.get("key_prob")), _ptr(workspace), workspace.numel(), _stream(dev))
     _check("spec_predict_outcomes", rc)
+    return out
+
+
+def _fanout_array(fanout):
+    fan = [int(f) for f in fanout]
+    return (ctypes.c_int32 * len(fan))(*fan), len(fan), sum(fan)
+
+
+def spec_predict_fanout(draft, fanout, temperature, workspace, draft_tokens=None, out=None):
+    """Per-slot fan-out keys. `fanout` is a host sequence of P ints. Returns dict(keys [B,S]
+    int32, key_prob [B,S] float32), S = sum(fanout); slot k's keys start at sum(fanout[:k])."""
+    torch = _torch()
+    B, K, V = draft.shape
+    dev = draft.device
+    _need(draft, "draft_logits", (B, K, V), draft.dtype, dev)
+    if draft_tokens is not None:
+        _need(draft_tokens, "draft_tokens", (B, K), torch.int32, dev)
+    fan, P, S = _fanout_array(fanout)
+    if out is None:
+        out = dict(keys=torch.empty((B, max(S, 1)), dtype=torch.int32, device=dev),
+                   key_prob=torch.empty((B, max(S, 1)), dtype=torch.float32, device=dev))
+    rc = load_library().spec_predict_fanout(
+        _ptr(draft), _dtype_code(draft), _ptr(draft_tokens), B, K, V, P, fan, float(temperature),
+        _ptr(out["keys"]), _ptr(out.get("key_prob")), _ptr(workspace), workspace.numel(),
+        _stream(dev))
+    _check("spec_predict_fanout", rc)
+    return out
+
+
+def spec_outcome_lookup(tau, tokens, keys, fanout, all_accept=True, out=None):
+    """Prepared continuation selected by each outcome (-1 for a miss). Returns int32 [B]."""
+    torch = _torch()
+    B = tau.shape[0]
+    K = tokens.shape[1] - 1
+    dev = tau.device
+    fan, P, S = _fanout_array(fanout)
+    _need(tau, "tau", (B,), torch.int32, dev)
+    _need(tokens, "tokens", (B, K + 1), torch.int32, dev)
+    _need(keys, "keys", (B, S), torch.int32, dev)
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=dev)
+    rc = load_library().spec_outcome_lookup(_ptr(tau), _ptr(tokens), _ptr(keys), B, K, P, fan,
+                                            1 if all_accept else 0, _ptr(out), _stream(dev))
+    _check("spec_outcome_lookup", rc)
     return out

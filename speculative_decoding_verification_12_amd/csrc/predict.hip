@@ -4,8 +4,14 @@
 // Saguaro Cache)": the outcome of a verification is how many drafts were kept plus the token the
 // target placed, and the placed token is predicted from the draft's top logits; page
 // "LLMの生成を5倍速くする「D3D」を図で読む", section "答え:…": an outcome is (kept count, placed
-// token)). For every draft slot k the F tokens with the largest draft logits, ordered by logit
-// descending then id ascending, are the keys (k, t); at T > 0 each key also gets q_k(t).
+// token)); page "LLMの生成を5倍速くする「D3D」を図で読む", sections "答え:…", "ヒット", "ミス":
+// for each of the first P slots the drafter prepares candidates for the token the target would
+// place there, its own top choices other than the draft token, plus one continuation for the case
+// where every draft is kept). For every slot k < P the F_k tokens with the largest draft logits,
+// ordered by logit descending then id ascending and optionally skipping the draft token x_k, are
+// the keys (k, t); at T > 0 each key also gets q_k(t). The uniform case (F_k = F for every slot,
+// no exclusion) is spec_predict_outcomes; the per-slot case is spec_predict_fanout. A second,
+// tiny kernel maps each verification outcome to the prepared continuation it selects.
 //
 // One launch: a workgroup of four independent waves per (request, slot, chunk of at most
 // kPredictVecs 16-byte vectors). Lane t of wave w reads vectors vbeg + p*1024 + i*256 + 64w + t
@@ -23,7 +29,9 @@
 //      (value, id) argmax.
 // The wave counts itself in on the slot's counter; the slot's last wave selects the F best of all
 // published lists by F rounds of argmax, each excluding everything at or before the previous
-// pick in the order (value desc, id asc), and writes the keys and q_k(key).
+// pick in the order (value desc, id asc), and writes the keys and q_k(key). With the draft token
+// excluded, a slot looks for F_k + 1 tokens and drops x_k (or, when x_k is not among them, the
+// last one).
 #include "api_common.hpp"
 #include "spec_common.hpp"
 
@@ -45,11 +53,22 @@ __device__ __forceinline__ int nth_bit(unsigned long long m, int n) {
   return m != 0ull ? __ffsll(static_cast<long long>(m)) - 1 : -1;
 }
 
+// Per-slot work of one launch, passed by value: slot k < P looks for pick[k] tokens and writes
+// count[k] keys at offset off[k] of its request's S keys (pick = count, or count + 1 when the
+// draft token is excluded; 0 skips the slot).
+struct FanoutTable {
+  int P;
+  int S;
+  int8_t pick[SPEC_MAX_K];
+  int8_t count[SPEC_MAX_K];
+  int16_t off[SPEC_MAX_K];
+};
+
 template <typename TIn>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void predict_kernel(
-    const TIn* __restrict__ drf, int K, int V, int F, float c, int nchunk, int cv,
-    ArgPart* __restrict__ part, int* __restrict__ pcnt, float2* __restrict__ pstat,
-    unsigned* __restrict__ cnt_base, int32_t* __restrict__ out_keys,
+    const TIn* __restrict__ drf, const int32_t* __restrict__ xtok, int K, int V, FanoutTable ft,
+    float c, int nchunk, int cv, ArgPart* __restrict__ part, int* __restrict__ pcnt,
+    float2* __restrict__ pstat, unsigned* __restrict__ cnt_base, int32_t* __restrict__ out_keys,
     float* __restrict__ out_prob) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
@@ -60,10 +79,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
   static_assert(SPEC_MAX_F <= kListSlots && kWaveSlots <= kListSlots, "list sizes");
 
   const int ch = blockIdx.x % nchunk;
-  const int rk = blockIdx.x / nchunk;   // b * K + k
+  const int rk = blockIdx.x / nchunk;   // b * P + k
+  const int k = rk % ft.P, b = rk / ft.P;
+  const int F = ft.pick[k];   // tokens this slot looks for
+  if (F == 0) return;         // the whole slot is skipped
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   unsigned* cnt = cnt_base + static_cast<size_t>(rk) * kCounterStride;
-  const TIn* row = drf + static_cast<size_t>(rk) * static_cast<size_t>(V);
+  const TIn* row = drf + (static_cast<size_t>(b) * K + k) * static_cast<size_t>(V);
   const RowSpan sp = row_span(row, V);
   const ChunkRange cr = chunk_range(sp, ch, nchunk, cv);   // cv <= kPredictVecs
   // vector v (0..kVecs-1) of lane tid
@@ -289,6 +311,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
     }
   }
   const bool more = total > kHeld * kWave;   // uniform
+  const int xk = xtok ? xtok[static_cast<size_t>(b) * K + k] : -1;   // excluded token, if any
+  const int nkeys = ft.count[k];
+  const size_t obase = static_cast<size_t>(b) * ft.S + ft.off[k];
+  int j = 0;   // keys written so far (uniform)
   float pv = INFINITY;
   int pi = -1;
   for (int f = 0; f < F; ++f) {
@@ -315,8 +341,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
     wave_argmax(bv, bi);
     pv = bv;
     pi = bi;
+    if (bi == xk) continue;   // the draft token itself: never the placed token after a rejection
+    if (j == nkeys) break;
+    const size_t o = obase + j;
+    ++j;
     if (lane == 0) {
-      const size_t o = static_cast<size_t>(rk) * F + f;
       out_keys[o] = bi;
       if (out_prob) {
         float pr_f;
@@ -333,19 +362,92 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) 
 }
 
 template <typename TIn>
-int launch_predict(const void* draft, int B, int K, int V, int F, float T, int32_t* out_keys,
-                   float* out_prob, void* ws, hipStream_t stream, const KernelPlan& P) {
+int launch_predict(const void* draft, const int32_t* xtok, int B, int K, int V,
+                   const FanoutTable& ft, float T, int32_t* out_keys, float* out_prob, void* ws,
+                   hipStream_t stream) {
+  // chunking as for all K slots of every request, so the workspace sized by
+  // spec_workspace_bytes(B, K, V, .) covers any P <= K
+  const KernelPlan P = predict_plan(B, K, V, 16 / static_cast<int>(sizeof(TIn)));
   if (P.cv > kPredictVecs) return SPEC_ERR_ARG;   // a chunk is one round of loads per lane
-  const size_t g = static_cast<size_t>(B) * K * P.nchunk;
+  const size_t g = static_cast<size_t>(B) * ft.P * P.nchunk;
   if (!grid_fits(g)) return SPEC_ERR_ARG;
-  const WsLayout L = ws_layout(B, K, V, F);
+  const WsLayout L = ws_layout(B, K, V, 1);
   const float c = T > 0.f ? exp2_scale(T) : 0.f;
   hipLaunchKernelGGL(predict_kernel<TIn>, dim3(static_cast<unsigned>(g)), dim3(kBlock), 0, stream,
-                     static_cast<const TIn*>(draft), K, V, F, c, P.nchunk, P.cv,
+                     static_cast<const TIn*>(draft), xtok, K, V, ft, c, P.nchunk, P.cv,
                      ws_ptr<ArgPart>(ws, L.part_topf), ws_ptr<int>(ws, L.part_pcnt),
                      ws_ptr<float2>(ws, L.part_pstat),
                      ws_ptr<unsigned>(ws, L.cnt_a), out_keys, out_prob);
   return launch_status();
+}
+
+int check_predict_common(const void* draft_logits, int dtype, int B, int K, int V,
+                         float temperature, const int32_t* out_keys) {
+  int rc = check_dtype(dtype);
+  if (rc != SPEC_OK) return rc;
+  if ((rc = check_dims(B, K, V)) != SPEC_OK) return rc;
+  if (check_logits(draft_logits, dtype) != SPEC_OK || out_keys == nullptr) return SPEC_ERR_ARG;
+  if (!std::isfinite(temperature) || temperature < 0.f ||
+      (temperature > 0.f && !std::isfinite(exp2_scale(temperature))))
+    return SPEC_ERR_TEMPERATURE;
+  return SPEC_OK;
+}
+
+int run_predict(const void* draft_logits, int dtype, const int32_t* xtok, int B, int K, int V,
+                const FanoutTable& ft, float temperature, int32_t* out_keys, float* out_key_prob,
+                void* workspace, hipStream_t stream) {
+  if (dtype == SPEC_BF16)
+    return launch_predict<uint16_t>(draft_logits, xtok, B, K, V, ft, temperature, out_keys,
+                                    out_key_prob, workspace, stream);
+  return launch_predict<float>(draft_logits, xtok, B, K, V, ft, temperature, out_keys,
+                               out_key_prob, workspace, stream);
+}
+
+// Builds the per-slot table; false when a fan-out is out of range.
+bool fanout_table(const int32_t* fanout, int P, bool exclude, int V, FanoutTable& ft) {
+  ft.P = P;
+  ft.S = 0;
+  for (int k = 0; k < SPEC_MAX_K; ++k) {
+    ft.pick[k] = 0;
+    ft.count[k] = 0;
+    ft.off[k] = 0;
+  }
+  for (int k = 0; k < P; ++k) {
+    const int F = fanout[k];
+    const int pick = F > 0 ? F + (exclude ? 1 : 0) : 0;
+    if (F < 0 || pick > SPEC_MAX_F || pick > V) return false;
+    ft.pick[k] = static_cast<int8_t>(pick);
+    ft.count[k] = static_cast<int8_t>(F);
+    ft.off[k] = static_cast<int16_t>(ft.S);
+    ft.S += F;
+  }
+  return ft.S > 0;
+}
+
+// ------------------------------------------------------------------------------ lookup
+// One thread per request: the outcome (tau, placed token) against the request's keys.
+__global__ __launch_bounds__(kBlock) void lookup_kernel(const int32_t* __restrict__ tau,
+                                                        const int32_t* __restrict__ tokens,
+                                                        const int32_t* __restrict__ keys, int B,
+                                                        int K, FanoutTable ft, int all_accept,
+                                                        int32_t* __restrict__ out_slot) {
+  const int b = blockIdx.x * kBlock + threadIdx.x;
+  if (b >= B) return;
+  const int tb = tau[b];
+  int slot = -1;
+  if (tb == K + 1) {
+    slot = all_accept ? ft.S : -1;
+  } else if (tb >= 1 && tb <= K && tb - 1 < ft.P) {
+    const int m = tb - 1;
+    const int y = tokens[static_cast<size_t>(b) * (K + 1) + m];
+    const int32_t* kr = keys + static_cast<size_t>(b) * ft.S + ft.off[m];
+    for (int j = 0; j < ft.count[m]; ++j)
+      if (kr[j] == y) {
+        slot = ft.off[m] + j;
+        break;
+      }
+  }
+  out_slot[b] = slot;
 }
 
 }  // namespace
@@ -356,18 +458,47 @@ extern "C" int spec_predict_outcomes(const void* draft_logits, int dtype, int B,
                                      float* out_key_prob, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream) {
   using namespace sv;
-  int rc = check_dtype(dtype);
+  int rc = check_predict_common(draft_logits, dtype, B, K, V, temperature, out_keys);
   if (rc != SPEC_OK) return rc;
-  if ((rc = check_dims(B, K, V)) != SPEC_OK) return rc;
   if (F < 1 || F > SPEC_MAX_F || F > V) return SPEC_ERR_ARG;
-  if (check_logits(draft_logits, dtype) != SPEC_OK || out_keys == nullptr) return SPEC_ERR_ARG;
-  if (!std::isfinite(temperature) || temperature < 0.f ||
-      (temperature > 0.f && !std::isfinite(exp2_scale(temperature))))
-    return SPEC_ERR_TEMPERATURE;
   if ((rc = check_workspace(workspace, workspace_bytes, B, K, V, F)) != SPEC_OK) return rc;
-  if (dtype == SPEC_BF16)
-    return launch_predict<uint16_t>(draft_logits, B, K, V, F, temperature, out_keys,
-                                    out_key_prob, workspace, stream, predict_plan(B, K, V, 8));
-  return launch_predict<float>(draft_logits, B, K, V, F, temperature, out_keys, out_key_prob,
-                               workspace, stream, predict_plan(B, K, V, 4));
+  int32_t fan[SPEC_MAX_K];
+  for (int k = 0; k < K; ++k) fan[k] = F;
+  FanoutTable ft;
+  if (!fanout_table(fan, K, false, V, ft)) return SPEC_ERR_ARG;
+  return run_predict(draft_logits, dtype, nullptr, B, K, V, ft, temperature, out_keys,
+                     out_key_prob, workspace, stream);
+}
+
+extern "C" int spec_predict_fanout(const void* draft_logits, int dtype,
+                                   const int32_t* draft_tokens, int B, int K, int V, int P,
+                                   const int32_t* fanout, float temperature, int32_t* out_keys,
+                                   float* out_key_prob, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  using namespace sv;
+  int rc = check_predict_common(draft_logits, dtype, B, K, V, temperature, out_keys);
+  if (rc != SPEC_OK) return rc;
+  if (P < 1 || P > K || fanout == nullptr) return SPEC_ERR_ARG;
+  FanoutTable ft;
+  if (!fanout_table(fanout, P, draft_tokens != nullptr, V, ft)) return SPEC_ERR_ARG;
+  if ((rc = check_workspace(workspace, workspace_bytes, B, K, V, 1)) != SPEC_OK) return rc;
+  return run_predict(draft_logits, dtype, draft_tokens, B, K, V, ft, temperature, out_keys,
+                     out_key_prob, workspace, stream);
+}
+
+extern "C" int spec_outcome_lookup(const int32_t* tau, const int32_t* tokens,
+                                   const int32_t* keys, int B, int K, int P,
+                                   const int32_t* fanout, int all_accept, int32_t* out_slot,
+                                   hipStream_t stream) {
+  using namespace sv;
+  if (tau == nullptr || tokens == nullptr || keys == nullptr || out_slot == nullptr ||
+      fanout == nullptr || B < 1 || K < 1 || K > SPEC_MAX_K || P < 1 || P > K)
+    return SPEC_ERR_ARG;
+  FanoutTable ft;
+  // the key lists only need count/off here; V does not constrain a lookup
+  if (!fanout_table(fanout, P, false, SPEC_MAX_V, ft)) return SPEC_ERR_ARG;
+  const unsigned blocks = static_cast<unsigned>((B + kBlock - 1) / kBlock);
+  hipLaunchKernelGGL(lookup_kernel, dim3(blocks), dim3(kBlock), 0, stream, tau, tokens, keys, B,
+                     K, ft, all_accept ? 1 : 0, out_slot);
+  return launch_status();
 }

@@ -149,3 +149,57 @@ def compare_predict(wl, gpu, F, T, requests=None):
         np.testing.assert_allclose(gpu["key_prob"][b], ref["key_prob"][i], rtol=0,
                                    atol=PROB_ATOL, err_msg=where)
     return ref
+
+
+def gpu_fanout(wl, fanout, T, exclude, dev=None, ws=None):
+    """Per-slot fan-out keys; exclusion skips wl.tokens (the draft tokens)."""
+    draft = dev["draft"] if dev else dev_logits(wl.draft, wl.dtype)
+    B, K = wl.B, wl.K
+    S = int(sum(fanout))
+    ws = ws if ws is not None else sv.new_workspace(B, K, wl.V)
+    x = (dev["tokens"] if dev else torch.from_numpy(wl.tokens).cuda()) if exclude else None
+    out = dict(keys=poisoned((B, S), torch.int32), key_prob=poisoned((B, S), torch.float32))
+    sv.spec_predict_fanout(draft, fanout, T, ws, draft_tokens=x, out=out)
+    torch.cuda.synchronize()
+    return {k: _np(v) for k, v in out.items()}
+
+
+def compare_fanout(wl, gpu, fanout, T, exclude, requests=None):
+    _assert_no_poison(gpu)
+    idx = list(range(wl.B)) if requests is None else list(requests)
+    ref = oracle.predict_fanout(wl.draft, wl.dtype, wl.tokens if exclude else None, fanout, T,
+                                requests=idx)
+    for i, b in enumerate(idx):
+        where = (f"request {b} ({wl.config.name}, fan-out {list(fanout)} T={T} "
+                 f"exclude={exclude})")
+        assert np.array_equal(gpu["keys"][b], ref["keys"][i]), where
+        np.testing.assert_allclose(gpu["key_prob"][b], ref["key_prob"][i], rtol=0,
+                                   atol=PROB_ATOL, err_msg=where)
+    return ref
+
+
+def oracle_outcomes(wl):
+    """(tau, tokens) of every request from the oracle, the input of the lookup parity check."""
+    if float(wl.T) > 0:
+        r = oracle.verify_sample(wl.target, wl.draft, wl.dtype, wl.tokens, wl.uniforms,
+                                 wl.kv_len, wl.T)
+    else:
+        r = oracle.verify_greedy(wl.target, wl.dtype, wl.tokens, wl.kv_len)
+    return r["tau"].astype(np.int32), r["tokens"].astype(np.int32)
+
+
+def compare_lookup(wl, keys, fanout, all_accept=True):
+    """GPU lookup on the oracle's outcomes and the oracle's keys against oracle.outcome_slot.
+    Returns the per-request slots."""
+    tau, tokens = oracle_outcomes(wl)
+    out = poisoned((wl.B,), torch.int32)
+    sv.spec_outcome_lookup(torch.from_numpy(tau).cuda(), torch.from_numpy(tokens).cuda(),
+                           torch.from_numpy(np.ascontiguousarray(keys, np.int32)).cuda(), fanout,
+                           all_accept, out=out)
+    torch.cuda.synchronize()
+    got = _np(out)
+    for b in range(wl.B):
+        exp = oracle.outcome_slot(keys[b], fanout, wl.K, int(tau[b]) - 1,
+                                  int(tokens[b, max(int(tau[b]) - 1, 0)]), all_accept)
+        assert int(got[b]) == exp, f"request {b}: lookup {got[b]} != {exp}"
+    return got

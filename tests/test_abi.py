@@ -157,6 +157,45 @@ def test_predict_validation(lib):
     assert call() == code["SPEC_ERR_WORKSPACE"]
 
 
+def test_fanout_validation(lib):
+    code = {v: k for k, v in sv.STATUS.items()}
+
+    def call(fan=(2, 2, 2), x=FAKE, **kw):
+        a = dict(d=FAKE, dtype=1, B=2, K=4, V=1000, T=1.0, keys=FAKE, prob=NULL, ws=FAKE, wsb=0,
+                 s=NULL)
+        a.update(kw)
+        arr = (ctypes.c_int32 * max(len(fan), 1))(*fan) if fan is not None else NULL
+        P = a.pop("P", len(fan) if fan is not None else 1)
+        return lib.spec_predict_fanout(a["d"], a["dtype"], x, a["B"], a["K"], a["V"], P, arr,
+                                       a["T"], a["keys"], a["prob"], a["ws"], a["wsb"], a["s"])
+    assert call(dtype=5) == code["SPEC_ERR_DTYPE"]
+    for kw in [dict(fan=None), dict(fan=(2,) * 5), dict(P=0), dict(fan=(0, 0)), dict(fan=(-1, 2)),
+               dict(fan=(16,)), dict(fan=(17,), x=NULL), dict(fan=(3,), V=3), dict(keys=NULL),
+               dict(d=NULL), dict(B=0)]:
+        assert call(**kw) == code["SPEC_ERR_ARG"], kw
+    # the same sizes are fine without exclusion (16 keys) or with V large enough
+    assert call(fan=(16,), x=NULL) == code["SPEC_ERR_WORKSPACE"]
+    assert call(fan=(2,), V=3) == code["SPEC_ERR_WORKSPACE"]
+    for T in [-1.0, float("nan")]:
+        assert call(T=T) == code["SPEC_ERR_TEMPERATURE"]
+    assert call() == code["SPEC_ERR_WORKSPACE"]
+
+
+def test_outcome_lookup_validation(lib):
+    code = {v: k for k, v in sv.STATUS.items()}
+    fan = (ctypes.c_int32 * 3)(2, 2, 2)
+    args = [FAKE, FAKE, FAKE, 2, 4, 3, fan, 1, FAKE, NULL]
+    for i, bad in [(0, NULL), (1, NULL), (2, NULL), (8, NULL), (3, 0), (4, 0), (4, 65), (5, 0),
+                   (5, 5), (6, NULL)]:
+        a = list(args)
+        a[i] = bad
+        assert lib.spec_outcome_lookup(*a) == code["SPEC_ERR_ARG"], (i, bad)
+    zero = (ctypes.c_int32 * 3)(0, 0, 0)
+    a = list(args)
+    a[6] = zero
+    assert lib.spec_outcome_lookup(*a) == code["SPEC_ERR_ARG"]
+
+
 def test_workspace_init_rejects_bad_pointer(lib):
     code = {v: k for k, v in sv.STATUS.items()}
     assert lib.spec_workspace_init(NULL, 4096, NULL) == code["SPEC_ERR_WORKSPACE"]

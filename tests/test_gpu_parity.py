@@ -7,8 +7,9 @@ import torch
 
 import oracle
 import speculative_decoding_verification_12_amd as sv
-from gpu_helpers import (announce, compare_greedy, compare_predict, compare_sample, dev_logits,
-                         gpu_greedy, gpu_predict, gpu_sample, upload)
+from gpu_helpers import (announce, compare_fanout, compare_greedy, compare_lookup,
+                         compare_predict, compare_sample, dev_logits, gpu_fanout, gpu_greedy,
+                         gpu_predict, gpu_sample, upload)
 from synthetic import make_tiny_random, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -52,6 +53,51 @@ def test_predict_massive_ties(dtype, V):
         for T in (0.0, 1.0):
             announce(f"predict ties dtype={dtype} V={V} F={F} T={T}")
             compare_predict(wl, gpu_predict(wl, F, T), F, T)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fanout_tiny_random(dtype):
+    """Per-slot fan-outs (zeros included), with and without the draft-token exclusion, at T > 0
+    and T = 0, on tiny rows with ties and masked tokens; then the outcome lookup."""
+    rng = np.random.default_rng(17)
+    for seed in range(30):
+        K = 1 + seed % 6
+        V = [3, 5, 8, 13, 40, 129, 1000][seed % 7]
+        T = [1.0, 0.7, 2.5][seed % 3]
+        P = int(rng.integers(1, K + 1))
+        fanout = [int(rng.integers(0, min(15, V - 1) + 1)) for _ in range(P)]
+        if sum(fanout) == 0:
+            fanout[0] = 1
+        wl = make_tiny_random(seed, B=6, K=K, V=V, T=T, dtype=dtype, ties=seed % 2 == 0,
+                              neg_inf=0.2 if seed % 3 else 0.0)
+        for exclude in (True, False):
+            for TT in (0.0, T):
+                announce(f"fan-out seed={seed} dtype={dtype} K={K} V={V} fan={fanout} "
+                         f"excl={exclude} T={TT}")
+                g = gpu_fanout(wl, fanout, TT, exclude)
+                compare_fanout(wl, g, fanout, TT, exclude)
+            compare_lookup(wl, g["keys"], fanout, all_accept=bool(seed % 2))
+
+
+@pytest.mark.parametrize("mode", ["sample", "greedy"])
+def test_fanout_d3d_setting(mode):
+    """The page's setting: 15 drafts per round, candidates at the first 11 positions, two each
+    (the drafter's 2nd and 3rd choices), plus the all-accept continuation: 384 prepared tokens.
+    C2's value recipe at K = 15."""
+    P, F = 11, 2
+    fanout = [F] * P
+    assert oracle.fanout_budget(fanout, 16) == 384
+    hits = n = 0
+    for rnd in range(3):
+        wl = make_workload(2, 300 + rnd, mode, B=8, K=15)
+        dev = upload(wl)
+        announce(f"D3D setting {mode} round {rnd}")
+        g = gpu_fanout(wl, fanout, float(wl.T), True, dev=dev)
+        compare_fanout(wl, g, fanout, float(wl.T), True)
+        slots = compare_lookup(wl, g["keys"], fanout)
+        hits += int(np.sum(slots >= 0))
+        n += wl.B
+    announce(f"D3D setting {mode}: prepared-continuation hit rate {hits / n:.3f} ({hits}/{n})")
 
 
 @pytest.mark.parametrize("V", [2, 7, 8, 9, 1000, 1001, 4097, 8191, 8192, 8193, 16389, 32064])
@@ -246,3 +292,25 @@ def test_c5_predict_full_and_hit_rate(T):
     rejected = m < wl.K
     announce(f"C5 T={T}: hit rate {np.mean(hits):.3f} over all rounds, "
              f"{np.sum(hits) / max(1, rejected.sum()):.3f} over rejected ones")
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_c5_fanout_full(T):
+    """C5 at full size with a per-slot fan-out and the draft token excluded: keys and lookup on
+    every request. With the same number of keys per slot, skipping the draft token never loses
+    a hit (the rejected draft token is never the placed one)."""
+    wl = make_workload(5, 1, "sample" if T > 0 else "greedy")
+    dev = upload(wl)
+    announce(f"C5 fan-out T={T}")
+    for fanout in ([3, 2, 2, 1], [3] * wl.K):
+        g = gpu_fanout(wl, fanout, T, True, dev=dev)
+        compare_fanout(wl, g, fanout, T, True)
+        slots = compare_lookup(wl, g["keys"], fanout)
+        announce(f"C5 T={T} fan-out {fanout} (draft token skipped): hit rate "
+                 f"{np.mean(slots >= 0):.3f}")
+    plain = gpu_fanout(wl, [3] * wl.K, T, False, dev=dev)
+    compare_fanout(wl, plain, [3] * wl.K, T, False)
+    plain_slots = compare_lookup(wl, plain["keys"], [3] * wl.K)
+    assert np.all((plain_slots < 0) | (slots >= 0))
+    announce(f"C5 T={T} fan-out 3 per slot, draft token kept: hit rate "
+             f"{np.mean(plain_slots >= 0):.3f}")
