@@ -384,6 +384,49 @@ def secondary(sv, torch, dev, hip, sets, dsets, ws, args):
     ms = start.elapsed_time(stop) / steps
     res["outcome_lookup"] = dict(ms_per_call=round(ms, 5),
                                  outcomes_per_s=round(B / (ms * 1e-3), 1))
+
+    # C5: verification plus keys (F=3, draft token skipped) from the same pass over the draft
+    # rows, against the two separate calls on the same inputs
+    log("C5 verification with keys from the same pass")
+    lg = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    full5 = [dict(t=lg(w.target), d=d5[r], x=x5[r], u=torch.from_numpy(w.uniforms).to(dev),
+                  kv=torch.from_numpy(w.kv_len).to(dev)) for r, w in enumerate(c5[:4])]
+    out = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+               tau=torch.empty(B, dtype=torch.int32, device=dev),
+               kv_len=torch.empty(B, dtype=torch.int32, device=dev),
+               p=torch.empty((B, K), dtype=torch.float32, device=dev),
+               q=torch.empty((B, K), dtype=torch.float32, device=dev))
+    outk = dict(out, keys=torch.empty((B, K, F), dtype=torch.int32, device=dev),
+                key_prob=torch.empty((B, K, F), dtype=torch.float32, device=dev))
+    T5 = float(c5[0].T)
+
+    def fused(i):
+        s = full5[i % 4]
+        sv.spec_verify_sample_keys(s["t"], s["d"], s["x"], s["u"], s["kv"], T5, F, ws,
+                                   exclude_draft=True, out=outk)
+
+    def separate(i):
+        s = full5[i % 4]
+        sv.spec_verify_sample(s["t"], s["d"], s["x"], s["u"], s["kv"], T5, ws, out=out)
+        sv.spec_predict_outcomes(s["d"], F, T5, ws, out=outp)
+
+    for name, fn in (("fused", fused), ("separate", separate)):
+        for i in range(10):
+            fn(i)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            fn(i)
+        stop.record()
+        torch.cuda.synchronize()
+        res.setdefault("sample_keys_c5", {})[f"{name}_ms_per_call"] = round(
+            start.elapsed_time(stop) / steps, 5)
+    vb = B * (2 * K + 1) * V * 2
+    r5 = res["sample_keys_c5"]
+    r5.update(F=F, draft_token_skipped=True, bytes_per_call=vb,
+              hbm_gbps=round(vb / (r5["fused_ms_per_call"] * 1e-3) / 1e9, 1),
+              rows_per_s=round(B * K / (r5["fused_ms_per_call"] * 1e-3), 1))
     return res
 
 

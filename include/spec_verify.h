@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 3
+#define SPEC_ABI_VERSION 4
 #define SPEC_MAX_K 64
 #define SPEC_MAX_F 16
 #define SPEC_MAX_V 4194304 /* 2^22 */
@@ -140,6 +140,27 @@ int spec_verify_sample_ex(const void* target_logits, const void* draft_logits, i
                           float* out_p, float* out_q,
                           void* workspace, size_t workspace_bytes, hipStream_t stream,
                           hipEvent_t* events, int wait_polls);
+
+/* spec_verify_sample plus the outcome keys of every slot, computed from the same pass over the
+ * draft rows ([SSD] section "1. Outcome Prediction": the keys are the draft's top logits; reading
+ * the draft rows once for both saves the separate pass of spec_predict_outcomes).
+ * Results of the verification are identical to spec_verify_sample's, bit for bit.
+ *   F             keys per slot, 1 <= F (+1 when exclude_draft) <= min(SPEC_MAX_F, V);
+ *   exclude_draft nonzero: slot k skips the draft token x_k (see spec_predict_fanout);
+ *   out_keys      [B,K,F] int32 (required): slot k's F tokens with the largest draft logits,
+ *                 ordered by logit descending then id ascending (x_k skipped when asked);
+ *   out_key_prob  [B,K,F] float (nullable): q_k(key) at the call's temperature, from the same
+ *                 row statistics as out_q.
+ * Three launches (statistics, draw, key merge; the merge re-reads only the parts of the draft
+ * rows that can hold a key, from the wave maxima the statistics pass keeps); errors as for
+ * spec_verify_sample, SPEC_ERR_ARG also for F out of range or a null out_keys. */
+int spec_verify_sample_keys(const void* target_logits, const void* draft_logits, int dtype,
+                            const int32_t* draft_tokens, const float* uniforms,
+                            const int32_t* kv_len_in, int B, int K, int V, float temperature,
+                            int F, int exclude_draft, int32_t* out_tokens, int32_t* out_tau,
+                            int32_t* out_kv_len, float* out_p, float* out_q, int32_t* out_keys,
+                            float* out_key_prob, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /* Greedy verification, temperature must be exactly 0 ([SD] stage 3 at temperature zero;
  * [D3D] 検証のしくみ③, 検証のまとめ). g_k = argmax_v target_logits[b,k,v] (lowest v on ties);

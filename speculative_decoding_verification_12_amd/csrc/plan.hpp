@@ -107,6 +107,8 @@ struct WsLayout {
   size_t part_topf;  // 8 B [B*K*nchunk*4*kWaveSlots]: each wave's candidate list
   size_t part_pcnt;  // 4 B [B*K*nchunk*4]: entries in each wave's list
   size_t part_pstat; // 8 B [B*K*nchunk*4]: each wave's (max, scaled sum)
+  size_t part_vwm;   // 4 B [B*K*nchunk*4]: wave maxima of the draft rows (outcome keys)
+  size_t part_vrow;  // 16 B [B*K]: merged draft-row statistics for the key probabilities
   size_t total;
 };
 
@@ -147,6 +149,10 @@ inline WsLayout ws_layout(int B, int K, int V, int F) {
   off = align256(off + 4 * b * k * np * 4);
   L.part_pstat = off;
   off = align256(off + 8 * b * k * np * 4);
+  L.part_vwm = off;
+  off = align256(off + 4 * b * k * ns * 4);
+  L.part_vrow = off;
+  off = align256(off + 16 * b * k);
   L.total = off;
   return L;
 }

@@ -30,6 +30,9 @@ template <> struct Elem<uint16_t> {
   __device__ static __forceinline__ float one(const uint16_t* p, int i) {
     return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
   }
+  // the stored bits, converted later with cvt (a load issued now, waited for at first use)
+  __device__ static __forceinline__ uint32_t raw(const uint16_t* p, int i) { return p[i]; }
+  __device__ static __forceinline__ float cvt(uint32_t r) { return __uint_as_float(r << 16); }
   // element j of a vector stored as 32-bit words (e.g. in LDS)
   __device__ static __forceinline__ float from_words(const uint32_t* w, int j) {
     const uint32_t x = w[j >> 1];
@@ -49,6 +52,10 @@ template <> struct Elem<float> {
   static constexpr int N = 4;
   static constexpr uint32_t kNegInfWord = 0xFF800000u;
   __device__ static __forceinline__ float one(const float* p, int i) { return p[i]; }
+  __device__ static __forceinline__ uint32_t raw(const float* p, int i) {
+    return __float_as_uint(p[i]);
+  }
+  __device__ static __forceinline__ float cvt(uint32_t r) { return __uint_as_float(r); }
   __device__ static __forceinline__ float from_words(const uint32_t* w, int j) {
     return __uint_as_float(w[j]);
   }

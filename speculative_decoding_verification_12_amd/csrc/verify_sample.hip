@@ -88,11 +88,13 @@ __device__ __forceinline__ void thread_chunk_stats(const TIn* row, const RowSpan
   }
 }
 
-// Block reduction of the threads' (m, s); the result is valid in thread 0.
+// Block reduction of the threads' (m, s); the result is valid in thread 0. With `wave_max_out`,
+// lane 0 of every wave also stores its wave's maximum there (indexed by wave).
 __device__ __forceinline__ void block_stats(float m, float s, float c, float* sm, float* ss,
-                                            float& M, float& S) {
+                                            float& M, float& S, float* wave_max_out = nullptr) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const float wm = wave_max(m);
+  if (wave_max_out != nullptr && lane == 0) wave_max_out[w] = wm;
   const float sc = (m > -INFINITY) ? s * fast_exp2(m * c - wm * c) : 0.f;
   const float ws = wave_sum(sc);
   if (lane == 0) {
@@ -119,11 +121,12 @@ __device__ __forceinline__ const TIn* slot_row(const TIn* tgt, const TIn* drf, i
                 : drf + (static_cast<size_t>(b) * K + (r - K - 1)) * static_cast<size_t>(V);
 }
 
-template <typename TIn>
+template <typename TIn, bool kKeys>
 __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
     const TIn* __restrict__ tgt, const TIn* __restrict__ drf, const int32_t* __restrict__ xtok,
     int K, int V, float c, int nchunk, int cv, float2* __restrict__ part,
-    float* __restrict__ gath, uint64_t* __restrict__ clear, int nclear) {
+    float* __restrict__ gath, uint64_t* __restrict__ clear, int nclear,
+    float* __restrict__ key_wave_max) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
   __shared__ float sm[kWaves], ss[kWaves];
@@ -155,7 +158,12 @@ __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
 
   float m, s, M, S;
   thread_chunk_stats(row, sp, cr, V, c, m, s);
-  block_stats(m, s, c, sm, ss, M, S);
+  // with outcome keys, a draft row's waves also keep their maxima (they bound where the row's
+  // top tokens can be; the key merge re-reads only the waves that can hold one)
+  float* wmax = (kKeys && r > K)
+                    ? key_wave_max + ((static_cast<size_t>(b) * K + slot) * nchunk + ch) * kWaves
+                    : nullptr;
+  block_stats(m, s, c, sm, ss, M, S, wmax);
   if (threadIdx.x == 0) part[static_cast<size_t>(rb) * nchunk + ch] = make_float2(M, S);
 }
 
@@ -322,16 +330,306 @@ __device__ __forceinline__ bool poll_mass(const uint64_t* p, int polls, double& 
 // most draw chunks a row of V <= SPEC_MAX_V elements can have (f32 rows: 4 elements per vector)
 constexpr int kMaxDrawChunks = (SPEC_MAX_V / 4 + kBlock * kDrawVecs - 1) / (kBlock * kDrawVecs);
 
+// ------------------------------------------------------------------------------ key merge
+// Outcome keys from the statistics pass ([SSD] section "1. Outcome Prediction": the placed
+// token is predicted from the draft's top logits). That pass keeps, for every wave of a draft
+// row, the wave's maximum. Let t be the F'-th largest of these maxima (F' = F, or F + 1 when the
+// draft token is skipped), ties counted: F' waves hold an element >= t, so the F'-th largest
+// element of the row is >= t and every one of the row's top F' sits in a wave whose maximum
+// reaches t. Only those waves (usually F') are read again, each by one wave of the merging
+// workgroup, which keeps the best F' of its elements by F' rounds of (value, id) argmax, each
+// round excluding everything at or before the previous pick; wave 0 merges the four results.
+constexpr int kSentinelId = 0x7fffffff;
+
+__device__ __forceinline__ bool after_in_order(float v, int i, float pv, int pi) {
+  return v < pv || (v == pv && i > pi);
+}
+
+__device__ __forceinline__ int lanes_below(unsigned long long bal) {
+  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+      static_cast<uint32_t>(bal >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u)));
+}
+
+// The wave's F-th largest lane maximum, ties counted (-inf when fewer than F lanes hold
+// elements).
+__device__ __forceinline__ float wave_fth_max(float lane_max, bool has, int F) {
+  float theta = -INFINITY, cur = has ? lane_max : -INFINITY;
+  bool in = has;
+  int need = F;
+  while (need > 0) {   // uniform: every quantity below is wave-wide
+    if (__ballot(in) == 0ull) {
+      theta = -INFINITY;
+      break;
+    }
+    const float mx = wave_max(in ? cur : -INFINITY);
+    const bool at = in && cur == mx;
+    need -= __popcll(__ballot(at));
+    theta = mx;
+    if (at) in = false;
+  }
+  return theta;
+}
+
+// Replaces the running best (lanes 0..Fp-1 hold picks in order) by the best Fp of itself and
+// the candidates each lane offers through `offer(pv, pi, bv, bi)` (its best entry after (pv, pi)).
+template <typename Offer>
+__device__ __forceinline__ void merge_running(float& rv, int& ri, int Fp, Offer offer) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const float hv = lane < Fp ? rv : -INFINITY;
+  const int hi = lane < Fp ? ri : kSentinelId;
+  float pv = INFINITY, nv = -INFINITY;
+  int pi = -1, ni = kSentinelId;
+  for (int f = 0; f < Fp; ++f) {
+    float bv = -INFINITY;
+    int bi = kSentinelId;
+    if (hi != kSentinelId && after_in_order(hv, hi, pv, pi) && better(hv, hi, bv, bi)) {
+      bv = hv;
+      bi = hi;
+    }
+    offer(pv, pi, bv, bi);
+    wave_argmax(bv, bi);
+    pv = bv;
+    pi = bi;
+    if (lane == f) {
+      nv = bv;
+      ni = bi;
+    }
+  }
+  rv = nv;
+  ri = ni;
+}
+
+struct RowStat {   // a row's merged statistics: max and sum of 2^(l*c - fl(max*c))
+  float M;
+  float pad;
+  double S;
+};
+
+// Outcome keys computed alongside the verification: where the statistics pass left the wave
+// maxima and where the keys go.
+struct KeyArgs {
+  int pick;            // tokens looked for per slot: F, or F + 1 with the draft token skipped
+  int F;               // keys written per slot
+  int exclude;         // skip the draft token
+  int cv_s;            // statistics chunk size (vectors)
+  const float* wave_max;   // [B,K,nchunk_s,4]: the statistics pass's wave maxima of draft rows
+  RowStat* row_stats;      // [B,K]: the draw's merged draft-row statistics
+  int32_t* out_keys;       // [B,K,F]
+  float* out_prob;         // [B,K,F] or null
+};
+
+// One workgroup of kMergeWaves waves per (request, draft slot).
+constexpr int kMergeWaves = 8;
+
+template <typename TIn>
+__global__ __launch_bounds__(kMergeWaves * kWave) void keys_merge_kernel(const TIn* __restrict__ drf,
+                                                            const int32_t* __restrict__ xtok,
+                                                            int K, int V, float c, int nchunk_s,
+                                                            KeyArgs ka) {
+  using E = Elem<TIn>;
+  constexpr int N = E::N;
+  __shared__ float s_cv[kMergeWaves][kWave];
+  __shared__ int s_ci[kMergeWaves][kWave];
+  __shared__ int s_cnt[kMergeWaves];
+  __shared__ float s_pv[SPEC_MAX_F];
+  __shared__ int s_pi[SPEC_MAX_F];
+  const size_t bk = blockIdx.x;   // b * K + k
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int nl = nchunk_s * kWaves;
+  const int Fp = ka.pick;
+  const float* wmx = ka.wave_max + bk * nl;
+  // everything this workgroup reads that does not depend on t goes out first
+  const int xk = ka.exclude ? xtok[bk] : -1;
+  const RowStat rs = ka.row_stats[bk];
+  constexpr int kHeldMax = 4;   // wave maxima a lane keeps (lists of up to 256 waves)
+  float hm[kHeldMax];
+#pragma unroll
+  for (int h = 0; h < kHeldMax; ++h) {
+    const int j = lane + h * kWave;
+    const float v = wmx[j < nl ? j : nl - 1];   // unconditional: all loads in flight at once
+    hm[h] = j < nl ? v : -INFINITY;
+  }
+  const bool more = nl > kHeldMax * kWave;   // uniform; longer lists are re-read
+
+  // ---- t, the Fp-th largest wave maximum (ties counted; -inf with fewer than Fp), computed by
+  // every wave alike
+  float t = -INFINITY;
+  {
+    float pv = INFINITY;
+    int pi = -1;
+    for (int f = 0; f < Fp; ++f) {
+      float bv = -INFINITY;
+      int bi = kSentinelId;
+#pragma unroll
+      for (int h = 0; h < kHeldMax; ++h) {
+        const int j = lane + h * kWave;
+        if (j < nl && after_in_order(hm[h], j, pv, pi) && better(hm[h], j, bv, bi)) {
+          bv = hm[h];
+          bi = j;
+        }
+      }
+      if (more)
+        for (int j = lane + kHeldMax * kWave; j < nl; j += kWave) {
+          const float v = wmx[j];
+          if (after_in_order(v, j, pv, pi) && better(v, j, bv, bi)) {
+            bv = v;
+            bi = j;
+          }
+        }
+      wave_argmax(bv, bi);
+      pv = bv;
+      pi = bi;
+      t = bi == kSentinelId ? -INFINITY : bv;
+    }
+  }
+
+  // ---- every wave: its share of the chosen waves (in order, dealt out round robin). Every
+  // element >= t (the row's top Fp among them) goes to the wave's LDS list, numbered by ballot
+  // one column of elements at a time (a column without any costs one scalar branch); the best
+  // Fp of the list follow by Fp rounds of argmax. A wave whose list would pass 64 entries (many
+  // elements equal to t) redoes its share exactly, element by element.
+  const TIn* row = drf + bk * static_cast<size_t>(V);
+  const RowSpan sp = row_span(row, V);
+  const uint4* vrow = reinterpret_cast<const uint4*>(row + sp.head);
+  float rv = -INFINITY;
+  int ri = kSentinelId;
+  // visit(exact): calls with every chosen wave of this wave's share, exact or listing
+  auto share = [&](auto&& chunk_fn) {
+    int nchosen = 0;   // uniform
+    for (int base = 0; base < nl; base += kWave) {
+      const int j = base + lane;
+      float mj = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < kHeldMax; ++h)
+        if (base == h * kWave) mj = hm[h];
+      if (base >= kHeldMax * kWave && j < nl) mj = wmx[j];
+      const unsigned long long pick = __ballot(j < nl && mj >= t);
+      for (unsigned long long m = pick; m != 0ull; m &= m - 1ull) {   // uniform
+        const int jj = base + __ffsll(static_cast<long long>(m)) - 1;
+        if ((nchosen++ % kMergeWaves) == w) chunk_fn(jj / kWaves, jj % kWaves);
+      }
+    }
+  };
+  // the elements a statistics thread held: (ok, value, id) for each, head and tail first
+  auto elements = [&](int ch, int sw, auto&& fn) {
+    const ChunkRange cr = chunk_range(sp, ch, nchunk_s, ka.cv_s);
+    const int st = sw * kWave + lane;   // the statistics thread whose elements this lane takes
+    const bool hh = cr.first && st < sp.head, ht = cr.last && st < V - sp.tail;
+    uint32_t rh = 0u, rt = 0u;
+    if ((cr.first && sp.head > 0) || (cr.last && V > sp.tail)) {   // uniform
+      rh = E::raw(row, min(st, V - 1));
+      rt = E::raw(row, min(sp.tail + st, V - 1));
+    }
+    fn(hh, hh ? E::cvt(rh) : -INFINITY, st);
+    fn(ht, ht ? E::cvt(rt) : -INFINITY, sp.tail + st);
+    for (int pbase = cr.vbeg; pbase < cr.vend; pbase += kPassVecs) {
+      uint4 qv[kVecPerThread];
+#pragma unroll
+      for (int i = 0; i < kVecPerThread; ++i)
+        qv[i] = vrow[min(pbase + i * kBlock + st, cr.vend - 1)];
+#pragma unroll
+      for (int i = 0; i < kVecPerThread; ++i) {
+        const int vi = pbase + i * kBlock + st;
+        float x[N];
+        E::unpack(qv[i], x);
+#pragma unroll
+        for (int e = 0; e < N; ++e) fn(vi < cr.vend, x[e], sp.head + vi * N + e);
+      }
+    }
+  };
+  int cnt = 0;   // uniform
+  share([&](int ch, int sw) {
+    elements(ch, sw, [&](bool ok, float v, int id) {
+      const unsigned long long bal = __ballot(ok && v >= t);
+      if (bal == 0ull) return;
+      const int at = cnt + lanes_below(bal);
+      if (ok && v >= t && at < kWave) {
+        s_cv[w][at] = v;
+        s_ci[w][at] = id;
+      }
+      cnt += __popcll(bal);
+    });
+  });
+  if (cnt > kWave) {   // rare: the wave's exact best Fp replace its list
+    share([&](int ch, int sw) {
+      merge_running(rv, ri, Fp, [&](float pv, int pi, float& bv, int& bi) {
+        elements(ch, sw, [&](bool ok, float v, int id) {
+          if (ok && v >= t && after_in_order(v, id, pv, pi) && better(v, id, bv, bi)) {
+            bv = v;
+            bi = id;
+          }
+        });
+      });
+    });
+    __builtin_amdgcn_wave_barrier();
+    if (lane < Fp) {
+      s_cv[w][lane] = rv;
+      s_ci[w][lane] = ri;
+    }
+    cnt = Fp;
+  }
+  if (lane == 0) s_cnt[w] = cnt;
+  __syncthreads();
+  if (w != 0) return;
+
+  // ---- wave 0: every candidate's rank in the order (value desc, id asc) among all of them;
+  // ranks 0..Fp-1 are the picks, in order. The keys skip the draft token.
+  // candidate g of the lists laid end to end: list lw, entry lj
+  int pre[kMergeWaves + 1];   // uniform prefix sums of the list lengths
+  pre[0] = 0;
+#pragma unroll
+  for (int i = 0; i < kMergeWaves; ++i) pre[i + 1] = pre[i] + s_cnt[i];
+  const int tot = pre[kMergeWaves];
+  for (int g0 = 0; g0 < tot; g0 += kWave) {   // uniform
+    const int g = g0 + lane;
+    int lw = 0, lj = g;
+#pragma unroll
+    for (int i = 1; i < kMergeWaves; ++i)
+      if (g >= pre[i]) {
+        lw = i;
+        lj = g - pre[i];
+      }
+    const bool mine = g < tot;
+    const float v = mine ? s_cv[lw][lj] : -INFINITY;
+    const int id = mine ? s_ci[lw][lj] : kSentinelId;
+    int rank = 0;
+#pragma unroll
+    for (int wl = 0; wl < kMergeWaves; ++wl)
+      for (int h = 0; h < pre[wl + 1] - pre[wl]; ++h)   // uniform
+        rank += better(s_cv[wl][h], s_ci[wl][h], v, id) ? 1 : 0;
+    if (mine && rank < Fp) {
+      s_pv[rank] = v;
+      s_pi[rank] = id;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  // lane f writes pick f (one lane per key); a pick equal to the draft token is skipped and the
+  // later picks move up by one
+  const bool valid = lane < Fp && lane < tot;
+  const int pid = valid ? s_pi[lane] : kSentinelId;
+  const float pvv = valid ? s_pv[lane] : -INFINITY;
+  const unsigned long long xm = __ballot(valid && pid == xk);
+  const int xpos = xm ? __ffsll(static_cast<long long>(xm)) - 1 : kWave;
+  const int pos = lane - (xpos < lane ? 1 : 0);
+  if (valid && lane != xpos && pos < ka.F) {
+    const size_t o = bk * ka.F + pos;
+    ka.out_keys[o] = pid;
+    if (ka.out_prob)
+      ka.out_prob[o] = static_cast<float>(
+          exp2_wide(static_cast<double>(pvv) * c - static_cast<double>(rs.M * c)) / rs.S);
+  }
+}
+
 // Chunks of kBlock * kDrawVecs vectors (see draw_plan). cm holds the published (R, P) of every
 // chunk, [b][ch][2] words, zeroed by the statistics kernel of the same call.
-template <typename TIn>
+template <typename TIn, bool kKeys>
 __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     const TIn* __restrict__ tgt, const TIn* __restrict__ drf, const int32_t* __restrict__ xtok,
     const float* __restrict__ uni, const int32_t* __restrict__ kv_in, int K, int V, float c,
     int nchunk_s, const float2* __restrict__ part_s, const float* __restrict__ gath,
     int nchunk, int cv, uint64_t* __restrict__ cm, int wait_polls,
     int32_t* __restrict__ out_tok, int32_t* __restrict__ out_tau, int32_t* __restrict__ out_kv,
-    float* __restrict__ out_p, float* __restrict__ out_q) {
+    float* __restrict__ out_p, float* __restrict__ out_q, KeyArgs ka) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
   __shared__ double s_red[2][kWaves];
@@ -420,6 +718,10 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       const unsigned long long rej = __ballot(valid && !keep);
       const int mm = rej ? (__ffsll(static_cast<long long>(rej)) - 1) : K;
       if (ch == 0) {   // one workgroup of the request writes everything but the drawn token
+        if constexpr (kKeys)   // the draft rows' statistics, for the key probabilities
+          if (valid)
+            ka.row_stats[static_cast<size_t>(b) * K + lane] =
+                RowStat{row_m[K + 1 + lane], 0.f, row_s[K + 1 + lane]};
         if (valid) {
           const size_t o = static_cast<size_t>(b) * K + lane;
           if (out_p) out_p[o] = err ? NAN : static_cast<float>(pk);
@@ -446,6 +748,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     __syncthreads();
   }
   const ReqState st = s_st;
+
   if (st.m < 0) return;   // row error: nothing to draw (every workgroup of b agrees)
 
   DrawRows<TIn> R;
@@ -633,16 +936,26 @@ struct SamplePlan {
 };
 
 template <typename TIn>
-SamplePlan default_sample_plan(int B, int K, int V) {
+SamplePlan default_sample_plan(int B, int K, int V, bool keys) {
   constexpr int N = 16 / sizeof(TIn);
+  (void)keys;   // the keys path streams the rows with the same plan
   return SamplePlan{stats_plan(B, K, V, N), draw_plan(B, K, V, N)};
 }
 
-template <typename TIn>
-int launch_sample(const void* target, const void* draft, const int32_t* xtok, const float* uni,
-                  const int32_t* kv_in, int B, int K, int V, float T, int32_t* out_tok,
-                  int32_t* out_tau, int32_t* out_kv, float* out_p, float* out_q, void* ws,
-                  hipStream_t stream, hipEvent_t* ev, int wait_polls, const SamplePlan& P) {
+// keys: F > 0 computes outcome keys during the same two launches
+struct KeyRequest {
+  int F;
+  int exclude;
+  int32_t* out_keys;
+  float* out_prob;
+};
+
+template <typename TIn, bool kKeys>
+int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, const float* uni,
+                    const int32_t* kv_in, int B, int K, int V, float T, int32_t* out_tok,
+                    int32_t* out_tau, int32_t* out_kv, float* out_p, float* out_q, void* ws,
+                    hipStream_t stream, hipEvent_t* ev, int wait_polls, const SamplePlan& P,
+                    const KeyRequest& kr) {
   const size_t g1 = static_cast<size_t>(B) * (2 * K + 1) * P.stats.nchunk;
   const size_t g2 = static_cast<size_t>(B) * P.draw.nchunk;
   if (!grid_fits(g1) || !grid_fits(g2) || P.draw.cv != kBlock * kDrawVecs ||
@@ -655,27 +968,55 @@ int launch_sample(const void* target, const void* draft, const int32_t* xtok, co
   float2* part1 = ws_ptr<float2>(ws, L.part_stats);
   float* gath = ws_ptr<float>(ws, L.gathered);
   uint64_t* cm = ws_ptr<uint64_t>(ws, L.part_draw);
+  float* kwmax = ws_ptr<float>(ws, L.part_vwm);
   const int nclear = static_cast<int>(g2 * 2);
   const dim3 grid1(static_cast<unsigned>(g1)), grid2(static_cast<unsigned>(g2)), block(kBlock);
   const int ns = P.stats.nchunk, cs = P.stats.cv, nd = P.draw.nchunk, cd = P.draw.cv;
   const int polls = wait_polls < 0 ? SPEC_DEFAULT_WAIT_POLLS : wait_polls;
+  const int pick = kr.F + (kr.exclude ? 1 : 0);
+  RowStat* krows = ws_ptr<RowStat>(ws, L.part_vrow);
+  const KeyArgs ka{pick, kr.F, kr.exclude, cs, kwmax, krows, kr.out_keys, kr.out_prob};
+  const dim3 grid3(static_cast<unsigned>(static_cast<size_t>(B) * K));
   if (ev == nullptr) {
-    hipLaunchKernelGGL(sample_stats_kernel<TIn>, grid1, block, 0, stream, t, d, xtok, K, V, c, ns,
-                       cs, part1, gath, cm, nclear);
-    hipLaunchKernelGGL(sample_draw_kernel<TIn>, grid2, block, 0, stream, t, d, xtok, uni, kv_in,
-                       K, V, c, ns, static_cast<const float2*>(part1),
+    hipLaunchKernelGGL((sample_stats_kernel<TIn, kKeys>), grid1, block, 0, stream, t, d, xtok, K,
+                       V, c, ns, cs, part1, gath, cm, nclear, kwmax);
+    hipLaunchKernelGGL((sample_draw_kernel<TIn, kKeys>), grid2, block, 0, stream, t, d, xtok, uni,
+                       kv_in, K, V, c, ns, static_cast<const float2*>(part1),
                        static_cast<const float*>(gath), nd, cd, cm, polls, out_tok, out_tau,
-                       out_kv, out_p, out_q);
+                       out_kv, out_p, out_q, ka);
+    if constexpr (kKeys)
+      hipLaunchKernelGGL(keys_merge_kernel<TIn>, grid3, dim3(kMergeWaves * kWave), 0, stream, d,
+                         xtok, K, V, c, ns, ka);
   } else {
     // profiling: the runtime records the events at each kernel's start and end
-    hipExtLaunchKernelGGL(sample_stats_kernel<TIn>, grid1, block, 0, stream, ev[0], ev[1], 0, t,
-                          d, xtok, K, V, c, ns, cs, part1, gath, cm, nclear);
-    hipExtLaunchKernelGGL(sample_draw_kernel<TIn>, grid2, block, 0, stream, ev[2], ev[3], 0, t, d,
-                          xtok, uni, kv_in, K, V, c, ns, static_cast<const float2*>(part1),
-                          static_cast<const float*>(gath), nd, cd, cm, polls, out_tok, out_tau,
-                          out_kv, out_p, out_q);
+    hipExtLaunchKernelGGL((sample_stats_kernel<TIn, kKeys>), grid1, block, 0, stream, ev[0],
+                          ev[1], 0, t, d, xtok, K, V, c, ns, cs, part1, gath, cm, nclear,
+                          kwmax);
+    hipExtLaunchKernelGGL((sample_draw_kernel<TIn, kKeys>), grid2, block, 0, stream, ev[2],
+                          ev[3], 0, t, d, xtok, uni, kv_in, K, V, c, ns,
+                          static_cast<const float2*>(part1), static_cast<const float*>(gath), nd,
+                          cd, cm, polls, out_tok, out_tau, out_kv, out_p, out_q, ka);
+    if constexpr (kKeys)
+      hipLaunchKernelGGL(keys_merge_kernel<TIn>, grid3, dim3(kMergeWaves * kWave), 0, stream, d,
+                         xtok, K, V, c, ns, ka);
   }
   return launch_status();
+}
+
+template <typename TIn>
+int launch_sample(const void* target, const void* draft, const int32_t* xtok, const float* uni,
+                  const int32_t* kv_in, int B, int K, int V, float T, int32_t* out_tok,
+                  int32_t* out_tau, int32_t* out_kv, float* out_p, float* out_q, void* ws,
+                  hipStream_t stream, hipEvent_t* ev, int wait_polls, const KeyRequest& kr) {
+  const bool keys = kr.F > 0;
+  const SamplePlan P = default_sample_plan<TIn>(B, K, V, keys);
+  if (keys)
+    return launch_sample_t<TIn, true>(target, draft, xtok, uni, kv_in, B, K, V, T, out_tok,
+                                      out_tau, out_kv, out_p, out_q, ws, stream, ev, wait_polls,
+                                      P, kr);
+  return launch_sample_t<TIn, false>(target, draft, xtok, uni, kv_in, B, K, V, T, out_tok,
+                                     out_tau, out_kv, out_p, out_q, ws, stream, ev, wait_polls, P,
+                                     kr);
 }
 
 int verify_sample_entry(const void* target_logits, const void* draft_logits, int dtype,
@@ -683,7 +1024,8 @@ int verify_sample_entry(const void* target_logits, const void* draft_logits, int
                         const int32_t* kv_len_in, int B, int K, int V, float temperature,
                         int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len, float* out_p,
                         float* out_q, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream, hipEvent_t* events, int wait_polls) {
+                        hipStream_t stream, hipEvent_t* events, int wait_polls,
+                        const KeyRequest& kr) {
   int rc = check_dtype(dtype);
   if (rc != SPEC_OK) return rc;
   if ((rc = check_dims(B, K, V)) != SPEC_OK) return rc;
@@ -691,6 +1033,10 @@ int verify_sample_entry(const void* target_logits, const void* draft_logits, int
       check_logits(draft_logits, dtype) != SPEC_OK || draft_tokens == nullptr ||
       uniforms == nullptr || out_tokens == nullptr || out_tau == nullptr)
     return SPEC_ERR_ARG;
+  if (kr.F != 0) {
+    const int pick = kr.F + (kr.exclude ? 1 : 0);
+    if (kr.F < 1 || pick > SPEC_MAX_F || pick > V || kr.out_keys == nullptr) return SPEC_ERR_ARG;
+  }
   if (!std::isfinite(temperature) || !(temperature > 0.f) ||
       !std::isfinite(exp2_scale(temperature)))
     return SPEC_ERR_TEMPERATURE;
@@ -701,12 +1047,10 @@ int verify_sample_entry(const void* target_logits, const void* draft_logits, int
   if (dtype == SPEC_BF16)
     return launch_sample<uint16_t>(target_logits, draft_logits, draft_tokens, uniforms, kv_len_in,
                                    B, K, V, temperature, out_tokens, out_tau, out_kv_len, out_p,
-                                   out_q, workspace, stream, events, wait_polls,
-                                   default_sample_plan<uint16_t>(B, K, V));
+                                   out_q, workspace, stream, events, wait_polls, kr);
   return launch_sample<float>(target_logits, draft_logits, draft_tokens, uniforms, kv_len_in, B,
                               K, V, temperature, out_tokens, out_tau, out_kv_len, out_p, out_q,
-                              workspace, stream, events, wait_polls,
-                              default_sample_plan<float>(B, K, V));
+                              workspace, stream, events, wait_polls, kr);
 }
 
 }  // namespace
@@ -721,7 +1065,7 @@ extern "C" int spec_verify_sample(const void* target_logits, const void* draft_l
   return sv::verify_sample_entry(target_logits, draft_logits, dtype, draft_tokens, uniforms,
                                  kv_len_in, B, K, V, temperature, out_tokens, out_tau,
                                  out_kv_len, out_p, out_q, workspace, workspace_bytes, stream,
-                                 nullptr, -1);
+                                 nullptr, -1, sv::KeyRequest{0, 0, nullptr, nullptr});
 }
 
 extern "C" int spec_verify_sample_ex(const void* target_logits, const void* draft_logits,
@@ -734,5 +1078,21 @@ extern "C" int spec_verify_sample_ex(const void* target_logits, const void* draf
   return sv::verify_sample_entry(target_logits, draft_logits, dtype, draft_tokens, uniforms,
                                  kv_len_in, B, K, V, temperature, out_tokens, out_tau,
                                  out_kv_len, out_p, out_q, workspace, workspace_bytes, stream,
-                                 events, wait_polls);
+                                 events, wait_polls, sv::KeyRequest{0, 0, nullptr, nullptr});
+}
+
+extern "C" int spec_verify_sample_keys(const void* target_logits, const void* draft_logits,
+                                       int dtype, const int32_t* draft_tokens,
+                                       const float* uniforms, const int32_t* kv_len_in, int B,
+                                       int K, int V, float temperature, int F, int exclude_draft,
+                                       int32_t* out_tokens, int32_t* out_tau,
+                                       int32_t* out_kv_len, float* out_p, float* out_q,
+                                       int32_t* out_keys, float* out_key_prob, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  if (F < 1) return SPEC_ERR_ARG;
+  return sv::verify_sample_entry(target_logits, draft_logits, dtype, draft_tokens, uniforms,
+                                 kv_len_in, B, K, V, temperature, out_tokens, out_tau,
+                                 out_kv_len, out_p, out_q, workspace, workspace_bytes, stream,
+                                 nullptr, -1,
+                                 sv::KeyRequest{F, exclude_draft ? 1 : 0, out_keys, out_key_prob});
 }

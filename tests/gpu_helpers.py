@@ -203,3 +203,27 @@ def compare_lookup(wl, keys, fanout, all_accept=True):
                                   int(tokens[b, max(int(tau[b]) - 1, 0)]), all_accept)
         assert int(got[b]) == exp, f"request {b}: lookup {got[b]} != {exp}"
     return got
+
+
+def gpu_sample_keys(wl, F, exclude, dev=None, ws=None):
+    dev = dev or upload(wl)
+    B, K = wl.B, wl.K
+    ws = ws if ws is not None else sv.new_workspace(B, K, wl.V)
+    out = dict(tokens=poisoned((B, K + 1), torch.int32), tau=poisoned((B,), torch.int32),
+               kv_len=poisoned((B,), torch.int32), p=poisoned((B, K), torch.float32),
+               q=poisoned((B, K), torch.float32), keys=poisoned((B, K, F), torch.int32),
+               key_prob=poisoned((B, K, F), torch.float32))
+    sv.spec_verify_sample_keys(dev["target"], dev["draft"], dev["tokens"], dev["uniforms"],
+                               dev["kv"], float(wl.T), F, ws, exclude_draft=exclude, out=out)
+    torch.cuda.synchronize()
+    return {k: _np(v) for k, v in out.items()}
+
+
+def compare_sample_keys(wl, gpu, F, exclude, requests=None):
+    """Verification parity as compare_sample; keys and key probabilities as the per-slot fan-out
+    oracle with F keys on every slot."""
+    verify = {k: gpu[k] for k in ("tokens", "tau", "kv_len", "p", "q")}
+    res = compare_sample(wl, verify, requests)
+    keys = dict(keys=gpu["keys"].reshape(wl.B, -1), key_prob=gpu["key_prob"].reshape(wl.B, -1))
+    compare_fanout(wl, keys, [F] * wl.K, float(wl.T), exclude, requests)
+    return res

@@ -123,6 +123,26 @@ def test_sample_ex_validation(lib):
     assert call(ctypes.cast(events, ctypes.c_void_p), -1, ws=ws, wsb=need) == code["SPEC_ERR_ARG"]
 
 
+def test_sample_keys_validation(lib):
+    code = {v: k for k, v in sv.STATUS.items()}
+
+    def call(F=3, excl=0, keys=FAKE, **kw):
+        a = dict(t=FAKE, d=FAKE, dtype=1, x=FAKE, u=FAKE, kv=NULL, B=2, K=4, V=1000, T=1.0,
+                 tok=FAKE, tau=FAKE, kvo=NULL, p=NULL, q=NULL, ws=FAKE, wsb=0, s=NULL)
+        a.update(kw)
+        return lib.spec_verify_sample_keys(a["t"], a["d"], a["dtype"], a["x"], a["u"], a["kv"],
+                                           a["B"], a["K"], a["V"], a["T"], F, excl, a["tok"],
+                                           a["tau"], a["kvo"], a["p"], a["q"], keys, NULL,
+                                           a["ws"], a["wsb"], a["s"])
+    assert call(dtype=9) == code["SPEC_ERR_DTYPE"]
+    for kw in [dict(F=0), dict(F=17), dict(F=16, excl=1), dict(keys=NULL), dict(V=2, F=3),
+               dict(V=3, F=3, excl=1), dict(x=NULL), dict(K=65)]:
+        assert call(**kw) == code["SPEC_ERR_ARG"], kw
+    assert call(F=16) == code["SPEC_ERR_WORKSPACE"]
+    assert call(T=0.0) == code["SPEC_ERR_TEMPERATURE"]
+    assert call() == code["SPEC_ERR_WORKSPACE"]
+
+
 def test_greedy_validation(lib):
     code = {v: k for k, v in sv.STATUS.items()}
 

@@ -8,8 +8,9 @@ import torch
 import oracle
 import speculative_decoding_verification_12_amd as sv
 from gpu_helpers import (announce, compare_fanout, compare_greedy, compare_lookup,
-                         compare_predict, compare_sample, dev_logits, gpu_fanout, gpu_greedy,
-                         gpu_predict, gpu_sample, upload)
+                         compare_predict, compare_sample, compare_sample_keys, dev_logits,
+                         gpu_fanout, gpu_greedy, gpu_predict, gpu_sample, gpu_sample_keys,
+                         upload)
 from synthetic import make_tiny_random, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -98,6 +99,39 @@ def test_fanout_d3d_setting(mode):
         hits += int(np.sum(slots >= 0))
         n += wl.B
     announce(f"D3D setting {mode}: prepared-continuation hit rate {hits / n:.3f} ({hits}/{n})")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sample_keys_tiny_random(dtype):
+    """Verification with the keys from the same pass: ties (lists that overflow and are
+    recomputed), masked tokens, bad tokens, ragged V; the verification outputs equal the plain
+    call's bit for bit."""
+    for seed in range(24):
+        K = 1 + seed % 6
+        V = [3, 5, 8, 13, 40, 129, 1000, 4099][seed % 8]
+        T = [1.0, 0.7, 2.5][seed % 3]
+        F = min(1 + seed % 4, V - 1)
+        wl = make_tiny_random(seed, B=6, K=K, V=V, T=T, dtype=dtype, ties=seed % 2 == 0,
+                              neg_inf=0.2 if seed % 3 else 0.0,
+                              bad_token_rate=0.1 if seed % 5 == 0 else 0.0)
+        dev = upload(wl)
+        plain = gpu_sample(wl, dev=dev)
+        for exclude in (False, True):
+            announce(f"sample+keys seed={seed} dtype={dtype} K={K} V={V} F={F} excl={exclude}")
+            g = gpu_sample_keys(wl, F, exclude, dev=dev)
+            compare_sample_keys(wl, g, F, exclude)
+            for k in plain:
+                assert np.array_equal(plain[k].view(np.int32), g[k].view(np.int32)), k
+
+
+@pytest.mark.parametrize("V", [40000, 1_000_003])
+def test_sample_keys_massive_ties(V):
+    """Logits on a coarse grid: the statistics pass's candidate lists overflow and the merge
+    recomputes those waves exactly; keys must be the lowest ids among the equal top logits."""
+    wl = make_tiny_random(8, B=2, K=3, V=V, T=1.0, dtype="bf16", ties=True)
+    for F, exclude in ((1, False), (3, True), (15, True), (16, False)):
+        announce(f"sample+keys ties V={V} F={F} excl={exclude}")
+        compare_sample_keys(wl, gpu_sample_keys(wl, F, exclude), F, exclude)
 
 
 @pytest.mark.parametrize("V", [2, 7, 8, 9, 1000, 1001, 4097, 8191, 8192, 8193, 16389, 32064])
@@ -314,3 +348,19 @@ def test_c5_fanout_full(T):
     assert np.all((plain_slots < 0) | (slots >= 0))
     announce(f"C5 T={T} fan-out 3 per slot, draft token kept: hit rate "
              f"{np.mean(plain_slots >= 0):.3f}")
+
+
+@pytest.mark.parametrize("cid,rnd", [(5, 2), (3, 5), (4, 1)])
+def test_sample_keys_full_size(cid, rnd):
+    """C5 (keys with the verification of its target), C3 and C4 at full size: verification as
+    the plain call, keys and key probabilities on every (C4: sampled) request."""
+    wl = make_workload(cid, rnd)
+    dev = upload(wl)
+    announce(f"C{cid} sample+keys round {rnd}")
+    plain = gpu_sample(wl, dev=dev)
+    g = gpu_sample_keys(wl, 3, True, dev=dev)
+    for k in plain:
+        assert np.array_equal(plain[k].view(np.int32), g[k].view(np.int32)), k
+    idx = None if cid != 4 else sorted(set(range(0, 8)) | set(range(100, 108)))
+    n, f, fb = compare_sample_keys(wl, g, 3, True, requests=idx)
+    announce(f"C{cid} sample+keys: {n} checked, {f} flagged, {fb} differ")
