@@ -8,7 +8,7 @@ generators in `synthetic/` are the only code both sides use.
 Modules
   reference  vectorised NumPy oracle in float64 (greedy, sampling, outcome prediction with a
              uniform or per-slot fan-out, hit check and prepared-continuation lookup, draft
-             budget, decision margins and near-tie flags)
+             budget, paged KV-cache rewind, decision margins and near-tie flags)
   naive      the same rules as literal pure-Python loops (math.exp, running sums), used only to
              cross-check `reference` on tiny inputs
 
@@ -30,9 +30,10 @@ from .reference import (NEAR_TIE, decode_logits, softmax, residual_weights, inve
                         verify_sample_request, verify_greedy_request, predict_request,
                         verify_sample, verify_greedy, predict_outcomes, outcome_hit,
                         fanout_offsets, predict_fanout_request, predict_fanout, outcome_slot,
-                        fanout_budget)
+                        fanout_budget, kv_rewind)
 
 __all__ = ["NEAR_TIE", "decode_logits", "softmax", "residual_weights", "inverse_cdf",
            "verify_sample_request", "verify_greedy_request", "predict_request", "verify_sample",
            "verify_greedy", "predict_outcomes", "outcome_hit", "fanout_offsets",
-           "predict_fanout_request", "predict_fanout", "outcome_slot", "fanout_budget"]
+           "predict_fanout_request", "predict_fanout", "outcome_slot", "fanout_budget",
+           "kv_rewind"]

@@ -165,3 +165,18 @@ def naive_outcome_slot(keys, fanout, K, m, y, all_accept=True):
     if m == K and all_accept:
         return start
     return -1
+
+
+def naive_kv_rewind(block_tables, block_size, kv_alloc, kv_new):
+    """Block by block: a block is released when it held an entry before (its first position is
+    below kv_alloc) and holds no kept entry now (its first position is at or past kv_new)."""
+    tables = [list(row) for row in block_tables]
+    freed, offsets = [], [0]
+    for b, row in enumerate(tables):
+        for j in range(len(row)):
+            first = j * block_size
+            if first < kv_alloc[b] and first >= max(kv_new[b], 0):
+                freed.append(row[j])
+                row[j] = -1
+        offsets.append(len(freed))
+    return tables, freed, offsets

@@ -257,6 +257,34 @@ def fanout_budget(fanout, block: int) -> int:
 
 
 # ----------------------------------------------------------------------------------------------
+# KV-cache rewind on a paged cache
+def kv_rewind(block_tables, block_size: int, kv_alloc, kv_new):
+    """Rewinds a paged KV cache after verification ([SD] section "speculative decodingとKV cache、
+    プロンプトキャッシュの関係は?": both models append the drafts' keys and values to their caches;
+    when the target rejects the drafts after position m, the engine truncates both caches, dropping
+    the rejected entries, before the next round).
+
+    Request b's entries [0, L) live in the blocks block_tables[b][0 .. ceil(L / block_size)).
+    With L = kv_alloc[b] entries held and L' = kv_new[b] kept, the whole blocks at positions
+    [ceil(L' / block_size), ceil(L / block_size)) hold nothing kept: they are released (their table
+    entries become -1). Nothing is released when L' >= L. Returns (tables, freed, offsets):
+    freed lists the released block ids request by request, each request's in table order;
+    offsets[b] is where request b's ids start and offsets[B] is their total.
+    """
+    tables = np.array(block_tables, dtype=np.int64, copy=True)
+    B, max_blocks = tables.shape
+    freed, offsets = [], [0]
+    for b in range(B):
+        held = min(max_blocks, -(-int(kv_alloc[b]) // block_size))
+        kept = min(max_blocks, -(-max(int(kv_new[b]), 0) // block_size))
+        for j in range(kept, held):
+            freed.append(int(tables[b, j]))
+            tables[b, j] = -1
+        offsets.append(len(freed))
+    return tables, np.array(freed, dtype=np.int64), np.array(offsets, dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------------------------
 # batches
 def _request_slices(n: int, requests):
     return range(n) if requests is None else requests
