@@ -422,6 +422,27 @@ def secondary(sv, torch, dev, hip, sets, dsets, ws, args):
         torch.cuda.synchronize()
         res.setdefault("sample_keys_c5", {})[f"{name}_ms_per_call"] = round(
             start.elapsed_time(stop) / steps, 5)
+    # paged KV-cache rewind of both caches after a C3 round (block size 16)
+    log("KV-cache rewind")
+    bs = 16
+    mb = (4096 + K + 1) // bs + 1
+    tab0 = torch.arange(B * mb, dtype=torch.int32, device=dev).reshape(B, mb)
+    tab = tab0.clone()
+    alloc = (dsets[0]["kv"] + K + 1).to(torch.int32)
+    kvo = torch.empty(B, dtype=torch.int32, device=dev)
+    kvo.copy_(dsets[0]["kv"] + 2)
+    rw = dict(freed=torch.empty(B * mb, dtype=torch.int32, device=dev),
+              offsets=torch.empty(B + 1, dtype=torch.int32, device=dev))
+    for i in range(10):
+        sv.spec_kv_rewind(tab, bs, alloc, kvo, out=rw)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        sv.spec_kv_rewind(tab, bs, alloc, kvo, out=rw)
+    stop.record()
+    torch.cuda.synchronize()
+    res["kv_rewind_c3"] = dict(block_size=bs, ms_per_call=round(start.elapsed_time(stop) / steps, 5))
+
     vb = B * (2 * K + 1) * V * 2
     r5 = res["sample_keys_c5"]
     r5.update(F=F, draft_token_skipped=True, bytes_per_call=vb,

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 4
+#define SPEC_ABI_VERSION 5
 #define SPEC_MAX_K 64
 #define SPEC_MAX_F 16
 #define SPEC_MAX_V 4194304 /* 2^22 */
@@ -219,6 +219,25 @@ int spec_predict_fanout(const void* draft_logits, int dtype, const int32_t* draf
 int spec_outcome_lookup(const int32_t* tau, const int32_t* tokens, const int32_t* keys, int B,
                         int K, int P, const int32_t* fanout, int all_accept, int32_t* out_slot,
                         hipStream_t stream);
+
+/* Paged KV-cache rewind after a verification round ([SD] section "speculative decodingとKV cache、
+ * プロンプトキャッシュの関係は?": both models' caches are truncated past the kept entries).
+ * Call once per cache (target and draft caches have their own tables and lengths).
+ *   block_tables [B, max_blocks] int32 (device, read and written): request b's entries [0, L)
+ *                live in blocks block_tables[b][0 .. ceil(L / block_size)).
+ *   kv_alloc [B] int32 (device): entries the cache holds now (e.g. kv_len_in + K + 1);
+ *   kv_new   [B] int32 (device): entries to keep (e.g. out_kv_len of a verify call; an engine
+ *                whose cache lacks the placed token's entry passes one less).
+ * The whole blocks [ceil(kv_new / block_size), ceil(kv_alloc / block_size)) (clamped to
+ * max_blocks; none when kv_new >= kv_alloc; negative lengths count as 0) are released: their
+ * table entries become -1 and their ids are written to out_freed [B * max_blocks] int32 request
+ * by request, each request's in table order, from out_offsets[b]; out_offsets [B+1] int32,
+ * out_offsets[B] = total released. Deterministic. One workgroup; no workspace.
+ * Errors: SPEC_ERR_ARG for null pointers, B < 1, max_blocks < 1, block_size < 1 or
+ * B * max_blocks >= 2^31; SPEC_ERR_HIP for a failed launch. */
+int spec_kv_rewind(int32_t* block_tables, int B, int max_blocks, int block_size,
+                   const int32_t* kv_alloc, const int32_t* kv_new, int32_t* out_freed,
+                   int32_t* out_offsets, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ STATUS = {0: "SPEC_OK", -1: "SPEC_ERR_ARG", -2: "SPEC_ERR_DTYPE", -3: "SPEC_ERR_
 EXPORTS = ("spec_abi_version", "spec_status_string", "spec_workspace_bytes",
            "spec_workspace_init", "spec_verify_sample", "spec_verify_sample_ex",
            "spec_verify_sample_keys", "spec_verify_greedy", "spec_predict_outcomes",
-           "spec_predict_fanout", "spec_outcome_lookup")
+           "spec_predict_fanout", "spec_outcome_lookup", "spec_kv_rewind")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGNATURES = {
@@ -43,6 +43,7 @@ _SIGNATURES = {
     "spec_predict_fanout": (_i, [_vp, _i, _vp, _i, _i, _i, _i, _vp, _f, _vp, _vp, _vp, _sz,
                                  _vp]),
     "spec_outcome_lookup": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp]),
+    "spec_kv_rewind": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
 }
 
 
@@ -300,4 +301,23 @@ def spec_outcome_lookup(tau, tokens, keys, fanout, all_accept=True, out=None):
     rc = load_library().spec_outcome_lookup(_ptr(tau), _ptr(tokens), _ptr(keys), B, K, P, fan,
                                             1 if all_accept else 0, _ptr(out), _stream(dev))
     _check("spec_outcome_lookup", rc)
+    return out
+
+
+def spec_kv_rewind(block_tables, block_size, kv_alloc, kv_new, out=None):
+    """Paged KV-cache rewind (block_tables is updated in place). Returns dict(freed [B*max_blocks]
+    int32, offsets [B+1] int32); the released ids are freed[:offsets[-1]]."""
+    torch = _torch()
+    B, max_blocks = block_tables.shape
+    dev = block_tables.device
+    _need(block_tables, "block_tables", (B, max_blocks), torch.int32, dev)
+    _need(kv_alloc, "kv_alloc", (B,), torch.int32, dev)
+    _need(kv_new, "kv_new", (B,), torch.int32, dev)
+    if out is None:
+        out = dict(freed=torch.empty(B * max_blocks, dtype=torch.int32, device=dev),
+                   offsets=torch.empty(B + 1, dtype=torch.int32, device=dev))
+    rc = load_library().spec_kv_rewind(_ptr(block_tables), B, max_blocks, int(block_size),
+                                       _ptr(kv_alloc), _ptr(kv_new), _ptr(out["freed"]),
+                                       _ptr(out["offsets"]), _stream(dev))
+    _check("spec_kv_rewind", rc)
     return out

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["api.hip", "verify_sample.hip", "verify_greedy.hip", "predict.hip"]
+SOURCES = ["api.hip", "verify_sample.hip", "verify_greedy.hip", "predict.hip", "kv_cache.hip"]
 ARCH = os.environ.get("SPEC_VERIFY_ARCH", "gfx950")
 
 

@@ -216,6 +216,18 @@ def test_outcome_lookup_validation(lib):
     assert lib.spec_outcome_lookup(*a) == code["SPEC_ERR_ARG"]
 
 
+def test_kv_rewind_validation(lib):
+    code = {v: k for k, v in sv.STATUS.items()}
+    args = [FAKE, 2, 8, 16, FAKE, FAKE, FAKE, FAKE, NULL]
+    for i, bad in [(0, NULL), (4, NULL), (5, NULL), (6, NULL), (7, NULL), (1, 0), (2, 0), (3, 0),
+                   (1, 1 << 20), (3, -4)]:
+        a = list(args)
+        a[i] = bad
+        if i == 1 and bad == 1 << 20:
+            a[2] = 1 << 12          # B * max_blocks >= 2^31
+        assert lib.spec_kv_rewind(*a) == code["SPEC_ERR_ARG"], (i, bad)
+
+
 def test_workspace_init_rejects_bad_pointer(lib):
     code = {v: k for k, v in sv.STATUS.items()}
     assert lib.spec_workspace_init(NULL, 4096, NULL) == code["SPEC_ERR_WORKSPACE"]

@@ -364,3 +364,44 @@ def test_sample_keys_full_size(cid, rnd):
     idx = None if cid != 4 else sorted(set(range(0, 8)) | set(range(100, 108)))
     n, f, fb = compare_sample_keys(wl, g, 3, True, requests=idx)
     announce(f"C{cid} sample+keys: {n} checked, {f} flagged, {fb} differ")
+
+
+@pytest.mark.parametrize("B,max_blocks,bs", [(1, 4, 16), (7, 9, 4), (300, 6, 16), (1000, 40, 1)])
+def test_kv_rewind_random(B, max_blocks, bs):
+    """Paged-cache rewind on random tables and lengths (more than one 256-request tile, lengths
+    below, at and above what is held, negative lengths): tables, released ids and offsets
+    identical to the oracle's."""
+    rng = np.random.default_rng(B * 31 + bs)
+    tables = rng.permutation(B * max_blocks).reshape(B, max_blocks).astype(np.int32)
+    alloc = rng.integers(-bs, max_blocks * bs + bs, size=B).astype(np.int32)
+    new = (alloc - rng.integers(-bs, 3 * bs, size=B)).astype(np.int32)
+    announce(f"kv rewind B={B} max_blocks={max_blocks} bs={bs}")
+    dt = torch.from_numpy(tables.copy()).cuda()
+    out = sv.spec_kv_rewind(dt, bs, torch.from_numpy(alloc).cuda(), torch.from_numpy(new).cuda())
+    torch.cuda.synchronize()
+    rt, rf, ro = oracle.kv_rewind(tables, bs, alloc, new)
+    assert np.array_equal(dt.cpu().numpy(), rt)
+    off = out["offsets"].cpu().numpy()
+    assert np.array_equal(off, ro)
+    assert np.array_equal(out["freed"].cpu().numpy()[:off[-1]], rf)
+
+
+def test_kv_rewind_after_c3_round():
+    """The rewind a C3 round drives: every request held kv_in + K + 1 entries of both caches
+    (block size 16); the oracle's verification outcome (kv_out = kv_in + tau) says how many stay."""
+    wl = make_workload(3, 7)
+    ref = oracle.verify_sample(wl.target, wl.draft, wl.dtype, wl.tokens, wl.uniforms, wl.kv_len,
+                               wl.T)
+    bs, mb = 16, (4096 + wl.K + 1) // 16 + 1
+    alloc = (wl.kv_len + wl.K + 1).astype(np.int32)
+    new = ref["kv_out"].astype(np.int32)
+    tables = np.arange(wl.B * mb, dtype=np.int32).reshape(wl.B, mb)
+    announce("kv rewind after a C3 round")
+    dt = torch.from_numpy(tables.copy()).cuda()
+    out = sv.spec_kv_rewind(dt, bs, torch.from_numpy(alloc).cuda(), torch.from_numpy(new).cuda())
+    torch.cuda.synchronize()
+    rt, rf, ro = oracle.kv_rewind(tables, bs, alloc, new)
+    assert np.array_equal(dt.cpu().numpy(), rt)
+    off = out["offsets"].cpu().numpy()
+    assert np.array_equal(off, ro) and np.array_equal(out["freed"].cpu().numpy()[:off[-1]], rf)
+    announce(f"C3 round: {off[-1]} blocks released over {wl.B} requests")
