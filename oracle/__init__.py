@@ -30,10 +30,11 @@ from .reference import (NEAR_TIE, decode_logits, softmax, residual_weights, inve
                         verify_sample_request, verify_greedy_request, predict_request,
                         verify_sample, verify_greedy, predict_outcomes, outcome_hit,
                         fanout_offsets, predict_fanout_request, predict_fanout, outcome_slot,
-                        fanout_budget, kv_rewind)
+                        fanout_budget, kv_rewind, temperature_is_valid, verify_mixed_request,
+                        verify_mixed)
 
 __all__ = ["NEAR_TIE", "decode_logits", "softmax", "residual_weights", "inverse_cdf",
            "verify_sample_request", "verify_greedy_request", "predict_request", "verify_sample",
            "verify_greedy", "predict_outcomes", "outcome_hit", "fanout_offsets",
            "predict_fanout_request", "predict_fanout", "outcome_slot", "fanout_budget",
-           "kv_rewind"]
+           "kv_rewind", "temperature_is_valid", "verify_mixed_request", "verify_mixed"]

@@ -158,6 +158,41 @@ def verify_greedy_request(t_rows: np.ndarray, x, kv_in: int):
     return out
 
 
+def temperature_is_valid(T: float) -> bool:
+    """A per-request temperature the mixed rule accepts: 0 (greedy), or positive and finite with
+    log2(e)/T finite once rounded to float32 (the factor the device uses)."""
+    T = float(T)
+    if T == 0.0:
+        return True
+    if not (T > 0.0 and np.isfinite(T)):
+        return False
+    with np.errstate(over="ignore"):
+        return bool(np.isfinite(np.float32(1.4426950408889634074 / np.float64(T))))
+
+
+def verify_mixed_request(t_rows: np.ndarray, d_rows: np.ndarray, x, u, kv_in: int, T: float):
+    """Verification at a request's own temperature ([SD] stage 3: temperature zero keeps a draft
+    while it equals the target's top choice; a positive temperature keeps it by the probability
+    ratio). T = 0: the greedy rule, with p_k(x_k) reported as 1 for the target's top choice and 0
+    otherwise and q_k(x_k) as 1 (the temperature-zero limits); T > 0: speculative sampling at T;
+    an invalid T (temperature_is_valid) is a row error."""
+    K = len(x)
+    if float(T) == 0.0:
+        r = verify_greedy_request(t_rows, x, kv_in)
+        if r["row_error"]:
+            p_x = q_x = np.full(K, np.nan)
+        else:
+            p_x = np.array([1.0 if int(x[k]) == r["g"][k] else 0.0 for k in range(K)])
+            q_x = np.ones(K)
+        r.update(p_x=p_x, q_x=q_x, margin=np.inf, flagged=False, resid_mass=np.nan)
+        return r
+    if not temperature_is_valid(T):
+        return dict(tokens=np.full(K + 1, -1, np.int64), tau=-1, kv_out=int(kv_in),
+                    p_x=np.full(K, np.nan), q_x=np.full(K, np.nan), m=-1, y=-1,
+                    resid_mass=np.nan, margin=np.inf, flagged=False, row_error=True)
+    return verify_sample_request(t_rows, d_rows, x, u, kv_in, float(T))
+
+
 def predict_request(d_rows: np.ndarray, F: int, T: float):
     """Outcome keys of one request ([SSD] section "1. Outcome Prediction": the token placed at a
     rejection is predicted from the draft's top logits).
@@ -297,6 +332,17 @@ def verify_sample(target, draft, dtype, tokens, uniforms, kv_len, T, requests=No
     res = [verify_sample_request(decode_logits(target[b], dtype), decode_logits(draft[b], dtype),
                                  tokens[b], np.asarray(uniforms[b], np.float64),
                                  int(kv_len[b]), float(np.float32(T)))
+           for b in idx]
+    return _stack(res, idx, K, sample=True)
+
+
+def verify_mixed(target, draft, dtype, tokens, uniforms, kv_len, temps, requests=None):
+    """Batch wrapper of verify_mixed_request; temps are the float32 values the device gets."""
+    idx = list(_request_slices(target.shape[0], requests))
+    K = tokens.shape[1]
+    res = [verify_mixed_request(decode_logits(target[b], dtype), decode_logits(draft[b], dtype),
+                                tokens[b], np.asarray(uniforms[b], np.float64), int(kv_len[b]),
+                                float(np.float32(temps[b])))
            for b in idx]
     return _stack(res, idx, K, sample=True)
 
