@@ -422,6 +422,32 @@ def secondary(sv, torch, dev, hip, sets, dsets, ws, args):
         torch.cuda.synchronize()
         res.setdefault("sample_keys_c5", {})[f"{name}_ms_per_call"] = round(
             start.elapsed_time(stop) / steps, 5)
+    # C3 as a mixed batch: half the requests at T = 0 (their draft rows are not read)
+    log("C3 mixed batch, half greedy")
+    temps = torch.tensor([0.0 if b % 2 == 0 else float(wl0.T) for b in range(B)],
+                         dtype=torch.float32, device=dev)
+    outm = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                tau=torch.empty(B, dtype=torch.int32, device=dev),
+                kv_len=torch.empty(B, dtype=torch.int32, device=dev),
+                p=torch.empty((B, K), dtype=torch.float32, device=dev),
+                q=torch.empty((B, K), dtype=torch.float32, device=dev))
+    for i in range(10):
+        s = dsets[i % len(dsets)]
+        sv.spec_verify_mixed(s["t"], s["d"], s["x"], s["u"], s["kv"], temps, ws, out=outm)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        s = dsets[i % len(dsets)]
+        sv.spec_verify_mixed(s["t"], s["d"], s["x"], s["u"], s["kv"], temps, ws, out=outm)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    mb_bytes = (B // 2) * (2 * K + 1) * V * 2 + (B - B // 2) * (K + 1) * V * 2
+    res["mixed_c3_half_greedy"] = dict(ms_per_call=round(ms, 5),
+                                       rows_per_s=round(B * K / (ms * 1e-3), 1),
+                                       bytes_per_call=mb_bytes,
+                                       hbm_gbps=round(mb_bytes / (ms * 1e-3) / 1e9, 1))
+
     # paged KV-cache rewind of both caches after a C3 round (block size 16)
     log("KV-cache rewind")
     bs = 16

@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 5
+#define SPEC_ABI_VERSION 6
 #define SPEC_MAX_K 64
 #define SPEC_MAX_F 16
 #define SPEC_MAX_V 4194304 /* 2^22 */
@@ -161,6 +161,23 @@ int spec_verify_sample_keys(const void* target_logits, const void* draft_logits,
                             int32_t* out_kv_len, float* out_p, float* out_q, int32_t* out_keys,
                             float* out_key_prob, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+/* Verification of a mixed batch: request b at its own temperature temperatures[b] ([SD] stage 3:
+ * temperature zero is the argmax rule, a positive temperature the probability-ratio rule).
+ *   temperatures [B] float (device): T_b = 0 verifies request b greedily (as spec_verify_greedy:
+ *                its draft rows are not read); T_b > 0 by speculative sampling at T_b (as
+ *                spec_verify_sample with temperature T_b: same outputs, bit for bit); a T_b that is
+ *                negative, not finite, or so small that log2(e)/T_b is not finite is a row error
+ *                for request b (the host cannot check device data).
+ * Other arguments and outputs as for spec_verify_sample. For a T_b = 0 request out_p[b,k] is 1
+ * when x_k is the target's top choice and 0 otherwise, and out_q[b,k] is 1 (a temperature-zero
+ * draft puts all its probability on its token). Errors as for spec_verify_sample, without the
+ * host-side temperature check; SPEC_ERR_ARG also for a null temperatures. */
+int spec_verify_mixed(const void* target_logits, const void* draft_logits, int dtype,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      const int32_t* kv_len_in, const float* temperatures, int B, int K, int V,
+                      int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len, float* out_p,
+                      float* out_q, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Greedy verification, temperature must be exactly 0 ([SD] stage 3 at temperature zero;
  * [D3D] 検証のしくみ③, 検証のまとめ). g_k = argmax_v target_logits[b,k,v] (lowest v on ties);

@@ -8,11 +8,12 @@ from ._binding import (EXPORTS, LIB_PATH, SPEC_BF16, SPEC_DEFAULT_WAIT_POLLS, SP
                        SPEC_MAX_F, SPEC_MAX_K, SPEC_MAX_V, STATUS, SpecVerifyError, hip_runtime,
                        load_library, new_workspace, spec_kv_rewind, spec_outcome_lookup,
                        spec_predict_fanout, spec_predict_outcomes, spec_verify_greedy,
-                       spec_verify_sample, spec_verify_sample_keys, status_string,
-                       workspace_bytes)
+                       spec_verify_mixed, spec_verify_sample, spec_verify_sample_keys,
+                       status_string, workspace_bytes)
 
 __all__ = ["EXPORTS", "LIB_PATH", "SPEC_BF16", "SPEC_DEFAULT_WAIT_POLLS", "SPEC_F32",
            "SPEC_MAX_F", "SPEC_MAX_K", "SPEC_MAX_V", "STATUS", "SpecVerifyError", "hip_runtime",
            "load_library", "new_workspace", "spec_kv_rewind", "spec_outcome_lookup",
            "spec_predict_fanout", "spec_predict_outcomes", "spec_verify_greedy",
-           "spec_verify_sample", "spec_verify_sample_keys", "status_string", "workspace_bytes"]
+           "spec_verify_mixed", "spec_verify_sample", "spec_verify_sample_keys", "status_string",
+           "workspace_bytes"]

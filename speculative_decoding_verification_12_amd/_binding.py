@@ -22,7 +22,8 @@ STATUS = {0: "SPEC_OK", -1: "SPEC_ERR_ARG", -2: "SPEC_ERR_DTYPE", -3: "SPEC_ERR_
 
 EXPORTS = ("spec_abi_version", "spec_status_string", "spec_workspace_bytes",
            "spec_workspace_init", "spec_verify_sample", "spec_verify_sample_ex",
-           "spec_verify_sample_keys", "spec_verify_greedy", "spec_predict_outcomes",
+           "spec_verify_sample_keys", "spec_verify_mixed", "spec_verify_greedy",
+           "spec_predict_outcomes",
            "spec_predict_fanout", "spec_outcome_lookup", "spec_kv_rewind")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -37,6 +38,8 @@ _SIGNATURES = {
                                    _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _i]),
     "spec_verify_sample_keys": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _f, _i, _i,
                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_mixed": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i,
+                               _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_greedy": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _f,
                                 _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_predict_outcomes": (_i, [_vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
@@ -219,6 +222,36 @@ def spec_verify_sample_keys(target, draft, draft_tokens, uniforms, kv_len, tempe
         _ptr(out.get("q")), _ptr(out["keys"]), _ptr(out.get("key_prob")), _ptr(workspace),
         workspace.numel(), _stream(dev))
     _check("spec_verify_sample_keys", rc)
+    return out
+
+
+def spec_verify_mixed(target, draft, draft_tokens, uniforms, kv_len, temperatures, workspace,
+                      out=None):
+    """Verification with a per-request temperature (float32 [B] on the device; 0 = greedy).
+    Returns dict(tokens, tau, kv_len, p, q)."""
+    torch = _torch()
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    _need(target, "target_logits", (B, K + 1, V), target.dtype, dev)
+    _need(draft, "draft_logits", (B, K, V), target.dtype, dev)
+    _need(draft_tokens, "draft_tokens", (B, K), torch.int32, dev)
+    _need(uniforms, "uniforms", (B, K + 1), torch.float32, dev)
+    _need(temperatures, "temperatures", (B,), torch.float32, dev)
+    if kv_len is not None:
+        _need(kv_len, "kv_len", (B,), torch.int32, dev)
+    if out is None:
+        out = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                   tau=torch.empty(B, dtype=torch.int32, device=dev),
+                   kv_len=torch.empty(B, dtype=torch.int32, device=dev),
+                   p=torch.empty((B, K), dtype=torch.float32, device=dev),
+                   q=torch.empty((B, K), dtype=torch.float32, device=dev))
+    rc = load_library().spec_verify_mixed(
+        _ptr(target), _ptr(draft), _dtype_code(target), _ptr(draft_tokens), _ptr(uniforms),
+        _ptr(kv_len), _ptr(temperatures), B, K, V, _ptr(out["tokens"]), _ptr(out["tau"]),
+        _ptr(out.get("kv_len")), _ptr(out.get("p")), _ptr(out.get("q")), _ptr(workspace),
+        workspace.numel(), _stream(dev))
+    _check("spec_verify_mixed", rc)
     return out
 
 

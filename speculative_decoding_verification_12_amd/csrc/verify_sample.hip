@@ -121,12 +121,77 @@ __device__ __forceinline__ const TIn* slot_row(const TIn* tgt, const TIn* drf, i
                 : drf + (static_cast<size_t>(b) * K + (r - K - 1)) * static_cast<size_t>(V);
 }
 
-template <typename TIn, bool kKeys>
+// log2(e) / T on the device, the same rounded value the host computes for a call's T
+__device__ __forceinline__ float exp2_scale_dev(float T) {
+  return static_cast<float>(1.4426950408889634074 / static_cast<double>(T));
+}
+
+// A thread's first maximum over chunk `cr` (elements visited in increasing token order), as
+// (value, lowest id), then the workgroup's in thread 0.
+template <typename TIn>
+__device__ __forceinline__ void chunk_argmax(const TIn* row, const RowSpan& sp,
+                                             const ChunkRange& cr, int V, float* s_v, int* s_i,
+                                             float& M, int& I) {
+  using E = Elem<TIn>;
+  constexpr int N = E::N;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  if (cr.first && tid < sp.head) {
+    bv = E::one(row, tid);
+    bi = tid;
+  }
+  const uint4* vrow = reinterpret_cast<const uint4*>(row + sp.head);
+  for (int base = cr.vbeg; base < cr.vend; base += kPassVecs) {
+    uint4 q[kVecPerThread];
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+      const int vi = base + i * kBlock + tid;
+      q[i] = vi < cr.vend ? vrow[vi] : neg_inf_vec<TIn>();
+    }
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+      float t[N];
+      E::unpack(q[i], t);
+      const int tok0 = sp.head + (base + i * kBlock + tid) * N;
+#pragma unroll
+      for (int j = 0; j < N; ++j)
+        if (t[j] > bv || (t[j] == bv && tok0 + j < bi)) {
+          bv = t[j];
+          bi = tok0 + j;
+        }
+    }
+  }
+  if (cr.last && tid < V - sp.tail) {
+    const float v = E::one(row, sp.tail + tid);
+    if (v > bv || (v == bv && sp.tail + tid < bi)) {
+      bv = v;
+      bi = sp.tail + tid;
+    }
+  }
+  wave_argmax(bv, bi);
+  if (lane == 0) {
+    s_v[w] = bv;
+    s_i[w] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    M = s_v[0];
+    I = s_i[0];
+    for (int k = 1; k < kWaves; ++k)
+      if (better(s_v[k], s_i[k], M, I)) {
+        M = s_v[k];
+        I = s_i[k];
+      }
+  }
+}
+
+template <typename TIn, bool kKeys, bool kMixed>
 __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
     const TIn* __restrict__ tgt, const TIn* __restrict__ drf, const int32_t* __restrict__ xtok,
-    int K, int V, float c, int nchunk, int cv, float2* __restrict__ part,
+    int K, int V, float c_call, int nchunk, int cv, float2* __restrict__ part,
     float* __restrict__ gath, uint64_t* __restrict__ clear, int nclear,
-    float* __restrict__ key_wave_max) {
+    float* __restrict__ key_wave_max, const float* __restrict__ temps) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
   __shared__ float sm[kWaves], ss[kWaves];
@@ -141,9 +206,33 @@ __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
   const int r = rb % rows;
   const int b = rb / rows;
 
+  // per-request temperature (mixed batches): T_b = 0 is the greedy rule, which reads no draft
+  // row and keeps each target chunk's (max, lowest id); an invalid T_b (a row error in the
+  // draw) is treated the same way here
+  float c = c_call;
+  bool greedy = false;
+  if constexpr (kMixed) {
+    const float Tb = temps[b];
+    greedy = !(Tb > 0.f);
+    c = greedy ? 0.f : exp2_scale_dev(Tb);
+    if (greedy && r > K) return;
+  }
+
   const TIn* row = slot_row(tgt, drf, b, r, K, V);
   const RowSpan sp = row_span(row, V);
   const ChunkRange cr = chunk_range(sp, ch, nchunk, cv);
+
+  if constexpr (kMixed) {
+    if (greedy) {
+      __shared__ int si[kWaves];
+      float M;
+      int I;
+      chunk_argmax(row, sp, cr, V, sm, si, M, I);
+      if (threadIdx.x == 0)
+        part[static_cast<size_t>(rb) * nchunk + ch] = make_float2(M, __int_as_float(I));
+      return;
+    }
+  }
 
   // The workgroup whose chunk holds the slot's draft token also reads that token's logit, so
   // the merge finds it without another dependent load. Rows 0..K-1 are target slots, K+1..2K
@@ -348,26 +437,6 @@ __device__ __forceinline__ bool after_in_order(float v, int i, float pv, int pi)
 __device__ __forceinline__ int lanes_below(unsigned long long bal) {
   return static_cast<int>(__builtin_amdgcn_mbcnt_hi(
       static_cast<uint32_t>(bal >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u)));
-}
-
-// The wave's F-th largest lane maximum, ties counted (-inf when fewer than F lanes hold
-// elements).
-__device__ __forceinline__ float wave_fth_max(float lane_max, bool has, int F) {
-  float theta = -INFINITY, cur = has ? lane_max : -INFINITY;
-  bool in = has;
-  int need = F;
-  while (need > 0) {   // uniform: every quantity below is wave-wide
-    if (__ballot(in) == 0ull) {
-      theta = -INFINITY;
-      break;
-    }
-    const float mx = wave_max(in ? cur : -INFINITY);
-    const bool at = in && cur == mx;
-    need -= __popcll(__ballot(at));
-    theta = mx;
-    if (at) in = false;
-  }
-  return theta;
 }
 
 // Replaces the running best (lanes 0..Fp-1 hold picks in order) by the best Fp of itself and
@@ -622,14 +691,15 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void keys_merge_kernel(const T
 
 // Chunks of kBlock * kDrawVecs vectors (see draw_plan). cm holds the published (R, P) of every
 // chunk, [b][ch][2] words, zeroed by the statistics kernel of the same call.
-template <typename TIn, bool kKeys>
+template <typename TIn, bool kKeys, bool kMixed>
 __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     const TIn* __restrict__ tgt, const TIn* __restrict__ drf, const int32_t* __restrict__ xtok,
-    const float* __restrict__ uni, const int32_t* __restrict__ kv_in, int K, int V, float c,
+    const float* __restrict__ uni, const int32_t* __restrict__ kv_in, int K, int V, float c_call,
     int nchunk_s, const float2* __restrict__ part_s, const float* __restrict__ gath,
     int nchunk, int cv, uint64_t* __restrict__ cm, int wait_polls,
     int32_t* __restrict__ out_tok, int32_t* __restrict__ out_tau, int32_t* __restrict__ out_kv,
-    float* __restrict__ out_p, float* __restrict__ out_q, KeyArgs ka) {
+    float* __restrict__ out_p, float* __restrict__ out_q, KeyArgs ka,
+    const float* __restrict__ temps) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
   __shared__ double s_red[2][kWaves];
@@ -646,6 +716,61 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
   const int ch = blockIdx.x % nchunk;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int rows = 2 * K + 1;
+
+  float c = c_call;
+  if constexpr (kMixed) {
+    // ---- per-request temperature: T_b = 0 takes the greedy rule on the (max, lowest id) chunk
+    // partials of the target rows; a T_b that is negative, not finite, or too small for log2(e)/T
+    // to be finite is a row error
+    __shared__ int row_g[SPEC_MAX_K + 1];
+    const float Tb = temps[b];
+    const bool greedy = Tb == 0.f;
+    const float cc = Tb > 0.f ? exp2_scale_dev(Tb) : 0.f;
+    const bool t_ok = greedy || (Tb > 0.f && isfinite(Tb) && isfinite(cc));
+    c = cc;
+    if (greedy || !t_ok) {
+      if (ch != 0) return;   // one workgroup of the request does all of it
+      if (t_ok)
+        for (int rr = w; rr <= K; rr += kWaves) {
+          const float2* pr = part_s + (static_cast<size_t>(b) * rows + rr) * nchunk_s;
+          float v = -INFINITY;
+          int i = 0x7fffffff;
+          for (int j = lane; j < nchunk_s; j += kWave) {
+            const float2 q = pr[j];
+            if (better(q.x, __float_as_int(q.y), v, i)) {
+              v = q.x;
+              i = __float_as_int(q.y);
+            }
+          }
+          wave_argmax(v, i);
+          // a row whose logits are all -inf keeps no index: its first token is the lowest id
+          if (lane == 0) row_g[rr] = i == 0x7fffffff ? 0 : i;
+        }
+      __syncthreads();
+      if (w != 0) return;
+      const bool valid = lane < K;
+      const int xk = valid ? xtok[static_cast<size_t>(b) * K + lane] : 0;
+      const bool err = __ballot(!t_ok || (valid && (xk < 0 || xk >= V))) != 0ull;
+      const unsigned long long miss = __ballot(!err && valid && xk != row_g[valid ? lane : 0]);
+      const int mm = miss ? __ffsll(static_cast<long long>(miss)) - 1 : K;
+      if (valid) {   // at temperature zero p_k(x_k) is 1 for the target's top choice, else 0
+        const size_t o = static_cast<size_t>(b) * K + lane;
+        if (out_p) out_p[o] = err ? NAN : (xk == row_g[lane] ? 1.f : 0.f);
+        if (out_q) out_q[o] = err ? NAN : 1.f;
+      }
+      for (int j = lane; j <= K; j += kWave) {
+        int tok = -1;
+        if (!err) tok = j < mm ? xk : (j == mm ? row_g[mm] : -1);
+        out_tok[static_cast<size_t>(b) * (K + 1) + j] = tok;
+      }
+      if (lane == 0) {
+        const int kv0 = kv_in ? kv_in[b] : 0;
+        out_tau[b] = err ? -1 : mm + 1;
+        if (out_kv) out_kv[b] = err ? kv0 : kv0 + mm + 1;
+      }
+      return;
+    }
+  }
 
   // ---- merge the statistics pass of request b (every workgroup of b does the same, bit for
   // bit): row (max, sum) in fp32/fp64, slot acceptance ratios, first rejection by ballot
@@ -950,12 +1075,12 @@ struct KeyRequest {
   float* out_prob;
 };
 
-template <typename TIn, bool kKeys>
+template <typename TIn, bool kKeys, bool kMixed>
 int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, const float* uni,
                     const int32_t* kv_in, int B, int K, int V, float T, int32_t* out_tok,
                     int32_t* out_tau, int32_t* out_kv, float* out_p, float* out_q, void* ws,
                     hipStream_t stream, hipEvent_t* ev, int wait_polls, const SamplePlan& P,
-                    const KeyRequest& kr) {
+                    const KeyRequest& kr, const float* temps) {
   const size_t g1 = static_cast<size_t>(B) * (2 * K + 1) * P.stats.nchunk;
   const size_t g2 = static_cast<size_t>(B) * P.draw.nchunk;
   if (!grid_fits(g1) || !grid_fits(g2) || P.draw.cv != kBlock * kDrawVecs ||
@@ -978,24 +1103,24 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
   const KeyArgs ka{pick, kr.F, kr.exclude, cs, kwmax, krows, kr.out_keys, kr.out_prob};
   const dim3 grid3(static_cast<unsigned>(static_cast<size_t>(B) * K));
   if (ev == nullptr) {
-    hipLaunchKernelGGL((sample_stats_kernel<TIn, kKeys>), grid1, block, 0, stream, t, d, xtok, K,
-                       V, c, ns, cs, part1, gath, cm, nclear, kwmax);
-    hipLaunchKernelGGL((sample_draw_kernel<TIn, kKeys>), grid2, block, 0, stream, t, d, xtok, uni,
-                       kv_in, K, V, c, ns, static_cast<const float2*>(part1),
+    hipLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed>), grid1, block, 0, stream, t, d,
+                       xtok, K, V, c, ns, cs, part1, gath, cm, nclear, kwmax, temps);
+    hipLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed>), grid2, block, 0, stream, t, d,
+                       xtok, uni, kv_in, K, V, c, ns, static_cast<const float2*>(part1),
                        static_cast<const float*>(gath), nd, cd, cm, polls, out_tok, out_tau,
-                       out_kv, out_p, out_q, ka);
+                       out_kv, out_p, out_q, ka, temps);
     if constexpr (kKeys)
       hipLaunchKernelGGL(keys_merge_kernel<TIn>, grid3, dim3(kMergeWaves * kWave), 0, stream, d,
                          xtok, K, V, c, ns, ka);
   } else {
     // profiling: the runtime records the events at each kernel's start and end
-    hipExtLaunchKernelGGL((sample_stats_kernel<TIn, kKeys>), grid1, block, 0, stream, ev[0],
-                          ev[1], 0, t, d, xtok, K, V, c, ns, cs, part1, gath, cm, nclear,
-                          kwmax);
-    hipExtLaunchKernelGGL((sample_draw_kernel<TIn, kKeys>), grid2, block, 0, stream, ev[2],
-                          ev[3], 0, t, d, xtok, uni, kv_in, K, V, c, ns,
+    hipExtLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed>), grid1, block, 0, stream,
+                          ev[0], ev[1], 0, t, d, xtok, K, V, c, ns, cs, part1, gath, cm, nclear,
+                          kwmax, temps);
+    hipExtLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed>), grid2, block, 0, stream,
+                          ev[2], ev[3], 0, t, d, xtok, uni, kv_in, K, V, c, ns,
                           static_cast<const float2*>(part1), static_cast<const float*>(gath), nd,
-                          cd, cm, polls, out_tok, out_tau, out_kv, out_p, out_q, ka);
+                          cd, cm, polls, out_tok, out_tau, out_kv, out_p, out_q, ka, temps);
     if constexpr (kKeys)
       hipLaunchKernelGGL(keys_merge_kernel<TIn>, grid3, dim3(kMergeWaves * kWave), 0, stream, d,
                          xtok, K, V, c, ns, ka);
@@ -1007,16 +1132,21 @@ template <typename TIn>
 int launch_sample(const void* target, const void* draft, const int32_t* xtok, const float* uni,
                   const int32_t* kv_in, int B, int K, int V, float T, int32_t* out_tok,
                   int32_t* out_tau, int32_t* out_kv, float* out_p, float* out_q, void* ws,
-                  hipStream_t stream, hipEvent_t* ev, int wait_polls, const KeyRequest& kr) {
+                  hipStream_t stream, hipEvent_t* ev, int wait_polls, const KeyRequest& kr,
+                  const float* temps) {
   const bool keys = kr.F > 0;
   const SamplePlan P = default_sample_plan<TIn>(B, K, V, keys);
+  if (temps != nullptr)
+    return launch_sample_t<TIn, false, true>(target, draft, xtok, uni, kv_in, B, K, V, T, out_tok,
+                                             out_tau, out_kv, out_p, out_q, ws, stream, ev,
+                                             wait_polls, P, kr, temps);
   if (keys)
-    return launch_sample_t<TIn, true>(target, draft, xtok, uni, kv_in, B, K, V, T, out_tok,
-                                      out_tau, out_kv, out_p, out_q, ws, stream, ev, wait_polls,
-                                      P, kr);
-  return launch_sample_t<TIn, false>(target, draft, xtok, uni, kv_in, B, K, V, T, out_tok,
-                                     out_tau, out_kv, out_p, out_q, ws, stream, ev, wait_polls, P,
-                                     kr);
+    return launch_sample_t<TIn, true, false>(target, draft, xtok, uni, kv_in, B, K, V, T, out_tok,
+                                             out_tau, out_kv, out_p, out_q, ws, stream, ev,
+                                             wait_polls, P, kr, nullptr);
+  return launch_sample_t<TIn, false, false>(target, draft, xtok, uni, kv_in, B, K, V, T, out_tok,
+                                            out_tau, out_kv, out_p, out_q, ws, stream, ev,
+                                            wait_polls, P, kr, nullptr);
 }
 
 int verify_sample_entry(const void* target_logits, const void* draft_logits, int dtype,
@@ -1025,7 +1155,7 @@ int verify_sample_entry(const void* target_logits, const void* draft_logits, int
                         int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len, float* out_p,
                         float* out_q, void* workspace, size_t workspace_bytes,
                         hipStream_t stream, hipEvent_t* events, int wait_polls,
-                        const KeyRequest& kr) {
+                        const KeyRequest& kr, const float* temps = nullptr) {
   int rc = check_dtype(dtype);
   if (rc != SPEC_OK) return rc;
   if ((rc = check_dims(B, K, V)) != SPEC_OK) return rc;
@@ -1037,8 +1167,8 @@ int verify_sample_entry(const void* target_logits, const void* draft_logits, int
     const int pick = kr.F + (kr.exclude ? 1 : 0);
     if (kr.F < 1 || pick > SPEC_MAX_F || pick > V || kr.out_keys == nullptr) return SPEC_ERR_ARG;
   }
-  if (!std::isfinite(temperature) || !(temperature > 0.f) ||
-      !std::isfinite(exp2_scale(temperature)))
+  if (temps == nullptr && (!std::isfinite(temperature) || !(temperature > 0.f) ||
+                           !std::isfinite(exp2_scale(temperature))))
     return SPEC_ERR_TEMPERATURE;
   if ((rc = check_workspace(workspace, workspace_bytes, B, K, V, 1)) != SPEC_OK) return rc;
   if (events != nullptr)
@@ -1047,10 +1177,10 @@ int verify_sample_entry(const void* target_logits, const void* draft_logits, int
   if (dtype == SPEC_BF16)
     return launch_sample<uint16_t>(target_logits, draft_logits, draft_tokens, uniforms, kv_len_in,
                                    B, K, V, temperature, out_tokens, out_tau, out_kv_len, out_p,
-                                   out_q, workspace, stream, events, wait_polls, kr);
+                                   out_q, workspace, stream, events, wait_polls, kr, temps);
   return launch_sample<float>(target_logits, draft_logits, draft_tokens, uniforms, kv_len_in, B,
                               K, V, temperature, out_tokens, out_tau, out_kv_len, out_p, out_q,
-                              workspace, stream, events, wait_polls, kr);
+                              workspace, stream, events, wait_polls, kr, temps);
 }
 
 }  // namespace
@@ -1095,4 +1225,17 @@ extern "C" int spec_verify_sample_keys(const void* target_logits, const void* dr
                                  out_kv_len, out_p, out_q, workspace, workspace_bytes, stream,
                                  nullptr, -1,
                                  sv::KeyRequest{F, exclude_draft ? 1 : 0, out_keys, out_key_prob});
+}
+
+extern "C" int spec_verify_mixed(const void* target_logits, const void* draft_logits, int dtype,
+                                 const int32_t* draft_tokens, const float* uniforms,
+                                 const int32_t* kv_len_in, const float* temperatures, int B,
+                                 int K, int V, int32_t* out_tokens, int32_t* out_tau,
+                                 int32_t* out_kv_len, float* out_p, float* out_q,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (temperatures == nullptr) return SPEC_ERR_ARG;
+  return sv::verify_sample_entry(target_logits, draft_logits, dtype, draft_tokens, uniforms,
+                                 kv_len_in, B, K, V, 1.f, out_tokens, out_tau, out_kv_len, out_p,
+                                 out_q, workspace, workspace_bytes, stream, nullptr, -1,
+                                 sv::KeyRequest{0, 0, nullptr, nullptr}, temperatures);
 }

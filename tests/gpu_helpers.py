@@ -227,3 +227,45 @@ def compare_sample_keys(wl, gpu, F, exclude, requests=None):
     keys = dict(keys=gpu["keys"].reshape(wl.B, -1), key_prob=gpu["key_prob"].reshape(wl.B, -1))
     compare_fanout(wl, keys, [F] * wl.K, float(wl.T), exclude, requests)
     return res
+
+
+def gpu_mixed(wl, temps, dev=None, ws=None):
+    dev = dev or upload(wl)
+    B, K = wl.B, wl.K
+    ws = ws if ws is not None else sv.new_workspace(B, K, wl.V)
+    out = dict(tokens=poisoned((B, K + 1), torch.int32), tau=poisoned((B,), torch.int32),
+               kv_len=poisoned((B,), torch.int32), p=poisoned((B, K), torch.float32),
+               q=poisoned((B, K), torch.float32))
+    sv.spec_verify_mixed(dev["target"], dev["draft"], dev["tokens"], dev["uniforms"], dev["kv"],
+                         torch.from_numpy(np.asarray(temps, np.float32)).cuda(), ws, out=out)
+    torch.cuda.synchronize()
+    return {k: _np(v) for k, v in out.items()}
+
+
+def compare_mixed(wl, gpu, temps, requests=None):
+    """Mixed-batch parity: greedy requests bit-exact with probabilities as the oracle reports
+    them; sampling requests by the sampling rules; invalid temperatures as row errors."""
+    _assert_no_poison(gpu)
+    idx = list(range(wl.B)) if requests is None else list(requests)
+    ref = oracle.verify_mixed(wl.target, wl.draft, wl.dtype, wl.tokens, wl.uniforms, wl.kv_len,
+                              temps, requests=idx)
+    K, V = wl.K, wl.V
+    n_flag = 0
+    for i, b in enumerate(idx):
+        tok, tau, kv = gpu["tokens"][b], int(gpu["tau"][b]), int(gpu["kv_len"][b])
+        where = f"request {b} (T={temps[b]}, {wl.config.name}, K={K} V={V})"
+        if ref["row_error"][i]:
+            assert tau == -1 and kv == int(ref["kv_out"][i]) and np.all(tok == -1), where
+            assert np.all(np.isnan(gpu["p"][b])) and np.all(np.isnan(gpu["q"][b])), where
+            continue
+        np.testing.assert_allclose(gpu["p"][b], ref["p_x"][i], rtol=0, atol=PROB_ATOL,
+                                   err_msg=where)
+        np.testing.assert_allclose(gpu["q"][b], ref["q_x"][i], rtol=0, atol=PROB_ATOL,
+                                   err_msg=where)
+        if ref["flagged"][i]:
+            n_flag += 1
+            assert 1 <= tau <= K + 1 and np.array_equal(tok[:tau - 1], wl.tokens[b, :tau - 1])
+            continue
+        assert tau == int(ref["tau"][i]) and np.array_equal(tok, ref["tokens"][i]), where
+        assert kv == int(ref["kv_out"][i]), where
+    return len(idx), n_flag

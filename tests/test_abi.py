@@ -143,6 +143,22 @@ def test_sample_keys_validation(lib):
     assert call() == code["SPEC_ERR_WORKSPACE"]
 
 
+def test_mixed_validation(lib):
+    code = {v: k for k, v in sv.STATUS.items()}
+
+    def call(temps=FAKE, **kw):
+        a = dict(t=FAKE, d=FAKE, dtype=1, x=FAKE, u=FAKE, kv=NULL, B=2, K=4, V=1000,
+                 tok=FAKE, tau=FAKE, kvo=NULL, p=NULL, q=NULL, ws=FAKE, wsb=0, s=NULL)
+        a.update(kw)
+        return lib.spec_verify_mixed(a["t"], a["d"], a["dtype"], a["x"], a["u"], a["kv"], temps,
+                                     a["B"], a["K"], a["V"], a["tok"], a["tau"], a["kvo"],
+                                     a["p"], a["q"], a["ws"], a["wsb"], a["s"])
+    assert call(dtype=3) == code["SPEC_ERR_DTYPE"]
+    for kw in [dict(temps=NULL), dict(B=0), dict(K=65), dict(x=NULL), dict(t=FAKE_ODD)]:
+        assert call(**kw) == code["SPEC_ERR_ARG"], kw
+    assert call() == code["SPEC_ERR_WORKSPACE"]   # temperatures are checked on the device
+
+
 def test_greedy_validation(lib):
     code = {v: k for k, v in sv.STATUS.items()}
 

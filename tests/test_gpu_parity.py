@@ -8,9 +8,9 @@ import torch
 import oracle
 import speculative_decoding_verification_12_amd as sv
 from gpu_helpers import (announce, compare_fanout, compare_greedy, compare_lookup,
-                         compare_predict, compare_sample, compare_sample_keys, dev_logits,
-                         gpu_fanout, gpu_greedy, gpu_predict, gpu_sample, gpu_sample_keys,
-                         upload)
+                         compare_mixed, compare_predict, compare_sample, compare_sample_keys,
+                         dev_logits, gpu_fanout, gpu_greedy, gpu_mixed, gpu_predict, gpu_sample,
+                         gpu_sample_keys, upload)
 from synthetic import make_tiny_random, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -405,3 +405,48 @@ def test_kv_rewind_after_c3_round():
     off = out["offsets"].cpu().numpy()
     assert np.array_equal(off, ro) and np.array_equal(out["freed"].cpu().numpy()[:off[-1]], rf)
     announce(f"C3 round: {off[-1]} blocks released over {wl.B} requests")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mixed_tiny_random(dtype):
+    """A temperature per request: zeros (greedy), several positive values and invalid ones
+    (negative, NaN, infinite, too small) in one call, on tiny rows with ties and masked tokens."""
+    rng = np.random.default_rng(33)
+    choices = [0.0, 0.0, 0.7, 1.0, 2.5, -1.0, float("nan"), float("inf"), 1e-45]
+    for seed in range(20):
+        K = 1 + seed % 6
+        V = [2, 3, 5, 8, 40, 129, 1000, 4099][seed % 8]
+        wl = make_tiny_random(seed, B=9, K=K, V=V, T=1.0, dtype=dtype, ties=seed % 2 == 0,
+                              neg_inf=0.2 if seed % 3 else 0.0,
+                              bad_token_rate=0.05 if seed % 4 == 0 else 0.0)
+        temps = [choices[(seed + b) % len(choices)] for b in range(wl.B)]
+        announce(f"mixed seed={seed} dtype={dtype} K={K} V={V}")
+        compare_mixed(wl, gpu_mixed(wl, temps), temps)
+
+
+def test_mixed_c3_half_greedy_bit_identical():
+    """C3 at full size with half the requests at T = 0: every sampling request equals
+    spec_verify_sample at its temperature and every greedy one spec_verify_greedy, bit for bit,
+    and both match the oracle."""
+    wl = make_workload(3, 3)
+    dev = upload(wl)
+    temps = np.where(np.arange(wl.B) % 2 == 0, 0.0, float(wl.T)).astype(np.float32)
+    temps[5] = 1.3
+    announce("C3 mixed, half greedy")
+    mixed = gpu_mixed(wl, temps, dev=dev)
+    n, f = compare_mixed(wl, mixed, temps)
+    announce(f"C3 mixed: {n} checked, {f} flagged")
+    plain = gpu_sample(wl, dev=dev)
+    for b in np.nonzero(temps == np.float32(wl.T))[0]:
+        for k in ("tokens", "tau", "kv_len", "p", "q"):
+            assert np.array_equal(plain[k][b].view(np.int32), mixed[k][b].view(np.int32)), (b, k)
+    ws = sv.new_workspace(wl.B, wl.K, wl.V)
+    out = dict(tokens=torch.empty((wl.B, wl.K + 1), dtype=torch.int32, device="cuda"),
+               tau=torch.empty(wl.B, dtype=torch.int32, device="cuda"),
+               kv_len=torch.empty(wl.B, dtype=torch.int32, device="cuda"))
+    sv.spec_verify_greedy(dev["target"], dev["tokens"], dev["kv"], ws, out=out)
+    torch.cuda.synchronize()
+    greedy = {k: v.cpu().numpy() for k, v in out.items()}
+    for b in np.nonzero(temps == 0)[0]:
+        for k in ("tokens", "tau", "kv_len"):
+            assert np.array_equal(greedy[k][b], mixed[k][b]), (b, k)
