@@ -8,7 +8,8 @@ generators in `synthetic/` are the only code both sides use.
 Modules
   reference  vectorised NumPy oracle in float64 (greedy, sampling, outcome prediction with a
              uniform or per-slot fan-out, hit check and prepared-continuation lookup, draft
-             budget, paged KV-cache rewind, decision margins and near-tie flags)
+             budget, paged KV-cache rewind, mixed temperatures, prompt-lookup drafting and
+             verification of drafts without a distribution, decision margins, near-tie flags)
   naive      the same rules as literal pure-Python loops (math.exp, running sums), used only to
              cross-check `reference` on tiny inputs
 
@@ -16,7 +17,9 @@ Sources (page titles and sections):
   [SD]   "speculative decodingとは" (lotook.com): section "speculative decodingはどのような手順で
          動くのか?" (the four-stage loop; stage 3 accept/reject, stage 4 residual resample and
          bonus token), section "speculative decodingとKV cache、プロンプトキャッシュの関係は?"
-         (KV-cache rewind) and the FAQ entry on output quality (losslessness).
+         (KV-cache rewind), section "別のドラフトモデルは常に必要なのか?" (n-gram and prompt
+         lookup drafting; the target checks any proposer's candidates with its own distribution)
+         and the FAQ entry on output quality (losslessness).
   [SSD]  "Speculative Speculative Decoding (SSD)" (jiwasawa.github.io): section
          "1. Outcome Prediction (The Saguaro Cache)".
   [D3D]  "LLMの生成を5倍速くする「D3D」を図で読む" (animemo.app): sections "検証のしくみ①",
@@ -31,10 +34,12 @@ from .reference import (NEAR_TIE, decode_logits, softmax, residual_weights, inve
                         verify_sample, verify_greedy, predict_outcomes, outcome_hit,
                         fanout_offsets, predict_fanout_request, predict_fanout, outcome_slot,
                         fanout_budget, kv_rewind, temperature_is_valid, verify_mixed_request,
-                        verify_mixed)
+                        verify_mixed, ngram_draft_request, ngram_draft, verify_point_request,
+                        verify_point)
 
 __all__ = ["NEAR_TIE", "decode_logits", "softmax", "residual_weights", "inverse_cdf",
            "verify_sample_request", "verify_greedy_request", "predict_request", "verify_sample",
            "verify_greedy", "predict_outcomes", "outcome_hit", "fanout_offsets",
            "predict_fanout_request", "predict_fanout", "outcome_slot", "fanout_budget",
-           "kv_rewind", "temperature_is_valid", "verify_mixed_request", "verify_mixed"]
+           "kv_rewind", "temperature_is_valid", "verify_mixed_request", "verify_mixed",
+           "ngram_draft_request", "ngram_draft", "verify_point_request", "verify_point"]

@@ -180,3 +180,27 @@ def naive_kv_rewind(block_tables, block_size, kv_alloc, kv_new):
                 row[j] = -1
         offsets.append(len(freed))
     return tables, freed, offsets
+
+
+def naive_ngram_draft(ctx, n_max, n_min, K):
+    """Prompt lookup by explicit loops: for n from the longest allowed down, scan earlier starts
+    j from the latest back and compare token by token. Returns (tokens, length, n, src)."""
+    ctx = [int(t) for t in ctx]
+    L = len(ctx)
+    n = min(int(n_max), L - 1)
+    while n >= int(n_min) and n >= 1:
+        j = L - n - 1
+        while j >= 0:
+            same = True
+            for i in range(n):
+                if ctx[j + i] != ctx[L - n + i]:
+                    same = False
+                    break
+            if same:
+                src = j + n
+                length = min(int(K), L - src)
+                toks = [ctx[src + i] if i < length else -1 for i in range(int(K))]
+                return toks, length, n, src
+            j -= 1
+        n -= 1
+    return [-1] * int(K), 0, 0, -1

@@ -320,6 +320,112 @@ def kv_rewind(block_tables, block_size: int, kv_alloc, kv_new):
 
 
 # ----------------------------------------------------------------------------------------------
+# drafting without a draft model: n-gram / prompt lookup, and verification of its drafts
+def ngram_draft_request(ctx, n_max: int, n_min: int, K: int):
+    """Drafts up to K tokens for one request by prompt lookup ([SD] section "別のドラフトモデルは
+    常に必要なのか?", the n-gram and prompt-search bullet: instead of a network, the engine looks
+    for a span of the prompt and of the output generated so far that matches the text just
+    produced, and proposes the tokens that followed that span).
+
+    ctx holds the request's tokens so far (prompt then output), L of them. The span to match is
+    the last n tokens, ctx[L-n:], tried from n = min(n_max, L-1) down to n_min (a longer match is
+    more specific); an occurrence is any earlier start j <= L-n-1 with ctx[j:j+n] equal to it,
+    and of those the most recent (largest j) is taken. Its continuation starts at src = j + n,
+    and the draft is ctx[src : src + length] with length = min(K, L - src) (at least one token
+    follows every occurrence). No occurrence for any n: length 0.
+    Returns dict(tokens [K] (-1 past length), length, n (0 without a match), src (-1 without)).
+    """
+    c = np.asarray(ctx, dtype=np.int64)
+    L = int(c.size)
+    out = dict(tokens=np.full(K, -1, np.int64), length=0, n=0, src=-1)
+    for n in range(min(int(n_max), L - 1), int(n_min) - 1, -1):
+        # every window of n tokens that ends before the last token, compared with the suffix
+        win = np.lib.stride_tricks.sliding_window_view(c[:L - 1], n)
+        hits = np.nonzero(np.all(win == c[L - n:], axis=1))[0]
+        if hits.size:
+            src = int(hits[-1]) + n
+            length = min(int(K), L - src)
+            out["tokens"][:length] = c[src:src + length]
+            out.update(length=length, n=n, src=src)
+            return out
+    return out
+
+
+def verify_point_request(t_rows: np.ndarray, x, n: int, u, kv_in: int, T: float):
+    """Verification of a draft that comes with no distribution, such as a prompt-lookup draft
+    ([SD] stages 3 and 4, and the closing remark of the section on drafting without a draft
+    model: however the candidates are proposed, the target checks them in parallel with its own
+    exact distribution). The proposer puts all its mass on its token: q_k = point mass at x_k.
+
+    t_rows [K+1,V] float64 logits; x [K] tokens of which the first n (0 <= n <= K) are drafts and
+    the rest are ignored; u [K+1] uniforms; T >= 0.
+      T > 0: slot k < n is kept iff u_k < min(1, p_k(x_k) / q_k(x_k)) = min(1, p_k(x_k)); at the
+             first rejection m < n the token is drawn with u_K from max(0, p_m - q_m), which is
+             p_m with x_m removed; with all n kept, from the target row n (the bonus row).
+      T = 0: the greedy rule over the first n slots (kept while x_k is the target's top choice,
+             lowest id on ties; at m the top choice of row m is placed).
+    Row errors: n outside [0, K], or a draft token (k < n) outside [0, V).
+    Reported per slot k < n: p_k(x_k) (at T = 0 the top-choice indicator) and q_k(x_k) = 1;
+    slots k >= n report NaN, as do row errors.
+    """
+    K = len(x)
+    V = t_rows.shape[1]
+    x = [int(v) for v in x]
+    u = np.asarray(u, dtype=np.float64)
+    out = dict(tokens=np.full(K + 1, -1, np.int64), tau=-1, kv_out=int(kv_in),
+               p_x=np.full(K, np.nan), q_x=np.full(K, np.nan), m=-1, y=-1,
+               resid_mass=np.nan, margin=np.inf, flagged=False, row_error=False)
+    n = int(n)
+    if n < 0 or n > K or any(v < 0 or v >= V for v in x[:n]):
+        out["row_error"] = True
+        return out
+
+    if float(T) == 0.0:
+        g = [int(np.argmax(t_rows[k])) for k in range(n + 1)]   # first maximum = lowest id
+        m = n
+        for k in range(n):
+            if x[k] != g[k]:
+                m = k
+                break
+        y = g[m]
+        out["p_x"][:n] = [1.0 if x[k] == g[k] else 0.0 for k in range(n)]
+        out["q_x"][:n] = 1.0
+        margin = np.inf
+        Z = np.nan
+    else:
+        p = [softmax(t_rows[k], T) for k in range(n + 1)]
+        P = np.array([p[k][x[k]] for k in range(n)])
+        out["p_x"][:n] = P
+        out["q_x"][:n] = 1.0
+        margins = []
+        m = n
+        for k in range(n):
+            r = min(1.0, P[k])          # q_k(x_k) = 1
+            margins.append(abs(u[k] - r))
+            if not (u[k] < r):
+                m = k
+                break
+        if m < n:
+            q_m = np.zeros(V)
+            q_m[x[m]] = 1.0
+            w = residual_weights(p[m], q_m)
+            if not np.sum(w) > 0.0:
+                w = p[m]
+        else:
+            w = p[n]
+        y, C, Z, t = inverse_cdf(w, u[K])
+        margins.append(_cdf_margin(C, Z, t, y))
+        margin = float(min(margins))
+
+    tokens = np.full(K + 1, -1, np.int64)
+    tokens[:m] = x[:m]
+    tokens[m] = y
+    out.update(tokens=tokens, tau=m + 1, kv_out=int(kv_in) + m + 1, m=m, y=y, resid_mass=Z,
+               margin=margin, flagged=bool(margin < NEAR_TIE))
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
 # batches
 def _request_slices(n: int, requests):
     return range(n) if requests is None else requests
@@ -370,6 +476,35 @@ def predict_fanout(draft, dtype, tokens, fanout, T, requests=None):
                                   float(np.float32(T))) for b in idx]
     return dict(requests=np.array(idx), keys=np.stack([o[0] for o in out]),
                 key_prob=np.stack([o[1] for o in out]))
+
+
+def ngram_draft(ctx, lens, n_max, n_min, K, requests=None):
+    """Batch wrapper of ngram_draft_request over rows ctx[b, :lens[b]]; a length outside
+    [0, row width] is a row error (length -1, tokens -1, n 0, src -1)."""
+    ctx = np.asarray(ctx)
+    idx = list(_request_slices(ctx.shape[0], requests))
+    res = []
+    for b in idx:
+        L = int(lens[b])
+        if L < 0 or L > ctx.shape[1]:
+            res.append(dict(tokens=np.full(K, -1, np.int64), length=-1, n=0, src=-1))
+        else:
+            res.append(ngram_draft_request(ctx[b, :L], n_max, n_min, K))
+    return dict(requests=np.array(idx), tokens=np.stack([r["tokens"] for r in res]),
+                length=np.array([r["length"] for r in res]), n=np.array([r["n"] for r in res]),
+                src=np.array([r["src"] for r in res]))
+
+
+def verify_point(target, dtype, tokens, lens, uniforms, kv_len, T, requests=None):
+    """Batch wrapper of verify_point_request; lens None means every request drafts K."""
+    idx = list(_request_slices(target.shape[0], requests))
+    K = tokens.shape[1]
+    res = [verify_point_request(decode_logits(target[b], dtype), tokens[b],
+                                K if lens is None else int(lens[b]),
+                                np.asarray(uniforms[b], np.float64), int(kv_len[b]),
+                                float(np.float32(T)))
+           for b in idx]
+    return _stack(res, idx, K, sample=True)
 
 
 def _stack(res, idx, K, sample):
