@@ -69,8 +69,10 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 6
+#define SPEC_ABI_VERSION 7
 #define SPEC_MAX_K 64
+#define SPEC_MAX_NGRAM 64
+#define SPEC_MAX_CONTEXT 1073741824 /* 2^30 tokens per context row */
 #define SPEC_MAX_F 16
 #define SPEC_MAX_V 4194304 /* 2^22 */
 #define SPEC_DEFAULT_WAIT_POLLS 16384
@@ -178,6 +180,50 @@ int spec_verify_mixed(const void* target_logits, const void* draft_logits, int d
                       const int32_t* kv_len_in, const float* temperatures, int B, int K, int V,
                       int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len, float* out_p,
                       float* out_q, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Prompt-lookup drafting, a draft source with no draft model ([SD] section
+ * "別のドラフトモデルは常に必要なのか?", the n-gram and prompt-search bullet: match the latest
+ * text against the prompt and the output so far, and propose the tokens that followed).
+ *   context     [B, ld] int32 (device): row b holds request b's tokens so far, prompt then
+ *               output; only the first context_len[b] are read. Token ids are compared only.
+ *   ld          row stride in tokens, 1 <= ld <= SPEC_MAX_CONTEXT.
+ *   context_len [B] int32 (device): L_b; a value outside [0, ld] is a row error.
+ *   n_max, n_min  span lengths tried, 1 <= n_min <= n_max <= SPEC_MAX_NGRAM.
+ *   K           tokens drafted at most, 1 <= K <= SPEC_MAX_K.
+ * Rule: for n = min(n_max, L-1) down to n_min, the span ctx[L-n:] is looked for at earlier
+ * starts j <= L-n-1; the first n with an occurrence is used, at its largest j. The draft is
+ * ctx[src : src + len], src = j + n, len = min(K, L - src) >= 1; with no occurrence, len = 0.
+ * Outputs (device): out_tokens [B, K] int32 (the draft, -1 past len); out_len [B] int32 (len;
+ * -1 for a row error); out_ngram [B] int32 (nullable: the n used, 0 without a match);
+ * out_src [B] int32 (nullable: src, -1 without a match). One launch, one workgroup per request,
+ * no workspace. Errors: SPEC_ERR_ARG for a null required pointer or a size out of range;
+ * SPEC_ERR_HIP if the launch fails. */
+int spec_ngram_draft(const int32_t* context, long long ld, const int32_t* context_len, int B,
+                     int n_max, int n_min, int K, int32_t* out_tokens, int32_t* out_len,
+                     int32_t* out_ngram, int32_t* out_src, hipStream_t stream);
+
+/* Verification of drafts that come with no distribution, such as spec_ngram_draft's ([SD]
+ * stages 3-4 and the closing remark of the section on drafting without a draft model: whatever
+ * proposes the candidates, the target checks them with its own distribution). The proposer is
+ * taken to put all its probability on its token: q_k is a point mass at x_k.
+ *   draft_len [B] int32 (device, nullable = K for every request): request b drafts only its
+ *             first n_b slots; x_k for k >= n_b is ignored (any value). n_b outside [0, K] is a
+ *             row error.
+ *   T > 0: slot k < n_b is kept iff uniforms[b,k] < min(1, p_k(x_k)); at the first rejection
+ *          m < n_b the token is drawn with uniforms[b,K] by inverse CDF from p_m with x_m
+ *          removed (max(0, p_m - q_m)); with all n_b kept, from p_{n_b} (the bonus row).
+ *   T = 0: the greedy rule over the first n_b slots; uniforms may be NULL.
+ * Target rows past n_b are not read, so a request costs (n_b + 1) * V logits. Outputs as for
+ * spec_verify_sample: tokens [B,K+1] (-1 after slot m), tau = m + 1, kv = kv_in + tau;
+ * out_p[b,k] = p_k(x_k) (at T = 0 the top-choice indicator) and out_q[b,k] = 1 for k < n_b, NaN
+ * for k >= n_b and for row errors. A row error (n_b, or a drafted token outside [0, V)) gives
+ * tau = -1, all tokens -1 and kv unchanged. Host errors as for spec_verify_sample; temperature 0
+ * is allowed. */
+int spec_verify_point(const void* target_logits, int dtype, const int32_t* draft_tokens,
+                      const int32_t* draft_len, const float* uniforms, const int32_t* kv_len_in,
+                      int B, int K, int V, float temperature, int32_t* out_tokens,
+                      int32_t* out_tau, int32_t* out_kv_len, float* out_p, float* out_q,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Greedy verification, temperature must be exactly 0 ([SD] stage 3 at temperature zero;
  * [D3D] 検証のしくみ③, 検証のまとめ). g_k = argmax_v target_logits[b,k,v] (lowest v on ties);

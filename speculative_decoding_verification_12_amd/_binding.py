@@ -16,6 +16,8 @@ SPEC_BF16 = 1
 SPEC_MAX_K = 64
 SPEC_MAX_F = 16
 SPEC_MAX_V = 1 << 22
+SPEC_MAX_NGRAM = 64
+SPEC_MAX_CONTEXT = 1 << 30
 SPEC_DEFAULT_WAIT_POLLS = 16384
 STATUS = {0: "SPEC_OK", -1: "SPEC_ERR_ARG", -2: "SPEC_ERR_DTYPE", -3: "SPEC_ERR_TEMPERATURE",
           -4: "SPEC_ERR_WORKSPACE", -5: "SPEC_ERR_HIP"}
@@ -24,9 +26,11 @@ EXPORTS = ("spec_abi_version", "spec_status_string", "spec_workspace_bytes",
            "spec_workspace_init", "spec_verify_sample", "spec_verify_sample_ex",
            "spec_verify_sample_keys", "spec_verify_mixed", "spec_verify_greedy",
            "spec_predict_outcomes",
-           "spec_predict_fanout", "spec_outcome_lookup", "spec_kv_rewind")
+           "spec_predict_fanout", "spec_outcome_lookup", "spec_kv_rewind", "spec_ngram_draft",
+           "spec_verify_point")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_ll = ctypes.c_longlong
 _SIGNATURES = {
     "spec_abi_version": (_i, []),
     "spec_status_string": (ctypes.c_char_p, [_i]),
@@ -47,6 +51,9 @@ _SIGNATURES = {
                                  _vp]),
     "spec_outcome_lookup": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _i, _vp, _vp]),
     "spec_kv_rewind": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "spec_ngram_draft": (_i, [_vp, _ll, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "spec_verify_point": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _f,
+                               _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -353,4 +360,56 @@ def spec_kv_rewind(block_tables, block_size, kv_alloc, kv_new, out=None):
                                        _ptr(kv_alloc), _ptr(kv_new), _ptr(out["freed"]),
                                        _ptr(out["offsets"]), _stream(dev))
     _check("spec_kv_rewind", rc)
+    return out
+
+
+def spec_ngram_draft(context, context_len, n_max, n_min, K, out=None):
+    """Prompt-lookup drafts from int32 contexts [B, ld] with lengths [B]. Returns dict(tokens
+    [B,K] int32, len [B], ngram [B], src [B])."""
+    torch = _torch()
+    B, ld = context.shape
+    dev = context.device
+    _need(context, "context", (B, ld), torch.int32, dev)
+    _need(context_len, "context_len", (B,), torch.int32, dev)
+    if out is None:
+        out = dict(tokens=torch.empty((B, K), dtype=torch.int32, device=dev),
+                   len=torch.empty(B, dtype=torch.int32, device=dev),
+                   ngram=torch.empty(B, dtype=torch.int32, device=dev),
+                   src=torch.empty(B, dtype=torch.int32, device=dev))
+    rc = load_library().spec_ngram_draft(_ptr(context), ld, _ptr(context_len), B, int(n_max),
+                                         int(n_min), int(K), _ptr(out["tokens"]),
+                                         _ptr(out["len"]), _ptr(out.get("ngram")),
+                                         _ptr(out.get("src")), _stream(dev))
+    _check("spec_ngram_draft", rc)
+    return out
+
+
+def spec_verify_point(target, draft_tokens, draft_len, uniforms, kv_len, temperature, workspace,
+                      out=None):
+    """Verification of drafts with no distribution (point-mass drafts), draft_len [B] int32 or
+    None (= K). Returns dict(tokens, tau, kv_len, p, q)."""
+    torch = _torch()
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    _need(target, "target_logits", (B, K + 1, V), target.dtype, dev)
+    _need(draft_tokens, "draft_tokens", (B, K), torch.int32, dev)
+    if draft_len is not None:
+        _need(draft_len, "draft_len", (B,), torch.int32, dev)
+    if uniforms is not None:
+        _need(uniforms, "uniforms", (B, K + 1), torch.float32, dev)
+    if kv_len is not None:
+        _need(kv_len, "kv_len", (B,), torch.int32, dev)
+    if out is None:
+        out = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                   tau=torch.empty(B, dtype=torch.int32, device=dev),
+                   kv_len=torch.empty(B, dtype=torch.int32, device=dev),
+                   p=torch.empty((B, K), dtype=torch.float32, device=dev),
+                   q=torch.empty((B, K), dtype=torch.float32, device=dev))
+    rc = load_library().spec_verify_point(
+        _ptr(target), _dtype_code(target), _ptr(draft_tokens), _ptr(draft_len), _ptr(uniforms),
+        _ptr(kv_len), B, K, V, float(temperature), _ptr(out["tokens"]), _ptr(out["tau"]),
+        _ptr(out.get("kv_len")), _ptr(out.get("p")), _ptr(out.get("q")), _ptr(workspace),
+        workspace.numel(), _stream(dev))
+    _check("spec_verify_point", rc)
     return out

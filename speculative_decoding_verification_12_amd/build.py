@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["api.hip", "verify_sample.hip", "verify_greedy.hip", "predict.hip", "kv_cache.hip"]
+SOURCES = ["api.hip", "verify_sample.hip", "verify_greedy.hip", "predict.hip", "kv_cache.hip",
+           "ngram.hip"]
 ARCH = os.environ.get("SPEC_VERIFY_ARCH", "gfx950")
 
 

@@ -53,4 +53,11 @@ inline T* ws_ptr(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
+// Greedy verification with optional draft lengths and p/q outputs (defined with the greedy
+// kernel); the point-mass verification entry uses it at temperature zero.
+int greedy_point_entry(const void* target, int dtype, const int32_t* xtok, const int32_t* dlen,
+                       const int32_t* kv_in, int B, int K, int V, int32_t* out_tok,
+                       int32_t* out_tau, int32_t* out_kv, float* out_p, float* out_q, void* ws,
+                       hipStream_t stream);
+
 }  // namespace sv

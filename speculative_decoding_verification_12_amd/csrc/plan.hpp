@@ -69,6 +69,10 @@ SV_HD inline KernelPlan draw_plan(int B, int K, int V, int epv) {
   const int nvec = V / epv > 0 ? V / epv : 1;
   return KernelPlan{kBlock * kDrawVecs, ceil_div(nvec, kBlock * kDrawVecs)};
 }
+// point-mass drafts: the statistics pass streams only the K+1 target rows
+SV_HD inline KernelPlan point_plan(int B, int K, int V, int epv) {
+  return plan_rows(B * (K + 1), V, epv, kStatsResident);
+}
 SV_HD inline KernelPlan greedy_plan(int B, int K, int V, int epv) {
   return plan_rows(B * (K + 1), V, epv, kGreedyResident);
 }
@@ -84,7 +88,7 @@ SV_HD inline KernelPlan predict_plan(int B, int K, int V, int epv) {
 // per-request outcome of the slot scan, as the draw needs it
 struct ReqState {
   int m;          // first rejected slot (K when all kept), -1 for a row error
-  int pad;
+  int xm;         // point-mass drafts: the rejected draft token, removed from the residual (-1)
   float mc_t;     // fl32(M_t * c): reference exponent of the target row used by the draw
   float inv_t;    // fl32(1 / S_t)
   float mc_d;     // same for the draft row of slot m (unused when m == K)
@@ -101,7 +105,7 @@ struct WsLayout {
   size_t cnt_b;      // unsigned[B * kCounterStride]: counters of the residual/bonus draw
   size_t counters_end;
   size_t gathered;   // float [B*2K]: target and draft logit of each slot's draft token
-  size_t part_stats; // 8 B [B*(2K+1)*nchunk]: chunk (max, scaled sum)
+  size_t part_stats; // 8 B [B*(2K+1)*nchunk] (point drafts: [B*(K+1)*nchunk]): chunk (max, sum)
   size_t part_draw;  // 16 B [B*nchunk]: published chunk (residual mass, target mass)
   size_t part_greedy;// 8 B [B*(K+1)*nchunk]: chunk (max, lowest index)
   size_t part_topf;  // 8 B [B*K*nchunk*4*kWaveSlots]: each wave's candidate list
@@ -124,6 +128,7 @@ inline size_t max_chunks(PlanFn fn, int B, int K, int V) {
 inline WsLayout ws_layout(int B, int K, int V, int F) {
   const size_t b = static_cast<size_t>(B), k = static_cast<size_t>(K);
   const size_t ns = max_chunks(stats_plan, B, K, V);
+  const size_t npt = max_chunks(point_plan, B, K, V);
   const size_t nd = max_chunks(draw_plan, B, K, V);
   const size_t ng = max_chunks(greedy_plan, B, K, V);
   const size_t np = max_chunks(predict_plan, B, K, V);
@@ -138,7 +143,8 @@ inline WsLayout ws_layout(int B, int K, int V, int F) {
   L.gathered = off;
   off = align256(off + sizeof(float) * 2 * b * k);
   L.part_stats = off;
-  off = align256(off + 8 * b * (2 * k + 1) * ns);
+  off = align256(off + 8 * (b * (2 * k + 1) * ns > b * (k + 1) * npt ? b * (2 * k + 1) * ns
+                                                                      : b * (k + 1) * npt));
   L.part_draw = off;
   off = align256(off + 16 * b * nd);
   L.part_greedy = off;

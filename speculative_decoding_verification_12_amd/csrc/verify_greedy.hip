@@ -6,6 +6,9 @@
 // the target's own g_m is placed and the rest dropped; if all K match, g_K (the extra row) is
 // appended. tau = m + 1, the KV length advances by tau. Ties in the target's top choice go to
 // the lowest token id. Only the K+1 target rows are read; the draft logits are not needed.
+// With draft lengths (drafts that carry no distribution, e.g. prompt lookup) only the first n_b
+// slots hold drafts: rows past n_b are not read, and with all n_b kept the top choice of row
+// n_b is appended.
 //
 // One launch: a workgroup per (request, row, chunk) streams its chunk once, tracks the largest
 // logit and its lowest id per thread, and reduces (value desc, id asc) across the workgroup. The
@@ -17,27 +20,14 @@
 namespace sv {
 namespace {
 
+// The (max, lowest id) of chunk `ch` of row `rb`, stored as that chunk's partial.
 template <typename TIn>
-__global__ __launch_bounds__(kBlock) void greedy_kernel(
-    const TIn* __restrict__ tgt, const int32_t* __restrict__ xtok,
-    const int32_t* __restrict__ kv_in, int K, int V, int nchunk, int cv,
-    ArgPart* __restrict__ part, unsigned* __restrict__ cnt_base, int32_t* __restrict__ out_tok,
-    int32_t* __restrict__ out_tau,
-    int32_t* __restrict__ out_kv) {
+__device__ __forceinline__ void greedy_chunk(const TIn* __restrict__ tgt, int rb, int ch, int V,
+                                             int nchunk, int cv, ArgPart* __restrict__ part,
+                                             float* s_v, int* s_i) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
-  __shared__ float s_v[kWaves];
-  __shared__ int s_i[kWaves];
-  __shared__ int s_flag;
-  __shared__ int row_g[SPEC_MAX_K + 1];
-
-  const int rows = K + 1;
-  const int ch = blockIdx.x % nchunk;
-  const int rb = blockIdx.x / nchunk;   // b * (K+1) + row
-  const int b = rb / rows;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  unsigned* cnt = cnt_base + static_cast<size_t>(b) * kCounterStride;
-
   const TIn* row = tgt + static_cast<size_t>(rb) * static_cast<size_t>(V);
   const RowSpan sp = row_span(row, V);
   const ChunkRange cr = chunk_range(sp, ch, nchunk, cv);
@@ -97,10 +87,40 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
       }
     store_coherent(&part[static_cast<size_t>(rb) * nchunk + ch], pack2(v, i));
   }
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(kBlock) void greedy_kernel(
+    const TIn* __restrict__ tgt, const int32_t* __restrict__ xtok,
+    const int32_t* __restrict__ kv_in, int K, int V, int nchunk, int cv,
+    ArgPart* __restrict__ part, unsigned* __restrict__ cnt_base, int32_t* __restrict__ out_tok,
+    int32_t* __restrict__ out_tau, int32_t* __restrict__ out_kv,
+    const int32_t* __restrict__ dlen, float* __restrict__ out_p, float* __restrict__ out_q) {
+  __shared__ float s_v[kWaves];
+  __shared__ int s_i[kWaves];
+  __shared__ int s_flag;
+  __shared__ int row_g[SPEC_MAX_K + 1];
+
+  const int rows = K + 1;
+  const int ch = blockIdx.x % nchunk;
+  const int rb = blockIdx.x / nchunk;   // b * (K+1) + row
+  const int b = rb / rows;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  unsigned* cnt = cnt_base + static_cast<size_t>(b) * kCounterStride;
+  // drafts in this request: K, or the first dlen[b] slots (outside [0, K]: a row error)
+  int nb = K;
+  bool nb_bad = false;
+  if (dlen != nullptr) {
+    nb = dlen[b];
+    nb_bad = nb < 0 || nb > K;
+    if (nb_bad) nb = -1;
+  }
+  // a row past n_b is never used by an outcome: it is not read, but its workgroups still arrive
+  if (rb % rows <= nb) greedy_chunk<TIn>(tgt, rb, ch, V, nchunk, cv, part, s_v, s_i);
   if (!arrive_last(cnt, static_cast<unsigned>(rows * nchunk), &s_flag)) return;
 
-  // ---- last workgroup of request b: per-row argmax over chunks
-  for (int rr = w; rr < rows; rr += kWaves) {
+  // ---- last workgroup of request b: per-row argmax over chunks (rows up to n_b)
+  for (int rr = w; rr < rows && rr <= nb; rr += kWaves) {
     const ArgPart* pr = part + (static_cast<size_t>(b) * rows + rr) * nchunk;
     float v = -INFINITY;
     int i = 0x7fffffff;
@@ -119,12 +139,17 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
   if (w != 0) return;
 
   const int k = lane;
-  const bool valid = k < K;
+  const bool valid = k < nb;
   const int xk = valid ? xtok[static_cast<size_t>(b) * K + k] : 0;
   const bool bad = valid && (xk < 0 || xk >= V);
-  const bool err = __ballot(bad) != 0ull;
+  const bool err = nb_bad || __ballot(bad) != 0ull;
   const unsigned long long miss = __ballot(valid && xk != row_g[valid ? k : 0]);
-  const int mm = miss ? (__ffsll(static_cast<long long>(miss)) - 1) : K;
+  const int mm = err ? 0 : (miss ? (__ffsll(static_cast<long long>(miss)) - 1) : nb);
+  if (out_p != nullptr && k < K) {   // at temperature zero: p_k(x_k) is the top-choice indicator
+    const size_t o = static_cast<size_t>(b) * K + k;
+    out_p[o] = (err || !valid) ? NAN : (xk == row_g[k] ? 1.f : 0.f);
+    if (out_q) out_q[o] = (err || !valid) ? NAN : 1.f;
+  }
   for (int j = lane; j <= K; j += kWave) {
     int tok = -1;
     if (!err) tok = j < mm ? xk : (j == mm ? row_g[mm] : -1);
@@ -141,18 +166,30 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
 template <typename TIn>
 int launch_greedy(const void* target, const int32_t* xtok, const int32_t* kv_in, int B, int K,
                   int V, int32_t* out_tok, int32_t* out_tau, int32_t* out_kv, void* ws,
-                  hipStream_t stream, const KernelPlan& P) {
+                  hipStream_t stream, const KernelPlan& P, const int32_t* dlen = nullptr,
+                  float* out_p = nullptr, float* out_q = nullptr) {
   const size_t g = static_cast<size_t>(B) * (K + 1) * P.nchunk;
   if (!grid_fits(g)) return SPEC_ERR_ARG;
   const WsLayout L = ws_layout(B, K, V, 1);
   hipLaunchKernelGGL(greedy_kernel<TIn>, dim3(static_cast<unsigned>(g)), dim3(kBlock), 0, stream,
                      static_cast<const TIn*>(target), xtok, kv_in, K, V, P.nchunk, P.cv,
                      ws_ptr<ArgPart>(ws, L.part_greedy), ws_ptr<unsigned>(ws, L.cnt_a), out_tok,
-                     out_tau, out_kv);
+                     out_tau, out_kv, dlen, out_p, out_q);
   return launch_status();
 }
 
 }  // namespace
+
+int greedy_point_entry(const void* target, int dtype, const int32_t* xtok, const int32_t* dlen,
+                       const int32_t* kv_in, int B, int K, int V, int32_t* out_tok,
+                       int32_t* out_tau, int32_t* out_kv, float* out_p, float* out_q, void* ws,
+                       hipStream_t stream) {
+  if (dtype == SPEC_BF16)
+    return launch_greedy<uint16_t>(target, xtok, kv_in, B, K, V, out_tok, out_tau, out_kv, ws,
+                                   stream, greedy_plan(B, K, V, 8), dlen, out_p, out_q);
+  return launch_greedy<float>(target, xtok, kv_in, B, K, V, out_tok, out_tau, out_kv, ws, stream,
+                              greedy_plan(B, K, V, 4), dlen, out_p, out_q);
+}
 }  // namespace sv
 
 extern "C" int spec_verify_greedy(const void* target_logits, int dtype,

@@ -186,12 +186,13 @@ __device__ __forceinline__ void chunk_argmax(const TIn* row, const RowSpan& sp,
   }
 }
 
-template <typename TIn, bool kKeys, bool kMixed>
+template <typename TIn, bool kKeys, bool kMixed, bool kPoint>
 __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
     const TIn* __restrict__ tgt, const TIn* __restrict__ drf, const int32_t* __restrict__ xtok,
     int K, int V, float c_call, int nchunk, int cv, float2* __restrict__ part,
     float* __restrict__ gath, uint64_t* __restrict__ clear, int nclear,
-    float* __restrict__ key_wave_max, const float* __restrict__ temps) {
+    float* __restrict__ key_wave_max, const float* __restrict__ temps,
+    const int32_t* __restrict__ dlen) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
   __shared__ float sm[kWaves], ss[kWaves];
@@ -200,11 +201,20 @@ __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
        gi < static_cast<size_t>(nclear); gi += static_cast<size_t>(gridDim.x) * kBlock)
     clear[gi] = 0ull;
 
-  const int rows = 2 * K + 1;
+  // point-mass drafts (kPoint) have no draft rows: only the K+1 target rows are streamed
+  const int rows = kPoint ? K + 1 : 2 * K + 1;
   const int ch = blockIdx.x % nchunk;
   const int rb = blockIdx.x / nchunk;   // request-major (request, row) index
   const int r = rb % rows;
   const int b = rb / rows;
+  if constexpr (kPoint) {
+    // with draft lengths, target rows past n_b are never used (the draw reads row m <= n_b); a
+    // length outside [0, K] is a row error and needs no row at all
+    if (dlen != nullptr) {
+      const int nb = dlen[b];
+      if (nb < 0 || nb > K || r > nb) return;
+    }
+  }
 
   // per-request temperature (mixed batches): T_b = 0 is the greedy rule, which reads no draft
   // row and keeps each target chunk's (max, lowest id); an invalid T_b (a row error in the
@@ -260,6 +270,8 @@ __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
 // Weights of the draw over row m: w = max(0, p - q) (residual, m < K) or w = p (bonus, m == K),
 // with p = 2^(l*c - mc_t) / S_t and q likewise. `use_p` switches to w = p, the fallback when
 // round-off leaves no residual mass.
+// With a point-mass draft (kMask) the residual max(0, p - q) is p with the draft token `mask`
+// removed (mask < 0: the bonus row, w = p).
 template <typename TIn>
 struct DrawRows {
   const TIn* t;
@@ -267,18 +279,20 @@ struct DrawRows {
   RowSpan sp;        // span of the target row; chunks follow it
   bool d_aligned;    // draft row has the same 16-byte phase, so vector loads line up
   bool resid;
+  int mask;          // point-mass residual: the token whose weight is 0 (-1: none)
 };
 
-template <typename TIn>
+template <bool kMask, typename TIn>
 __device__ __forceinline__ float weight_one(const DrawRows<TIn>& R, const ReqState& st, float c,
                                             int tok, bool use_p, float& p) {
   p = fast_exp2(fmaf(Elem<TIn>::one(R.t, tok), c, -st.mc_t)) * st.inv_t;
+  if constexpr (kMask) return (tok == R.mask && !use_p) ? 0.f : p;
   if (!R.resid || use_p) return p;
   const float q = fast_exp2(fmaf(Elem<TIn>::one(R.d, tok), c, -st.mc_d)) * st.inv_d;
   return fmaxf(p - q, 0.f);
 }
 
-template <typename TIn>
+template <bool kMask, typename TIn>
 __device__ __forceinline__ void weight_group(const DrawRows<TIn>& R, const ReqState& st, float c,
                                              const uint4& qt, const uint4& qd, int v, bool use_p,
                                              float (&w)[Elem<TIn>::N],
@@ -289,6 +303,12 @@ __device__ __forceinline__ void weight_group(const DrawRows<TIn>& R, const ReqSt
   E::unpack(qt, lt);
 #pragma unroll
   for (int j = 0; j < N; ++j) p[j] = fast_exp2(fmaf(lt[j], c, -st.mc_t)) * st.inv_t;
+  if constexpr (kMask) {
+    const int tok0 = R.sp.head + v * N;
+#pragma unroll
+    for (int j = 0; j < N; ++j) w[j] = (tok0 + j == R.mask && !use_p) ? 0.f : p[j];
+    return;
+  }
   if (!R.resid || use_p) {
 #pragma unroll
     for (int j = 0; j < N; ++j) w[j] = p[j];
@@ -346,7 +366,7 @@ __device__ __forceinline__ ThreadElems thread_elems(const RowSpan& sp, int V, in
 
 // One thread's draw mass ws (sum of w) and target mass ps (sum of p), summed in token order;
 // `qt`/`qd` receive its vectors. Deterministic: the owner and any helper get the same bits.
-template <typename TIn>
+template <bool kMask, typename TIn>
 __device__ __forceinline__ void thread_mass(const DrawRows<TIn>& R, const ReqState& st, float c,
                                             int V, const ThreadElems& el, uint4 (&qt)[kDrawVecs],
                                             uint4 (&qd)[kDrawVecs], float& ws, float& ps) {
@@ -357,14 +377,14 @@ __device__ __forceinline__ void thread_mass(const DrawRows<TIn>& R, const ReqSta
   ps = 0.f;
   float p;
   for (int e = 0; e < el.nh; ++e) {
-    ws += weight_one(R, st, c, e, false, p);
+    ws += weight_one<kMask>(R, st, c, e, false, p);
     ps += p;
   }
 #pragma unroll
   for (int i = 0; i < kDrawVecs; ++i) {
     if (i < el.nv) {
       float wv[N], pv[N];
-      weight_group(R, st, c, qt[i], qd[i], el.v0 + i, false, wv, pv);
+      weight_group<kMask>(R, st, c, qt[i], qd[i], el.v0 + i, false, wv, pv);
 #pragma unroll
       for (int j = 0; j < N; ++j) {
         ws += wv[j];
@@ -373,7 +393,7 @@ __device__ __forceinline__ void thread_mass(const DrawRows<TIn>& R, const ReqSta
     }
   }
   for (int e = 0; e < el.nt; ++e) {
-    ws += weight_one(R, st, c, el.tail0 + e, false, p);
+    ws += weight_one<kMask>(R, st, c, el.tail0 + e, false, p);
     ps += p;
   }
 }
@@ -691,7 +711,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void keys_merge_kernel(const T
 
 // Chunks of kBlock * kDrawVecs vectors (see draw_plan). cm holds the published (R, P) of every
 // chunk, [b][ch][2] words, zeroed by the statistics kernel of the same call.
-template <typename TIn, bool kKeys, bool kMixed>
+template <typename TIn, bool kKeys, bool kMixed, bool kPoint>
 __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     const TIn* __restrict__ tgt, const TIn* __restrict__ drf, const int32_t* __restrict__ xtok,
     const float* __restrict__ uni, const int32_t* __restrict__ kv_in, int K, int V, float c_call,
@@ -699,7 +719,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     int nchunk, int cv, uint64_t* __restrict__ cm, int wait_polls,
     int32_t* __restrict__ out_tok, int32_t* __restrict__ out_tau, int32_t* __restrict__ out_kv,
     float* __restrict__ out_p, float* __restrict__ out_q, KeyArgs ka,
-    const float* __restrict__ temps) {
+    const float* __restrict__ temps, const int32_t* __restrict__ dlen) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
   __shared__ double s_red[2][kWaves];
@@ -715,7 +735,19 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
   const int b = blockIdx.x / nchunk;
   const int ch = blockIdx.x % nchunk;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  const int rows = 2 * K + 1;
+  const int rows = kPoint ? K + 1 : 2 * K + 1;
+
+  // drafts in this request: K, or (point-mass drafts with lengths) the first dlen[b] slots; a
+  // length outside [0, K] is a row error
+  int nb = K;
+  bool nb_bad = false;
+  if constexpr (kPoint) {
+    if (dlen != nullptr) {
+      nb = dlen[b];
+      nb_bad = nb < 0 || nb > K;
+      if (nb_bad) nb = 0;
+    }
+  }
 
   float c = c_call;
   if constexpr (kMixed) {
@@ -775,14 +807,14 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
   // ---- merge the statistics pass of request b (every workgroup of b does the same, bit for
   // bit): row (max, sum) in fp32/fp64, slot acceptance ratios, first rejection by ballot
   {
-    const bool valid = w == 0 && lane < K;
+    const bool valid = w == 0 && lane < nb;
     int xk = 0;
     float lt = 0.f, ld = 0.f, uk = 0.f;
     if (valid) {
       xk = xtok[static_cast<size_t>(b) * K + lane];
       uk = uni[static_cast<size_t>(b) * (K + 1) + lane];
       lt = gath[static_cast<size_t>(b) * 2 * K + lane];
-      ld = gath[static_cast<size_t>(b) * 2 * K + K + lane];
+      if constexpr (!kPoint) ld = gath[static_cast<size_t>(b) * 2 * K + K + lane];
     }
     const int kv0 = (ch == 0 && tid == 0 && kv_in) ? kv_in[b] : 0;
     // Rows are merged in groups of W lanes (W = nchunk_s rounded up to a power of two, at most
@@ -827,30 +859,36 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     __syncthreads();
     if (w == 0) {
       // a draft token must be a token the draft could have sampled
-      const bool bad = valid && (xk < 0 || xk >= V || ld == -INFINITY);
+      const bool bad = valid && (xk < 0 || xk >= V || (!kPoint && ld == -INFINITY));
       bool keep = true;
       double pk = 0.0, qk = 0.0;
       if (valid && !bad) {
-        // p_k(x_k) and q_k(x_k): 2^(l*c - fl(M*c)) / S of each row
+        // p_k(x_k) and q_k(x_k): 2^(l*c - fl(M*c)) / S of each row; a point-mass draft has
+        // q_k(x_k) = 1
         pk = exp2_wide(static_cast<double>(lt) * c - static_cast<double>(row_m[lane] * c)) /
              row_s[lane];
-        qk = exp2_wide(static_cast<double>(ld) * c - static_cast<double>(row_m[K + 1 + lane] * c)) /
-             row_s[K + 1 + lane];
+        if constexpr (kPoint)
+          qk = 1.0;
+        else
+          qk = exp2_wide(static_cast<double>(ld) * c -
+                         static_cast<double>(row_m[K + 1 + lane] * c)) /
+               row_s[K + 1 + lane];
         // kept iff u < min(1, p/q): p >= q is kept for every u in [0,1)
         keep = pk >= qk || static_cast<double>(uk) < pk / qk;
       }
-      const bool err = __ballot(bad) != 0ull;
+      const bool err = nb_bad || __ballot(bad) != 0ull;
       const unsigned long long rej = __ballot(valid && !keep);
-      const int mm = rej ? (__ffsll(static_cast<long long>(rej)) - 1) : K;
+      const int mm = rej ? (__ffsll(static_cast<long long>(rej)) - 1) : nb;
+      const int xm = __shfl(xk, mm < nb ? mm : 0, kWave);   // the rejected draft token
       if (ch == 0) {   // one workgroup of the request writes everything but the drawn token
         if constexpr (kKeys)   // the draft rows' statistics, for the key probabilities
           if (valid)
             ka.row_stats[static_cast<size_t>(b) * K + lane] =
                 RowStat{row_m[K + 1 + lane], 0.f, row_s[K + 1 + lane]};
-        if (valid) {
+        if (lane < K) {   // slots past the request's drafts report NaN
           const size_t o = static_cast<size_t>(b) * K + lane;
-          if (out_p) out_p[o] = err ? NAN : static_cast<float>(pk);
-          if (out_q) out_q[o] = err ? NAN : static_cast<float>(qk);
+          if (out_p) out_p[o] = (err || !valid) ? NAN : static_cast<float>(pk);
+          if (out_q) out_q[o] = (err || !valid) ? NAN : static_cast<float>(qk);
         }
         for (int j = lane; j <= K; j += kWave)
           if (err || j != mm) out_tok[static_cast<size_t>(b) * (K + 1) + j] = (!err && j < mm) ? xk : -1;
@@ -862,11 +900,11 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       if (lane == 0) {
         ReqState st;
         st.m = err ? -1 : mm;
-        st.pad = 0;
+        st.xm = (kPoint && mm < nb) ? xm : -1;
         st.mc_t = row_m[mm] * c;
         st.inv_t = static_cast<float>(1.0 / row_s[mm]);
-        st.mc_d = mm < K ? row_m[K + 1 + mm] * c : 0.f;
-        st.inv_d = mm < K ? static_cast<float>(1.0 / row_s[K + 1 + mm]) : 0.f;
+        st.mc_d = (!kPoint && mm < K) ? row_m[K + 1 + mm] * c : 0.f;
+        st.inv_d = (!kPoint && mm < K) ? static_cast<float>(1.0 / row_s[K + 1 + mm]) : 0.f;
         s_st = st;
       }
     }
@@ -877,7 +915,8 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
   if (st.m < 0) return;   // row error: nothing to draw (every workgroup of b agrees)
 
   DrawRows<TIn> R;
-  R.resid = st.m < K;
+  R.resid = !kPoint && st.m < K;
+  R.mask = st.xm;
   R.t = tgt + (static_cast<size_t>(b) * (K + 1) + st.m) * static_cast<size_t>(V);
   R.d = R.resid ? drf + (static_cast<size_t>(b) * K + st.m) * static_cast<size_t>(V) : R.t;
   R.sp = row_span(R.t, V);
@@ -888,7 +927,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
   const ThreadElems el = thread_elems(R.sp, V, nchunk, cv, ch, tid);
   uint4 qt[kDrawVecs], qd[kDrawVecs];
   float ws, ps;
-  thread_mass(R, st, c, V, el, qt, qd, ws, ps);
+  thread_mass<kPoint>(R, st, c, V, el, qt, qd, ws, ps);
   double R0, P0;
   chunk_mass(ws, ps, s_red, R0, P0);
   if (tid == 0) {
@@ -912,7 +951,8 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       if (!(s_cm[j].x < 0.0)) continue;   // uniform: read after a barrier
       uint4 ht[kDrawVecs], hd[kDrawVecs];
       float hw, hp;
-      thread_mass(R, st, c, V, thread_elems(R.sp, V, nchunk, cv, j, tid), ht, hd, hw, hp);
+      thread_mass<kPoint>(R, st, c, V, thread_elems(R.sp, V, nchunk, cv, j, tid), ht, hd, hw,
+                          hp);
       double hr, hq;
       chunk_mass(hw, hp, s_red, hr, hq);
       if (tid == 0) s_cm[j] = make_double2(hr, hq);
@@ -1043,7 +1083,11 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     float we = 0.f;
     if (has) {
       const float p = fast_exp2(fmaf(lt, c, -st.mc_t)) * st.inv_t;
-      we = (!R.resid || use_p) ? p : fmaxf(p - fast_exp2(fmaf(ld, c, -st.mc_d)) * st.inv_d, 0.f);
+      if constexpr (kPoint)
+        we = (tok == R.mask && !use_p) ? 0.f : p;
+      else
+        we = (!R.resid || use_p) ? p
+                                 : fmaxf(p - fast_exp2(fmaf(ld, c, -st.mc_d)) * st.inv_d, 0.f);
     }
     const double cum = s_cb + wave_scan_incl(static_cast<double>(we));
     const unsigned long long pos = __ballot(we > 0.f);
@@ -1075,13 +1119,13 @@ struct KeyRequest {
   float* out_prob;
 };
 
-template <typename TIn, bool kKeys, bool kMixed>
+template <typename TIn, bool kKeys, bool kMixed, bool kPoint = false>
 int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, const float* uni,
                     const int32_t* kv_in, int B, int K, int V, float T, int32_t* out_tok,
                     int32_t* out_tau, int32_t* out_kv, float* out_p, float* out_q, void* ws,
                     hipStream_t stream, hipEvent_t* ev, int wait_polls, const SamplePlan& P,
-                    const KeyRequest& kr, const float* temps) {
-  const size_t g1 = static_cast<size_t>(B) * (2 * K + 1) * P.stats.nchunk;
+                    const KeyRequest& kr, const float* temps, const int32_t* dlen = nullptr) {
+  const size_t g1 = static_cast<size_t>(B) * (kPoint ? K + 1 : 2 * K + 1) * P.stats.nchunk;
   const size_t g2 = static_cast<size_t>(B) * P.draw.nchunk;
   if (!grid_fits(g1) || !grid_fits(g2) || P.draw.cv != kBlock * kDrawVecs ||
       P.draw.nchunk > kMaxDrawChunks)
@@ -1089,7 +1133,7 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
   const WsLayout L = ws_layout(B, K, V, 1);
   const float c = exp2_scale(T);
   const TIn* t = static_cast<const TIn*>(target);
-  const TIn* d = static_cast<const TIn*>(draft);
+  const TIn* d = static_cast<const TIn*>(draft);   // null for point-mass drafts
   float2* part1 = ws_ptr<float2>(ws, L.part_stats);
   float* gath = ws_ptr<float>(ws, L.gathered);
   uint64_t* cm = ws_ptr<uint64_t>(ws, L.part_draw);
@@ -1103,24 +1147,25 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
   const KeyArgs ka{pick, kr.F, kr.exclude, cs, kwmax, krows, kr.out_keys, kr.out_prob};
   const dim3 grid3(static_cast<unsigned>(static_cast<size_t>(B) * K));
   if (ev == nullptr) {
-    hipLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed>), grid1, block, 0, stream, t, d,
-                       xtok, K, V, c, ns, cs, part1, gath, cm, nclear, kwmax, temps);
-    hipLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed>), grid2, block, 0, stream, t, d,
+    hipLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0, stream, t, d,
+                       xtok, K, V, c, ns, cs, part1, gath, cm, nclear, kwmax, temps, dlen);
+    hipLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint>), grid2, block, 0, stream, t, d,
                        xtok, uni, kv_in, K, V, c, ns, static_cast<const float2*>(part1),
                        static_cast<const float*>(gath), nd, cd, cm, polls, out_tok, out_tau,
-                       out_kv, out_p, out_q, ka, temps);
+                       out_kv, out_p, out_q, ka, temps, dlen);
     if constexpr (kKeys)
       hipLaunchKernelGGL(keys_merge_kernel<TIn>, grid3, dim3(kMergeWaves * kWave), 0, stream, d,
                          xtok, K, V, c, ns, ka);
   } else {
     // profiling: the runtime records the events at each kernel's start and end
-    hipExtLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed>), grid1, block, 0, stream,
+    hipExtLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0, stream,
                           ev[0], ev[1], 0, t, d, xtok, K, V, c, ns, cs, part1, gath, cm, nclear,
-                          kwmax, temps);
-    hipExtLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed>), grid2, block, 0, stream,
+                          kwmax, temps, dlen);
+    hipExtLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint>), grid2, block, 0, stream,
                           ev[2], ev[3], 0, t, d, xtok, uni, kv_in, K, V, c, ns,
                           static_cast<const float2*>(part1), static_cast<const float*>(gath), nd,
-                          cd, cm, polls, out_tok, out_tau, out_kv, out_p, out_q, ka, temps);
+                          cd, cm, polls, out_tok, out_tau, out_kv, out_p, out_q, ka, temps,
+                          dlen);
     if constexpr (kKeys)
       hipLaunchKernelGGL(keys_merge_kernel<TIn>, grid3, dim3(kMergeWaves * kWave), 0, stream, d,
                          xtok, K, V, c, ns, ka);
@@ -1238,4 +1283,38 @@ extern "C" int spec_verify_mixed(const void* target_logits, const void* draft_lo
                                  kv_len_in, B, K, V, 1.f, out_tokens, out_tau, out_kv_len, out_p,
                                  out_q, workspace, workspace_bytes, stream, nullptr, -1,
                                  sv::KeyRequest{0, 0, nullptr, nullptr}, temperatures);
+}
+
+extern "C" int spec_verify_point(const void* target_logits, int dtype,
+                                 const int32_t* draft_tokens, const int32_t* draft_len,
+                                 const float* uniforms, const int32_t* kv_len_in, int B, int K,
+                                 int V, float temperature, int32_t* out_tokens, int32_t* out_tau,
+                                 int32_t* out_kv_len, float* out_p, float* out_q,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  using namespace sv;
+  int rc = check_dtype(dtype);
+  if (rc != SPEC_OK) return rc;
+  if ((rc = check_dims(B, K, V)) != SPEC_OK) return rc;
+  if (check_logits(target_logits, dtype) != SPEC_OK || draft_tokens == nullptr ||
+      out_tokens == nullptr || out_tau == nullptr)
+    return SPEC_ERR_ARG;
+  if (!(temperature == 0.f) &&
+      (!std::isfinite(temperature) || !(temperature > 0.f) ||
+       !std::isfinite(exp2_scale(temperature))))
+    return SPEC_ERR_TEMPERATURE;
+  if ((rc = check_workspace(workspace, workspace_bytes, B, K, V, 1)) != SPEC_OK) return rc;
+  if (temperature == 0.f)
+    return greedy_point_entry(target_logits, dtype, draft_tokens, draft_len, kv_len_in, B, K, V,
+                              out_tokens, out_tau, out_kv_len, out_p, out_q, workspace, stream);
+  if (uniforms == nullptr) return SPEC_ERR_ARG;
+  const KeyRequest none{0, 0, nullptr, nullptr};
+  if (dtype == SPEC_BF16)
+    return launch_sample_t<uint16_t, false, false, true>(
+        target_logits, nullptr, draft_tokens, uniforms, kv_len_in, B, K, V, temperature,
+        out_tokens, out_tau, out_kv_len, out_p, out_q, workspace, stream, nullptr, -1,
+        SamplePlan{point_plan(B, K, V, 8), draw_plan(B, K, V, 8)}, none, nullptr, draft_len);
+  return launch_sample_t<float, false, false, true>(
+      target_logits, nullptr, draft_tokens, uniforms, kv_len_in, B, K, V, temperature,
+      out_tokens, out_tau, out_kv_len, out_p, out_q, workspace, stream, nullptr, -1,
+      SamplePlan{point_plan(B, K, V, 4), draw_plan(B, K, V, 4)}, none, nullptr, draft_len);
 }

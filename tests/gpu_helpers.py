@@ -269,3 +269,70 @@ def compare_mixed(wl, gpu, temps, requests=None):
         assert tau == int(ref["tau"][i]) and np.array_equal(tok, ref["tokens"][i]), where
         assert kv == int(ref["kv_out"][i]), where
     return len(idx), n_flag
+
+
+def gpu_ngram(ctx, lens, n_max, n_min, K):
+    c = torch.from_numpy(np.ascontiguousarray(ctx, np.int32)).cuda()
+    n = torch.from_numpy(np.ascontiguousarray(lens, np.int32)).cuda()
+    B = c.shape[0]
+    out = dict(tokens=poisoned((B, K), torch.int32), len=poisoned((B,), torch.int32),
+               ngram=poisoned((B,), torch.int32), src=poisoned((B,), torch.int32))
+    sv.spec_ngram_draft(c, n, n_max, n_min, K, out=out)
+    torch.cuda.synchronize()
+    return {k: _np(v) for k, v in out.items()}
+
+
+def compare_ngram(ctx, lens, n_max, n_min, K, gpu, where=""):
+    """Prompt-lookup drafts: every output identical to the oracle's (integer work)."""
+    _assert_no_poison(gpu)
+    ref = oracle.ngram_draft(ctx, lens, n_max, n_min, K)
+    for key, rk in (("len", "length"), ("ngram", "n"), ("src", "src")):
+        bad = np.nonzero(gpu[key] != ref[rk])[0]
+        assert bad.size == 0, f"{key} differs at requests {bad[:8]} {where}"
+    bad = np.nonzero(np.any(gpu["tokens"] != ref["tokens"], axis=1))[0]
+    assert bad.size == 0, f"tokens differ at requests {bad[:8]} {where}"
+    return ref
+
+
+def gpu_point(wl, tokens, lens, T, dev=None, ws=None):
+    dev = dev or upload(wl, with_draft=False)
+    B, K = wl.B, wl.K
+    ws = ws if ws is not None else sv.new_workspace(B, K, wl.V)
+    out = dict(tokens=poisoned((B, K + 1), torch.int32), tau=poisoned((B,), torch.int32),
+               kv_len=poisoned((B,), torch.int32), p=poisoned((B, K), torch.float32),
+               q=poisoned((B, K), torch.float32))
+    x = torch.from_numpy(np.ascontiguousarray(tokens, np.int32)).cuda()
+    n = None if lens is None else torch.from_numpy(np.ascontiguousarray(lens, np.int32)).cuda()
+    sv.spec_verify_point(dev["target"], x, n, dev["uniforms"], dev["kv"], T, ws, out=out)
+    torch.cuda.synchronize()
+    return {k: _np(v) for k, v in out.items()}
+
+
+def compare_point(wl, gpu, tokens, lens, T, requests=None):
+    """Point-mass draft verification: the sampling rules (T > 0) or greedy rules (T = 0) over the
+    first n_b slots; NaN probabilities past n_b; row errors as in the other entry points."""
+    _assert_no_poison(gpu)
+    idx = list(range(wl.B)) if requests is None else list(requests)
+    ref = oracle.verify_point(wl.target, wl.dtype, tokens, lens, wl.uniforms, wl.kv_len, T,
+                              requests=idx)
+    K, V = wl.K, wl.V
+    n_flag = 0
+    for i, b in enumerate(idx):
+        tok, tau, kv = gpu["tokens"][b], int(gpu["tau"][b]), int(gpu["kv_len"][b])
+        nb = K if lens is None else int(lens[b])
+        where = f"request {b} (n={nb}, T={T}, {wl.config.name}, K={K} V={V})"
+        if ref["row_error"][i]:
+            assert tau == -1 and kv == int(ref["kv_out"][i]) and np.all(tok == -1), where
+            assert np.all(np.isnan(gpu["p"][b])) and np.all(np.isnan(gpu["q"][b])), where
+            continue
+        np.testing.assert_allclose(gpu["p"][b], ref["p_x"][i], rtol=0, atol=PROB_ATOL,
+                                   err_msg=where)
+        np.testing.assert_array_equal(gpu["q"][b], ref["q_x"][i], err_msg=where)
+        if ref["flagged"][i]:
+            n_flag += 1
+            assert 1 <= tau <= nb + 1 and np.array_equal(tok[:tau - 1], tokens[b, :tau - 1])
+            assert 0 <= tok[tau - 1] < V and np.all(tok[tau:] == -1), where
+            continue
+        assert tau == int(ref["tau"][i]) and np.array_equal(tok, ref["tokens"][i]), where
+        assert kv == int(ref["kv_out"][i]), where
+    return len(idx), n_flag

@@ -47,6 +47,8 @@ def test_constants_match_header(lib):
     assert sv.SPEC_MAX_F == header_define("SPEC_MAX_F")
     assert sv.SPEC_MAX_V == header_define("SPEC_MAX_V") == 1 << 22
     assert sv.SPEC_DEFAULT_WAIT_POLLS == header_define("SPEC_DEFAULT_WAIT_POLLS")
+    assert sv.SPEC_MAX_NGRAM == header_define("SPEC_MAX_NGRAM")
+    assert sv.SPEC_MAX_CONTEXT == header_define("SPEC_MAX_CONTEXT") == 1 << 30
     for code, name in sv.STATUS.items():
         assert header_define(name) == code
 
@@ -242,6 +244,38 @@ def test_kv_rewind_validation(lib):
         if i == 1 and bad == 1 << 20:
             a[2] = 1 << 12          # B * max_blocks >= 2^31
         assert lib.spec_kv_rewind(*a) == code["SPEC_ERR_ARG"], (i, bad)
+
+
+def test_ngram_draft_validation(lib):
+    code = {v: k for k, v in sv.STATUS.items()}
+    # context, ld, context_len, B, n_max, n_min, K, out_tokens, out_len, out_ngram, out_src, stream
+    args = [FAKE, 4096, FAKE, 2, 4, 1, 4, FAKE, FAKE, NULL, NULL, NULL]
+    for i, bad in [(0, NULL), (2, NULL), (7, NULL), (8, NULL), (1, 0), (1, (1 << 30) + 1),
+                   (3, 0), (4, 0), (4, 65), (5, 0), (5, 5), (6, 0), (6, 65)]:
+        a = list(args)
+        a[i] = bad
+        assert lib.spec_ngram_draft(*a) == code["SPEC_ERR_ARG"], (i, bad)
+
+
+def test_verify_point_validation(lib):
+    code = {v: k for k, v in sv.STATUS.items()}
+
+    def call(**kw):
+        a = dict(t=FAKE, dtype=1, x=FAKE, n=NULL, u=FAKE, kv=NULL, B=2, K=4, V=1000, T=1.0,
+                 tok=FAKE, tau=FAKE, kvo=NULL, p=NULL, q=NULL, ws=FAKE, wsb=0, s=NULL)
+        a.update(kw)
+        return lib.spec_verify_point(a["t"], a["dtype"], a["x"], a["n"], a["u"], a["kv"], a["B"],
+                                     a["K"], a["V"], a["T"], a["tok"], a["tau"], a["kvo"], a["p"],
+                                     a["q"], a["ws"], a["wsb"], a["s"])
+    assert call(dtype=5) == code["SPEC_ERR_DTYPE"]
+    for kw in [dict(B=0), dict(K=0), dict(K=65), dict(V=1), dict(x=NULL), dict(tok=NULL),
+               dict(tau=NULL), dict(t=NULL), dict(t=FAKE_ODD)]:
+        assert call(**kw) == code["SPEC_ERR_ARG"], kw
+    for T in (-1.0, float("nan"), float("inf"), 1e-45):
+        assert call(T=T) == code["SPEC_ERR_TEMPERATURE"], T
+    assert call() == code["SPEC_ERR_WORKSPACE"] and call(T=0.0) == code["SPEC_ERR_WORKSPACE"]
+    wsb = lib.spec_workspace_bytes(2, 4, 1000, 1)
+    assert call(u=NULL, wsb=wsb) == code["SPEC_ERR_ARG"]   # sampling needs the uniforms
 
 
 def test_workspace_init_rejects_bad_pointer(lib):

@@ -8,10 +8,11 @@ import torch
 import oracle
 import speculative_decoding_verification_12_amd as sv
 from gpu_helpers import (announce, compare_fanout, compare_greedy, compare_lookup,
-                         compare_mixed, compare_predict, compare_sample, compare_sample_keys,
-                         dev_logits, gpu_fanout, gpu_greedy, gpu_mixed, gpu_predict, gpu_sample,
+                         compare_mixed, compare_ngram, compare_point, compare_predict,
+                         compare_sample, compare_sample_keys, dev_logits, gpu_fanout, gpu_greedy,
+                         gpu_mixed, gpu_ngram, gpu_point, gpu_predict, gpu_sample,
                          gpu_sample_keys, upload)
-from synthetic import make_tiny_random, make_workload
+from synthetic import make_contexts, make_runs, make_tiny_random, make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -450,3 +451,127 @@ def test_mixed_c3_half_greedy_bit_identical():
     for b in np.nonzero(temps == 0)[0]:
         for k in ("tokens", "tau", "kv_len"):
             assert np.array_equal(greedy[k][b], mixed[k][b]), (b, k)
+
+
+# ------------------------------------------------------------------------------ prompt lookup
+def test_ngram_tiny_random():
+    """Drafts from short random histories over 2-8 symbols (dense matches), with empty, one-token,
+    full-width and invalid lengths, every span length and draft size up to the limits."""
+    for seed in range(40):
+        rng = np.random.default_rng(500 + seed)
+        B, ld = 12, int(rng.integers(1, 300))
+        ctx = rng.integers(0, int(rng.integers(2, 9)), (B, ld)).astype(np.int32)
+        lens = rng.integers(0, ld + 1, B).astype(np.int32)
+        lens[:5] = [0, min(1, ld), ld, -1, ld + 1]
+        n_max = 64 if seed % 10 == 0 else int(rng.integers(1, 9))
+        n_min = int(rng.integers(1, n_max + 1))
+        K = 64 if seed % 10 == 5 else int(rng.integers(1, 9))
+        where = f"seed={seed} ld={ld} n={n_min}..{n_max} K={K}"
+        announce(f"ngram {where}")
+        compare_ngram(ctx, lens, n_max, n_min, K, gpu_ngram(ctx, lens, n_max, n_min, K), where)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_ngram_contexts_full_size(seed):
+    """64 histories of 1k-16k tokens (prompt, then output quoting earlier spans) over a 128256-id
+    vocabulary, spans of 1-4 tokens, 4 drafts; plus one row wider than two passes of the
+    workgroup (40000 tokens)."""
+    ctx, lens = make_contexts(700 + seed, 64, 16384, 1024, 16384, 128256)
+    announce(f"ngram contexts seed={seed}")
+    ref = compare_ngram(ctx, lens, 4, 1, 4, gpu_ngram(ctx, lens, 4, 1, 4), f"seed={seed}")
+    announce(f"ngram contexts: {int(np.sum(ref['length'] > 0))} of 64 matched")
+    wide, wl = make_contexts(710 + seed, 3, 40000, 30000, 40000, 50000)
+    compare_ngram(wide, wl, 8, 2, 16, gpu_ngram(wide, wl, 8, 2, 16), "wide")
+
+
+def test_ngram_runs_and_periods():
+    """Runs of one token and short periods (every position matches the last token, the backward
+    extension runs to n_max everywhere), n_max = 64."""
+    ctx, lens = make_runs(71, 16, 5000, 3)
+    announce("ngram runs")
+    compare_ngram(ctx, lens, 64, 1, 8, gpu_ngram(ctx, lens, 64, 1, 8), "runs")
+    compare_ngram(ctx, lens, 5, 5, 3, gpu_ngram(ctx, lens, 5, 5, 3), "runs n=5")
+
+
+def _point_tokens(wl, lens, rng):
+    """The workload's drafts on the first n_b slots, junk (invalid ids) after them."""
+    x = wl.tokens.copy()
+    for b in range(wl.B):
+        nb = int(lens[b])
+        if 0 <= nb < wl.K:
+            x[b, nb:] = rng.integers(-9, 0, wl.K - nb)
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_point_tiny_random(dtype):
+    """Point-mass drafts with lengths 0..K (and invalid ones) at T = 0 and T > 0 on tiny rows with
+    ties, masked tokens and bad draft tokens."""
+    for seed in range(24):
+        rng = np.random.default_rng(800 + seed)
+        K = 1 + seed % 6
+        V = [2, 3, 5, 8, 40, 129, 1000, 4099][seed % 8]
+        T = [1.0, 0.0, 0.7, 2.5][seed % 4]
+        wl = make_tiny_random(seed, B=10, K=K, V=V, T=max(T, 1.0), dtype=dtype,
+                              ties=seed % 2 == 0, neg_inf=0.2 if seed % 3 else 0.0,
+                              bad_token_rate=0.05 if seed % 4 == 1 else 0.0)
+        lens = rng.integers(0, K + 1, wl.B).astype(np.int32)
+        lens[:4] = [0, K, -1, K + 1]
+        x = _point_tokens(wl, lens, rng)
+        announce(f"point seed={seed} dtype={dtype} K={K} V={V} T={T}")
+        compare_point(wl, gpu_point(wl, x, lens, T), x, lens, T)
+        if seed % 4 == 0:
+            compare_point(wl, gpu_point(wl, wl.tokens, None, T), wl.tokens, None, T)
+
+
+def test_point_c3_full_size():
+    """C3 shapes (64 requests, K = 4, V = 128256, bf16) with lengths 0..K, at T = 1 and T = 0."""
+    wl = make_workload(3, 5)
+    rng = np.random.default_rng(88)
+    lens = rng.integers(0, wl.K + 1, wl.B).astype(np.int32)
+    x = _point_tokens(wl, lens, rng)
+    dev = upload(wl, with_draft=False)
+    for T in (float(wl.T), 0.0):
+        announce(f"C3 point T={T}")
+        n, f = compare_point(wl, gpu_point(wl, x, lens, T, dev=dev), x, lens, T)
+        announce(f"C3 point T={T}: {n} checked, {f} flagged")
+
+
+def test_point_equals_sampling_with_one_hot_drafts():
+    """With every slot drafted, point-mass verification is speculative sampling against one-hot
+    draft rows (0 at x_k, -inf elsewhere): on C3, spec_verify_point and spec_verify_sample make the
+    same decisions and emit the same tokens on every request the oracle does not flag, q is 1 in
+    both, and p agrees to float rounding (the point path cuts its K+1 rows into different chunks,
+    so its row sums are added in another order)."""
+    wl = make_workload(3, 6)
+    dev = upload(wl, with_draft=False)
+    onehot = torch.full((wl.B, wl.K, wl.V), float("-inf"), dtype=torch.bfloat16, device="cuda")
+    onehot.scatter_(2, dev["tokens"].long().unsqueeze(2), 0.0)
+    dev["draft"] = onehot
+    announce("C3 point vs one-hot sampling")
+    plain = gpu_sample(wl, dev=dev)
+    point = gpu_point(wl, wl.tokens, None, float(wl.T), dev=dev)
+    flagged = oracle.verify_point(wl.target, wl.dtype, wl.tokens, None, wl.uniforms, wl.kv_len,
+                                  float(wl.T))["flagged"]
+    ok = ~flagged
+    for k in ("tokens", "tau", "kv_len"):
+        assert np.array_equal(plain[k][ok], point[k][ok]), k
+    assert np.array_equal(plain["q"], point["q"]) and np.all(point["q"] == 1.0)
+    np.testing.assert_allclose(point["p"], plain["p"], rtol=0, atol=1e-6)
+    announce(f"C3 point vs one-hot: {int(flagged.sum())} flagged")
+
+
+def test_ngram_round_on_c3():
+    """A round without a draft model: prompt-lookup drafts from 64 histories, verified against the
+    C3 target rows at T = 1 and T = 0; both steps on the GPU match the oracle's chain."""
+    wl = make_workload(3, 7)
+    ctx, lens = make_contexts(990, wl.B, 8192, 512, 8192, wl.V)
+    announce("round: drafts")
+    d = gpu_ngram(ctx, lens, 4, 1, wl.K)
+    compare_ngram(ctx, lens, 4, 1, wl.K, d, "round")
+    dev = upload(wl, with_draft=False)
+    for T in (float(wl.T), 0.0):
+        announce(f"round: verify T={T}")
+        n, f = compare_point(wl, gpu_point(wl, d["tokens"], d["len"], T, dev=dev), d["tokens"],
+                             d["len"], T)
+        announce(f"round T={T}: {n} checked, {f} flagged")
