@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from synthetic import make_workload  # noqa: E402
+from synthetic import make_contexts, make_workload  # noqa: E402
 
 METRIC = "verified draft rows/sec and HBM GB/s (% of peak), B=64 K=4 V=128256 bf16"
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E, published
@@ -468,6 +468,64 @@ def secondary(sv, torch, dev, hip, sets, dsets, ws, args):
     stop.record()
     torch.cuda.synchronize()
     res["kv_rewind_c3"] = dict(block_size=bs, ms_per_call=round(start.elapsed_time(stop) / steps, 5))
+
+    # a round without a draft model: prompt-lookup drafts from 64 histories of 1k-16k tokens
+    # (prompt, then output quoting earlier spans), then verification of those drafts against the
+    # C3 target rows at C3's temperature and at T = 0
+    log("prompt-lookup drafts and point-mass verification")
+    ctx_np, lens_np = make_contexts(4242, B, 16384, 1024, 16384, V)
+    ctx, lens = torch.from_numpy(ctx_np).to(dev), torch.from_numpy(lens_np).to(dev)
+    outd = dict(tokens=torch.empty((B, K), dtype=torch.int32, device=dev),
+                len=torch.empty(B, dtype=torch.int32, device=dev),
+                ngram=torch.empty(B, dtype=torch.int32, device=dev),
+                src=torch.empty(B, dtype=torch.int32, device=dev))
+
+    def timed(fn):
+        for i in range(10):
+            fn(i)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            fn(i)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps
+
+    ms = timed(lambda i: sv.spec_ngram_draft(ctx, lens, 4, 1, K, out=outd))
+    dl = outd["len"].cpu().numpy()
+    res["ngram_draft_64x16k"] = dict(ms_per_call=round(ms, 5), n_max=4, n_min=1, K=K,
+                                     context_tokens=int(lens_np.sum()),
+                                     matched=int((dl > 0).sum()),
+                                     mean_draft_len=round(float(dl.mean()), 3))
+    outp = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                tau=torch.empty(B, dtype=torch.int32, device=dev),
+                kv_len=torch.empty(B, dtype=torch.int32, device=dev),
+                p=torch.empty((B, K), dtype=torch.float32, device=dev),
+                q=torch.empty((B, K), dtype=torch.float32, device=dev))
+    pb = int(((dl + 1) * V * 2).sum())
+    rp = dict(bytes_per_call=pb, mean_draft_len=round(float(dl.mean()), 3))
+    for name, T in (("T", float(wl0.T)), ("T0", 0.0)):
+        ms = timed(lambda i: sv.spec_verify_point(dsets[i % len(dsets)]["t"], outd["tokens"],
+                                                  outd["len"], dsets[i % len(dsets)]["u"],
+                                                  dsets[i % len(dsets)]["kv"], T, ws, out=outp))
+        rp[f"{name}_ms_per_call"] = round(ms, 5)
+        rp[f"{name}_hbm_gbps"] = round(pb / (ms * 1e-3) / 1e9, 1)
+    ms = timed(lambda i: (sv.spec_ngram_draft(ctx, lens, 4, 1, K, out=outd),
+                          sv.spec_verify_point(dsets[i % len(dsets)]["t"], outd["tokens"],
+                                               outd["len"], dsets[i % len(dsets)]["u"],
+                                               dsets[i % len(dsets)]["kv"], float(wl0.T), ws,
+                                               out=outp)))
+    rp["round_T_ms_per_call"] = round(ms, 5)
+    res["point_verify_c3_lookup_drafts"] = rp
+    # every slot drafted: the same bytes as greedy, against the C3 sampling call's (2K+1) rows
+    fb = B * (K + 1) * V * 2
+    ms = timed(lambda i: sv.spec_verify_point(dsets[i % len(dsets)]["t"], dsets[i % len(dsets)]["x"],
+                                              None, dsets[i % len(dsets)]["u"],
+                                              dsets[i % len(dsets)]["kv"], float(wl0.T), ws,
+                                              out=outp))
+    res["point_verify_c3_full_K"] = dict(ms_per_call=round(ms, 5), bytes_per_call=fb,
+                                         rows_per_s=round(B * K / (ms * 1e-3), 1),
+                                         hbm_gbps=round(fb / (ms * 1e-3) / 1e9, 1))
 
     vb = B * (2 * K + 1) * V * 2
     r5 = res["sample_keys_c5"]
