@@ -76,11 +76,10 @@ SV_HD inline KernelPlan point_plan(int B, int K, int V, int epv) {
 SV_HD inline KernelPlan greedy_plan(int B, int K, int V, int epv) {
   return plan_rows(B * (K + 1), V, epv, kGreedyResident);
 }
-// outcome keys: a lane issues all its loads of a chunk at once (kPredictPasses rounds of
-// kVecPerThread vectors); each wave of a chunk publishes its own candidates and statistics for
-// its slot's merge
-constexpr int kPredictPasses = 2;
-constexpr int kPredictVecs = kPassVecs * kPredictPasses;
+// outcome keys: chunks of at most kPredictVecs vectors, so that even a batch that would fill the
+// GPU once with larger chunks runs in several rounds and the workgroups' arithmetic overlaps the
+// loads of others
+constexpr int kPredictVecs = 1024;
 SV_HD inline KernelPlan predict_plan(int B, int K, int V, int epv) {
   return plan_rows(B * K, V, epv, kPredictResident, kPredictVecs);
 }
@@ -108,9 +107,8 @@ struct WsLayout {
   size_t part_stats; // 8 B [B*(2K+1)*nchunk] (point drafts: [B*(K+1)*nchunk]): chunk (max, sum)
   size_t part_draw;  // 16 B [B*nchunk]: published chunk (residual mass, target mass)
   size_t part_greedy;// 8 B [B*(K+1)*nchunk]: chunk (max, lowest index)
-  size_t part_topf;  // 8 B [B*K*nchunk*4*kWaveSlots]: each wave's candidate list
-  size_t part_pcnt;  // 4 B [B*K*nchunk*4]: entries in each wave's list
-  size_t part_pstat; // 8 B [B*K*nchunk*4]: each wave's (max, scaled sum)
+  size_t part_pred;  // 8 B [B*K*nchunk]: outcome keys, chunk (max, scaled sum)
+  size_t part_pwm;   // 4 B [B*K*nchunk*4]: outcome keys, wave maxima
   size_t part_vwm;   // 4 B [B*K*nchunk*4]: wave maxima of the draft rows (outcome keys)
   size_t part_vrow;  // 16 B [B*K]: merged draft-row statistics for the key probabilities
   size_t total;
@@ -149,12 +147,10 @@ inline WsLayout ws_layout(int B, int K, int V, int F) {
   off = align256(off + 16 * b * nd);
   L.part_greedy = off;
   off = align256(off + 8 * b * (k + 1) * ng);
-  L.part_topf = off;
-  off = align256(off + 8 * b * k * np * 4 * 16);
-  L.part_pcnt = off;
+  L.part_pred = off;
+  off = align256(off + 8 * b * k * np);
+  L.part_pwm = off;
   off = align256(off + 4 * b * k * np * 4);
-  L.part_pstat = off;
-  off = align256(off + 8 * b * k * np * 4);
   L.part_vwm = off;
   off = align256(off + 4 * b * k * ns * 4);
   L.part_vrow = off;
