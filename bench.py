@@ -58,7 +58,7 @@ def parse():
 
 # ------------------------------------------------------------------------------ counter traffic
 COUNTERS_MD = os.path.join(ROOT, "profiles", "sample_verify_c3_hbm_counters.md")
-KERNEL_SOURCES = ("verify_sample.hip", "spec_common.hpp", "plan.hpp")
+KERNEL_SOURCES = ("verify_sample.hip", "row_keys.hpp", "spec_common.hpp", "plan.hpp")
 
 
 def kernel_source_hash():
