@@ -170,6 +170,26 @@ def test_max_lookahead_k64():
     compare_predict(wl, gpu_predict(wl, 16, 1.0), 16, 1.0)
 
 
+@pytest.mark.parametrize("cid", [1, 2])
+def test_max_vocabulary(cid):
+    """V = SPEC_MAX_V (2^22): the most draw chunks a row can have (1024 for f32 rows), with the
+    sampling, greedy, outcome-key and point-mass paths; K = 64 point-mass drafts of every length."""
+    V = sv.SPEC_MAX_V
+    wl = make_workload(cid, 9, B=2, K=2, V=V)
+    announce(f"V={V} {wl.dtype}")
+    compare_sample(wl, gpu_sample(wl))
+    wg = make_workload(cid, 9, "greedy", B=2, K=2, V=V)
+    compare_greedy(wg, gpu_greedy(wg))
+    compare_predict(wl, gpu_predict(wl, 4, 1.0), 4, 1.0)
+    lens = np.array([0, 2], np.int32)
+    compare_point(wl, gpu_point(wl, wl.tokens, lens, float(wl.T)), wl.tokens, lens, float(wl.T))
+    w64 = make_workload(2, 8, B=4, K=64, V=3001)
+    lens = np.array([0, 1, 37, 64], np.int32)
+    announce("point K=64")
+    for T in (float(w64.T), 0.0):
+        compare_point(w64, gpu_point(w64, w64.tokens, lens, T), w64.tokens, lens, T)
+
+
 @pytest.mark.parametrize("offset", [1, 3])
 def test_misaligned_base_pointer(offset):
     """Logit tensors whose first element is not 16-byte aligned."""
