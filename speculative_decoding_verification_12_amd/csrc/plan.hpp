@@ -69,9 +69,11 @@ SV_HD inline KernelPlan draw_plan(int B, int K, int V, int epv) {
   const int nvec = V / epv > 0 ? V / epv : 1;
   return KernelPlan{kBlock * kDrawVecs, ceil_div(nvec, kBlock * kDrawVecs)};
 }
-// point-mass drafts: the statistics pass streams only the K+1 target rows
+// point-mass drafts: the statistics pass streams only the K+1 target rows, in chunks of at most
+// one pass of the block (16 KiB of bf16) so that even a batch that would fill the GPU once with
+// larger chunks runs in several rounds (measured faster: the pass has no per-workgroup handshake)
 SV_HD inline KernelPlan point_plan(int B, int K, int V, int epv) {
-  return plan_rows(B * (K + 1), V, epv, kStatsResident);
+  return plan_rows(B * (K + 1), V, epv, kStatsResident, kPassVecs);
 }
 SV_HD inline KernelPlan greedy_plan(int B, int K, int V, int epv) {
   return plan_rows(B * (K + 1), V, epv, kGreedyResident);
