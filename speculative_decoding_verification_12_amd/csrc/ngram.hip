@@ -14,9 +14,10 @@
 // r_e >= n_min: a maximum over positions, packed as the 64-bit key (r_e << 32) | e.
 //
 // One workgroup of 1024 threads per request (a context is a few KiB to a few hundred KiB of
-// token ids, a latency-bound read): every thread tests 8 positions per pass with all 8 first-
-// token loads in flight, extends the rare matches backwards from the cache, and the workgroup
-// reduces the keys; wave 0 then copies the draft.
+// token ids, a latency-bound read). The context goes through LDS in tiles of 8192 positions
+// (plus the n_max tokens before each tile), all of a tile's loads in flight at once, the span's
+// tokens loaded with the first tile; every thread tests 8 positions of a tile and extends the
+// rare matches backwards in LDS; the workgroup reduces the keys and wave 0 copies the draft.
 #include "api_common.hpp"
 #include "spec_common.hpp"
 
@@ -25,7 +26,10 @@ namespace {
 
 constexpr int kLookupBlock = 1024;
 constexpr int kLookupWaves = kLookupBlock / kWave;
-constexpr int kLookupPer = 8;   // positions a thread tests per pass
+constexpr int kLookupPer = 8;                                // positions a thread tests per tile
+constexpr int kLookupTile = kLookupBlock * kLookupPer;      // positions per tile
+constexpr int kLookupHalo = SPEC_MAX_NGRAM;                 // tokens kept before a tile
+constexpr int kLookupLoads = (kLookupHalo + kLookupTile + kLookupBlock - 1) / kLookupBlock;
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
 #pragma unroll
@@ -42,7 +46,8 @@ __global__ __launch_bounds__(kLookupBlock) void ngram_draft_kernel(
     const int32_t* __restrict__ ctx, long long ld, const int32_t* __restrict__ lens, int n_max,
     int n_min, int K, int32_t* __restrict__ out_tok, int32_t* __restrict__ out_len,
     int32_t* __restrict__ out_n, int32_t* __restrict__ out_src) {
-  __shared__ int s_suf[SPEC_MAX_NGRAM];   // s_suf[i] = ctx[L-1-i]
+  __shared__ int s_suf[SPEC_MAX_NGRAM];                  // s_suf[i] = ctx[L-1-i]
+  __shared__ int s_ctx[kLookupHalo + kLookupTile];       // s_ctx[i] = ctx[e0 - halo + i]
   __shared__ unsigned long long s_best[kLookupWaves];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
@@ -50,25 +55,34 @@ __global__ __launch_bounds__(kLookupBlock) void ngram_draft_kernel(
   const int L = lens[b];
   const bool ok = L >= 0 && static_cast<long long>(L) <= ld;   // else a row error
   const int nsuf = ok ? min(n_max, L) : 0;
-  if (tid < nsuf) s_suf[tid] = row[L - 1 - tid];
-  __syncthreads();
 
   unsigned long long best = 0ull;   // 0: no allowed match
-  if (ok && L >= 2) {
-    const int last = s_suf[0];
-    for (int base = 1; base < L; base += kLookupBlock * kLookupPer) {
-      int prev[kLookupPer];
+  if (ok && L >= 2) {               // uniform
+    // the span's own tokens, issued together with the first tile's loads
+    const int sv = row[L - 1 - min(tid, nsuf - 1)];
+    for (int e0 = 1; e0 < L; e0 += kLookupTile) {   // uniform
+      int v[kLookupLoads];
 #pragma unroll
-      for (int i = 0; i < kLookupPer; ++i) {   // clamped so every load is issued at once
-        const int e = base + i * kLookupBlock + tid;
-        prev[i] = row[min(e, L - 1) - 1];
+      for (int i = 0; i < kLookupLoads; ++i) {   // clamped: every load is issued at once
+        const int g = e0 - kLookupHalo + i * kLookupBlock + tid;
+        v[i] = row[min(max(g, 0), L - 1)];
       }
+      __syncthreads();   // the previous tile is no longer read
+      if (e0 == 1 && tid < nsuf) s_suf[tid] = sv;
 #pragma unroll
-      for (int i = 0; i < kLookupPer; ++i) {
-        const int e = base + i * kLookupBlock + tid;
-        if (e < L && prev[i] == last) {
-          int r = 1;
-          while (r < n_max && r < e && row[e - 1 - r] == s_suf[r]) ++r;
+      for (int i = 0; i < kLookupLoads; ++i) {
+        const int li = i * kLookupBlock + tid;
+        if (li < kLookupHalo + kLookupTile) s_ctx[li] = v[i];
+      }
+      __syncthreads();
+      const int last = s_suf[0];
+#pragma unroll
+      for (int j = 0; j < kLookupPer; ++j) {
+        const int e = e0 + j * kLookupBlock + tid;   // continuation start tested
+        const int li = e - e0 + kLookupHalo;          // s_ctx index of ctx[e]
+        if (e < L && s_ctx[li - 1] == last) {
+          int r = 1;   // ctx[e-1-r] sits at s_ctx[li-1-r], r < n_max <= halo
+          while (r < n_max && r < e && s_ctx[li - 1 - r] == s_suf[r]) ++r;
           const unsigned long long key =
               (static_cast<unsigned long long>(r) << 32) | static_cast<unsigned>(e);
           if (r >= n_min && key > best) best = key;
