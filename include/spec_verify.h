@@ -153,9 +153,10 @@ int spec_verify_sample_ex(const void* target_logits, const void* draft_logits, i
  *                 ordered by logit descending then id ascending (x_k skipped when asked);
  *   out_key_prob  [B,K,F] float (nullable): q_k(key) at the call's temperature, from the same
  *                 row statistics as out_q.
- * Three launches (statistics, draw, key merge; the merge re-reads only the parts of the draft
- * rows that can hold a key, from the wave maxima the statistics pass keeps); errors as for
- * spec_verify_sample, SPEC_ERR_ARG also for F out of range or a null out_keys. */
+ * Two launches, as spec_verify_sample: the statistics pass also keeps every draft-row wave's
+ * maximum, and the draw's grid has one more workgroup per draft slot that selects the slot's
+ * keys while the draw runs (re-reading only the parts of the draft row that can hold a key);
+ * errors as for spec_verify_sample, SPEC_ERR_ARG also for F out of range or a null out_keys. */
 int spec_verify_sample_keys(const void* target_logits, const void* draft_logits, int dtype,
                             const int32_t* draft_tokens, const float* uniforms,
                             const int32_t* kv_len_in, int B, int K, int V, float temperature,

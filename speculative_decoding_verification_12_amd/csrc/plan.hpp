@@ -112,7 +112,6 @@ struct WsLayout {
   size_t part_pred;  // 8 B [B*K*nchunk]: outcome keys, chunk (max, scaled sum)
   size_t part_pwm;   // 4 B [B*K*nchunk*4]: outcome keys, wave maxima
   size_t part_vwm;   // 4 B [B*K*nchunk*4]: wave maxima of the draft rows (outcome keys)
-  size_t part_vrow;  // 16 B [B*K]: merged draft-row statistics for the key probabilities
   size_t total;
 };
 
@@ -155,8 +154,6 @@ inline WsLayout ws_layout(int B, int K, int V, int F) {
   off = align256(off + 4 * b * k * np * 4);
   L.part_vwm = off;
   off = align256(off + 4 * b * k * ns * 4);
-  L.part_vrow = off;
-  off = align256(off + 16 * b * k);
   L.total = off;
   return L;
 }

@@ -25,6 +25,8 @@
 //     token, from the values still in its registers. A workgroup that has polled for a mass too
 //     long computes that chunk's mass itself (bit for bit what its owner publishes), so no
 //     workgroup ever waits on one that has not been scheduled.
+// With outcome keys (kKeys) the statistics pass also keeps the draft rows' wave maxima, and the
+// draw's grid has one more workgroup per draft slot that selects the slot's keys meanwhile.
 #include <hip/hip_ext.h>
 
 #include "api_common.hpp"
@@ -368,28 +370,48 @@ struct KeyArgs {
   int exclude;         // skip the draft token
   int cv_s;            // statistics chunk size (vectors)
   const float* wave_max;   // [B,K,nchunk_s,4]: the statistics pass's wave maxima of draft rows
-  RowStat* row_stats;      // [B,K]: the draw's merged draft-row statistics
   int32_t* out_keys;       // [B,K,F]
   float* out_prob;         // [B,K,F] or null
 };
 
-// One workgroup of kMergeWaves waves per (request, draft slot): select_keys over the draft row.
-constexpr int kMergeWaves = 8;
+// A row's (max, sum) from its n chunk partials pr[0..n), merged by an aligned group of W lanes
+// (W a power of two; lane i of the group holds chunks i, i + W, ...): every lane of the group
+// gets the same bits, wherever the group sits in the wave. has = false (a group without a row)
+// gives (-inf, 0).
+__device__ __forceinline__ void merge_row_stats(const float2* pr, bool has, int n, int W, int i,
+                                                float c, float& Mr, double& Sr) {
+  constexpr int kHeld = 4;   // chunks a lane keeps in registers between the two passes
+  float hm[kHeld], hs[kHeld];
+  float lm = -INFINITY;
+#pragma unroll
+  for (int h = 0; h < kHeld; ++h) {
+    const int j = i + h * W;
+    const float2 q = (has && j < n) ? pr[j] : make_float2(-INFINITY, 0.f);
+    hm[h] = q.x;
+    hs[h] = q.y;
+    lm = fmaxf(lm, hm[h]);
+  }
+  if (has)
+    for (int j = i + kHeld * W; j < n; j += W) lm = fmaxf(lm, pr[j].x);
+  Mr = group_reduce(lm, W, OpMax{});
+  const float mc = Mr * c;
+  double ls = 0.0;
+#pragma unroll
+  for (int h = 0; h < kHeld; ++h)
+    if (hm[h] > -INFINITY) ls += static_cast<double>(hs[h]) * fast_exp2(hm[h] * c - mc);
+  if (has)
+    for (int j = i + kHeld * W; j < n; j += W) {
+      const float2 q = pr[j];
+      if (q.x > -INFINITY) ls += static_cast<double>(q.y) * fast_exp2(q.x * c - mc);
+    }
+  Sr = group_reduce(ls, W, OpAdd{});
+}
 
-template <typename TIn>
-__global__ __launch_bounds__(kMergeWaves * kWave) void keys_merge_kernel(const TIn* __restrict__ drf,
-                                                            const int32_t* __restrict__ xtok,
-                                                            int K, int V, float c, int nchunk_s,
-                                                            KeyArgs ka) {
-  const size_t bk = blockIdx.x;   // b * K + k
-  // loaded first; used only at the end
-  const int xk = ka.exclude ? xtok[bk] : -1;
-  const RowStat rs = ka.row_stats[bk];
-  select_keys<TIn, kMergeWaves, false>(
-      drf + bk * static_cast<size_t>(V), V, nchunk_s, ka.cv_s,
-      ka.wave_max + bk * static_cast<size_t>(nchunk_s * kWaves), ka.pick, ka.F, xk,
-      [&]() { return rs; }, c, ka.out_keys + bk * ka.F,
-      ka.out_prob ? ka.out_prob + bk * ka.F : nullptr);
+// the group width the merges use for rows of n chunks
+__device__ __forceinline__ int merge_width(int n) {
+  int W = 1;
+  while (W < n && W < kWave) W <<= 1;
+  return W;
 }
 
 // Chunks of kBlock * kDrawVecs vectors (see draw_plan). cm holds the published (R, P) of every
@@ -402,7 +424,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     int nchunk, int cv, uint64_t* __restrict__ cm, int wait_polls,
     int32_t* __restrict__ out_tok, int32_t* __restrict__ out_tau, int32_t* __restrict__ out_kv,
     float* __restrict__ out_p, float* __restrict__ out_q, KeyArgs ka,
-    const float* __restrict__ temps, const int32_t* __restrict__ dlen) {
+    const float* __restrict__ temps, const int32_t* __restrict__ dlen, int n_draw) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
   __shared__ double s_red[2][kWaves];
@@ -414,6 +436,33 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
   __shared__ float row_m[2 * SPEC_MAX_K + 1];
   __shared__ double row_s[2 * SPEC_MAX_K + 1];
   __shared__ ReqState s_st;
+
+  if constexpr (kKeys) {
+    // ---- the workgroups past the draw's select one draft slot's outcome keys each, alongside
+    // the draw (they wait on nothing). The slot's row statistics are merged by wave 0 exactly as
+    // the draw merges them (same group width, same lanes' chunks), so q_k(key) uses the same
+    // (M, S) bits as out_q.
+    if (static_cast<int>(blockIdx.x) >= n_draw) {
+      const size_t bk = blockIdx.x - n_draw;   // b * K + k
+      const int kb = static_cast<int>(bk / K), kk = static_cast<int>(bk % K);
+      const int lane = threadIdx.x & (kWave - 1);
+      const int xk = ka.exclude ? xtok[bk] : -1;
+      const float2* pr = part_s + (static_cast<size_t>(kb) * (2 * K + 1) + K + 1 + kk) * nchunk_s;
+      const int Wk = merge_width(nchunk_s);
+      auto row_stat = [&]() {
+        float Mr;
+        double Sr;
+        merge_row_stats(pr, lane < Wk, nchunk_s, Wk, lane % Wk, c_call, Mr, Sr);
+        return RowStat{readlane_f32(Mr, 0), 0.f, readlane_f64(Sr, 0)};
+      };
+      select_keys<TIn, kWaves, false>(drf + bk * static_cast<size_t>(V), V, nchunk_s, ka.cv_s,
+                                      ka.wave_max + bk * static_cast<size_t>(nchunk_s * kWaves),
+                                      ka.pick, ka.F, xk, row_stat, c_call,
+                                      ka.out_keys + bk * ka.F,
+                                      ka.out_prob ? ka.out_prob + bk * ka.F : nullptr);
+      return;
+    }
+  }
 
   const int b = blockIdx.x / nchunk;
   const int ch = blockIdx.x % nchunk;
@@ -503,37 +552,14 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     // Rows are merged in groups of W lanes (W = nchunk_s rounded up to a power of two, at most
     // 64), 64/W rows per wave, so one pass over the block issues every partial load at once.
     // Lanes past nchunk_s (or past the last row) carry (-inf, 0).
-    int W = 1;
-    while (W < nchunk_s && W < kWave) W <<= 1;
+    const int W = merge_width(nchunk_s);
     const int per_wave = kWave / W, g = lane / W, i = lane % W;
     for (int base = 0; base < rows; base += kWaves * per_wave) {
       const int rr = base + w * per_wave + g;
       const float2* pr = part_s + (static_cast<size_t>(b) * rows + (rr < rows ? rr : 0)) * nchunk_s;
-      constexpr int kHeld = 4;   // chunks a lane keeps in registers between the two passes
-      float hm[kHeld], hs[kHeld];
-      float lm = -INFINITY;
-#pragma unroll
-      for (int h = 0; h < kHeld; ++h) {
-        const int j = i + h * W;
-        const float2 q = (rr < rows && j < nchunk_s) ? pr[j] : make_float2(-INFINITY, 0.f);
-        hm[h] = q.x;
-        hs[h] = q.y;
-        lm = fmaxf(lm, hm[h]);
-      }
-      if (rr < rows)
-        for (int j = i + kHeld * W; j < nchunk_s; j += W) lm = fmaxf(lm, pr[j].x);
-      const float Mr = group_reduce(lm, W, OpMax{});
-      const float mc = Mr * c;
-      double ls = 0.0;
-#pragma unroll
-      for (int h = 0; h < kHeld; ++h)
-        if (hm[h] > -INFINITY) ls += static_cast<double>(hs[h]) * fast_exp2(hm[h] * c - mc);
-      if (rr < rows)
-        for (int j = i + kHeld * W; j < nchunk_s; j += W) {
-          const float2 q = pr[j];
-          if (q.x > -INFINITY) ls += static_cast<double>(q.y) * fast_exp2(q.x * c - mc);
-        }
-      const double Sr = group_reduce(ls, W, OpAdd{});
+      float Mr;
+      double Sr;
+      merge_row_stats(pr, rr < rows, nchunk_s, W, i, c, Mr, Sr);
       if (i == 0 && rr < rows) {
         row_m[rr] = Mr;
         row_s[rr] = Sr;
@@ -564,10 +590,6 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       const int mm = rej ? (__ffsll(static_cast<long long>(rej)) - 1) : nb;
       const int xm = __shfl(xk, mm < nb ? mm : 0, kWave);   // the rejected draft token
       if (ch == 0) {   // one workgroup of the request writes everything but the drawn token
-        if constexpr (kKeys)   // the draft rows' statistics, for the key probabilities
-          if (valid)
-            ka.row_stats[static_cast<size_t>(b) * K + lane] =
-                RowStat{row_m[K + 1 + lane], 0.f, row_s[K + 1 + lane]};
         if (lane < K) {   // slots past the request's drafts report NaN
           const size_t o = static_cast<size_t>(b) * K + lane;
           if (out_p) out_p[o] = (err || !valid) ? NAN : static_cast<float>(pk);
@@ -809,7 +831,9 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
                     hipStream_t stream, hipEvent_t* ev, int wait_polls, const SamplePlan& P,
                     const KeyRequest& kr, const float* temps, const int32_t* dlen = nullptr) {
   const size_t g1 = static_cast<size_t>(B) * (kPoint ? K + 1 : 2 * K + 1) * P.stats.nchunk;
-  const size_t g2 = static_cast<size_t>(B) * P.draw.nchunk;
+  const size_t n_draw = static_cast<size_t>(B) * P.draw.nchunk;
+  // with keys, one more workgroup per draft slot selects that slot's keys during the draw
+  const size_t g2 = n_draw + (kKeys ? static_cast<size_t>(B) * K : 0);
   if (!grid_fits(g1) || !grid_fits(g2) || P.draw.cv != kBlock * kDrawVecs ||
       P.draw.nchunk > kMaxDrawChunks)
     return SPEC_ERR_ARG;
@@ -821,24 +845,20 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
   float* gath = ws_ptr<float>(ws, L.gathered);
   uint64_t* cm = ws_ptr<uint64_t>(ws, L.part_draw);
   float* kwmax = ws_ptr<float>(ws, L.part_vwm);
-  const int nclear = static_cast<int>(g2 * 2);
+  const int nclear = static_cast<int>(n_draw * 2);
   const dim3 grid1(static_cast<unsigned>(g1)), grid2(static_cast<unsigned>(g2)), block(kBlock);
   const int ns = P.stats.nchunk, cs = P.stats.cv, nd = P.draw.nchunk, cd = P.draw.cv;
   const int polls = wait_polls < 0 ? SPEC_DEFAULT_WAIT_POLLS : wait_polls;
   const int pick = kr.F + (kr.exclude ? 1 : 0);
-  RowStat* krows = ws_ptr<RowStat>(ws, L.part_vrow);
-  const KeyArgs ka{pick, kr.F, kr.exclude, cs, kwmax, krows, kr.out_keys, kr.out_prob};
-  const dim3 grid3(static_cast<unsigned>(static_cast<size_t>(B) * K));
+  const KeyArgs ka{pick, kr.F, kr.exclude, cs, kwmax, kr.out_keys, kr.out_prob};
+  const int nd_wg = static_cast<int>(n_draw);
   if (ev == nullptr) {
     hipLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0, stream, t, d,
                        xtok, K, V, c, ns, cs, part1, gath, cm, nclear, kwmax, temps, dlen);
     hipLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint>), grid2, block, 0, stream, t, d,
                        xtok, uni, kv_in, K, V, c, ns, static_cast<const float2*>(part1),
                        static_cast<const float*>(gath), nd, cd, cm, polls, out_tok, out_tau,
-                       out_kv, out_p, out_q, ka, temps, dlen);
-    if constexpr (kKeys)
-      hipLaunchKernelGGL(keys_merge_kernel<TIn>, grid3, dim3(kMergeWaves * kWave), 0, stream, d,
-                         xtok, K, V, c, ns, ka);
+                       out_kv, out_p, out_q, ka, temps, dlen, nd_wg);
   } else {
     // profiling: the runtime records the events at each kernel's start and end
     hipExtLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0, stream,
@@ -848,10 +868,7 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
                           ev[2], ev[3], 0, t, d, xtok, uni, kv_in, K, V, c, ns,
                           static_cast<const float2*>(part1), static_cast<const float*>(gath), nd,
                           cd, cm, polls, out_tok, out_tau, out_kv, out_p, out_q, ka, temps,
-                          dlen);
-    if constexpr (kKeys)
-      hipLaunchKernelGGL(keys_merge_kernel<TIn>, grid3, dim3(kMergeWaves * kWave), 0, stream, d,
-                         xtok, K, V, c, ns, ka);
+                          dlen, nd_wg);
   }
   return launch_status();
 }
