@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=4, help="rotated input sets")
-    ap.add_argument("--cpu-repeats", type=int, default=16,
+    ap.add_argument("--cpu-repeats", type=int, default=32,
                     help="passes of the oracle over the 64 requests of set 0")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-secondary", action="store_true",
