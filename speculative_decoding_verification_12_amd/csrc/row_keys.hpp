@@ -57,7 +57,7 @@ __device__ __forceinline__ void thread_chunk_stats(const TIn* row, const RowSpan
 #pragma unroll
     for (int i = 0; i < kVecPerThread; ++i) {
       const int vi = base + i * kBlock + tid;
-      q[i] = vi < cr.vend ? vrow[vi] : neg_inf_vec<TIn>();
+      q[i] = vi < cr.vend ? load_stream(vrow, vi) : neg_inf_vec<TIn>();
     }
     float v[kVecPerThread * N];
 #pragma unroll

@@ -73,6 +73,14 @@ __device__ __forceinline__ uint4 neg_inf_vec() {
   return make_uint4(w, w, w, w);
 }
 
+// Vector i of a logit row read once in a streaming pass: a non-temporal load (the `nt` hint),
+// since the pass does not come back to it (measured ~1 % faster on the sampling call).
+__device__ __forceinline__ uint4 load_stream(const uint4* p, int i) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p) + i);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // 2^x on the hardware exponential unit (results below 2^-126 may flush to zero, which is far
 // below the resolution any sum here can see)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -48,7 +48,7 @@ __device__ __forceinline__ void greedy_chunk(const TIn* __restrict__ tgt, int rb
 #pragma unroll
     for (int i = 0; i < kVecPerThread; ++i) {
       const int vi = base + i * kBlock + tid;
-      q[i] = vi < cr.vend ? vrow[vi] : neg_inf_vec<TIn>();
+      q[i] = vi < cr.vend ? load_stream(vrow, vi) : neg_inf_vec<TIn>();
     }
 #pragma unroll
     for (int i = 0; i < kVecPerThread; ++i) {
