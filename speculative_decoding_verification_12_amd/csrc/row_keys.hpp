@@ -36,7 +36,10 @@ __device__ __forceinline__ void absorb(const float (&v)[n], float c, float& m, f
 
 // One thread's share of chunk `cr`: scalar head/tail elements, then passes of
 // kVecPerThread vectors, all loads of a pass issued before any arithmetic.
-template <typename TIn, bool kSum = true>
+// kNT reads the vectors with non-temporal loads. Whether that pays depends on what reads the rows
+// again afterwards (the draw's re-read of row m, the key selection's re-read of a few waves); it
+// is chosen per pass from measurements.
+template <typename TIn, bool kSum = true, bool kNT = false>
 __device__ __forceinline__ void thread_chunk_stats(const TIn* row, const RowSpan& sp,
                                                    const ChunkRange& cr, int V, float c,
                                                    float& m, float& s) {
@@ -57,7 +60,10 @@ __device__ __forceinline__ void thread_chunk_stats(const TIn* row, const RowSpan
 #pragma unroll
     for (int i = 0; i < kVecPerThread; ++i) {
       const int vi = base + i * kBlock + tid;
-      q[i] = vi < cr.vend ? load_stream(vrow, vi) : neg_inf_vec<TIn>();
+      if constexpr (kNT)
+        q[i] = vi < cr.vend ? load_stream(vrow, vi) : neg_inf_vec<TIn>();
+      else
+        q[i] = vi < cr.vend ? vrow[vi] : neg_inf_vec<TIn>();
     }
     float v[kVecPerThread * N];
 #pragma unroll

@@ -179,7 +179,9 @@ __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
   }
 
   float m, s, M, S;
-  thread_chunk_stats(row, sp, cr, V, c, m, s);
+  // non-temporal loads for the plain and keys passes (measured faster); the mixed and point-mass
+  // passes measured faster with ordinary loads
+  thread_chunk_stats<TIn, true, !kMixed && !kPoint>(row, sp, cr, V, c, m, s);
   // with outcome keys, a draft row's waves also keep their maxima (they bound where the row's
   // top tokens can be; the key merge re-reads only the waves that can hold one)
   float* wmax = (kKeys && r > K)
