@@ -73,10 +73,11 @@ __device__ __forceinline__ uint4 neg_inf_vec() {
   return make_uint4(w, w, w, w);
 }
 
-// Vector i of a logit row read with a non-temporal load (the `nt` hint). It is used where it
-// measured faster: greedy verification (~4 %, its rows are read once), the plain and keys
-// sampling statistics; the mixed, point-mass and outcome-key statistics passes measured faster
-// with ordinary loads (what reads their rows again afterwards then hits the caches).
+// Vector i of a logit row read with a non-temporal load (the `nt` hint), for passes after which
+// nothing reads the row again: greedy verification (measured ~4 % faster) and the greedy rows of
+// mixed batches. The statistics passes keep ordinary loads: the draw's re-read of row m (and
+// the key selection's re-read of a few waves) then hits the caches, which measured faster for
+// the whole call even though the statistics pass alone is ~2 us slower.
 __device__ __forceinline__ uint4 load_stream(const uint4* p, int i) {
   typedef unsigned int v4u __attribute__((ext_vector_type(4)));
   const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p) + i);

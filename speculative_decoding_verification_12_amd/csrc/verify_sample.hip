@@ -179,9 +179,9 @@ __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
   }
 
   float m, s, M, S;
-  // non-temporal loads for the plain and keys passes (measured faster); the mixed and point-mass
-  // passes measured faster with ordinary loads
-  thread_chunk_stats<TIn, true, !kMixed && !kPoint>(row, sp, cr, V, c, m, s);
+  // ordinary loads: the draw re-reads row m right after this pass, and a non-temporal pass made
+  // that re-read miss the caches (the whole call measured ~1 us slower)
+  thread_chunk_stats<TIn, true, false>(row, sp, cr, V, c, m, s);
   // with outcome keys, a draft row's waves also keep their maxima (they bound where the row's
   // top tokens can be; the key merge re-reads only the waves that can hold one)
   float* wmax = (kKeys && r > K)
