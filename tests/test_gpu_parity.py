@@ -268,6 +268,74 @@ def test_draw_help_path_bit_identical(cid, B, V, rnd):
     compare_sample(wl, h, requests=range(min(wl.B, 16)))
 
 
+def _same_bits(a, b):
+    for k in a:
+        assert np.array_equal(a[k].view(np.int32), b[k].view(np.int32)), k
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace serves calls of other shapes and inputs in turn: partial results and
+    published masses left by an earlier call sit where a later call of another shape looks, and
+    must never be taken for its own. Every call must equal a call on a fresh workspace, also
+    with a zero poll budget (every draw workgroup then computes each chunk mass it does not find
+    already published)."""
+    shapes = [(16, 40000, 41), (5, 12345, 42), (16, 40000, 43), (3, 40000, 44), (16, 999, 45),
+              (11, 40000, 46)]
+    ws = sv.new_workspace(16, 4, 40000)
+    for B, V, rnd in shapes:
+        wl = make_workload(3, rnd, B=B, V=V)
+        dev = upload(wl)
+        announce(f"workspace reuse B={B} V={V}")
+        ref = gpu_sample(wl, dev=dev, ws=sv.new_workspace(B, wl.K, V))
+        for polls in (None, 0):
+            _same_bits(ref, gpu_sample(wl, dev=dev, ws=ws, wait_polls=polls))
+        compare_sample(wl, ref)
+
+
+def test_graph_capture_replays():
+    """Captured into a HIP graph (no memset node: the draw's published-mass words are cleared
+    by the statistics kernel's own stores), every replay after new inputs are copied in equals
+    an eager call on them, with eager calls on the same workspace between the replays."""
+    wls = [make_workload(3, 50 + i, B=8, V=40000) for i in range(3)]
+    devs = [upload(w) for w in wls]
+    ws = sv.new_workspace(8, 4, 40000)
+    eager = [gpu_sample(w, dev=d, ws=sv.new_workspace(8, 4, 40000)) for w, d in zip(wls, devs)]
+    static = {k: v.clone() for k, v in devs[0].items()}
+    out = dict(tokens=torch.empty((8, 5), dtype=torch.int32, device="cuda"),
+               tau=torch.empty(8, dtype=torch.int32, device="cuda"),
+               kv_len=torch.empty(8, dtype=torch.int32, device="cuda"),
+               p=torch.empty((8, 4), dtype=torch.float32, device="cuda"),
+               q=torch.empty((8, 4), dtype=torch.float32, device="cuda"))
+    T = float(wls[0].T)
+
+    def call():
+        sv.spec_verify_sample(static["target"], static["draft"], static["tokens"],
+                              static["uniforms"], static["kv"], T, ws, out=out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    announce("graph capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for r, i in enumerate([1, 0, 2, 2, 1]):
+        for k in static:
+            static[k].copy_(devs[i][k])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy() for k, v in out.items()}
+        announce(f"  replay {r} (input set {i})")
+        _same_bits(eager[i], got)
+        # an eager call on the same workspace between replays
+        _same_bits(eager[i], gpu_sample(wls[i], dev=devs[i], ws=ws))
+
+
 # ------------------------------------------------------------------------------ the five configs
 def _rounds_sample(cid, rounds, mode):
     tot = flag = flag_bad = 0
