@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the greedy and outcome-key timings")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the C1/C2 latency, C4 throughput and C5 hit-rate figures")
+    ap.add_argument("--no-c4", action="store_true",
+                    help="skip C4 (its 1.32 GB input takes ~30 s to generate on the host)")
     ap.add_argument("--calib-mib", type=int, default=256,
                     help="size of one plain device-to-device copy run before timing; under "
                          "rocprofv3 --pmc its FETCH_SIZE/WRITE_SIZE calibrate the counters")
@@ -268,6 +272,8 @@ def main():
 
     if not args.no_secondary:
         extra.update(secondary(sv, torch, dev, hip, sets, dsets, ws, args))
+    if not args.no_configs:
+        extra.update(other_configs(sv, torch, dev, args))
 
     for i in range(n_ev):
         hip.hipEventDestroy(evs[i])
@@ -300,6 +306,149 @@ def main():
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def other_configs(sv, torch, dev, args):
+    """The other workloads' own figures: C1 and C2 per-call latency (one request each; device
+    time between events around every call, and host wall time of a launch-and-wait), C4
+    throughput with its share of bonus-path requests, and the C5 outcome-key hit rates."""
+    res = {}
+    steps = max(50, args.steps)
+
+    def upload(w):
+        if w.dtype == "bf16":
+            lg = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        else:
+            lg = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        return dict(t=lg(w.target), d=lg(w.draft), x=torch.from_numpy(w.tokens).to(dev),
+                    u=torch.from_numpy(w.uniforms).to(dev),
+                    kv=torch.from_numpy(w.kv_len).to(dev))
+
+    def outputs(B, K):
+        return dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                    tau=torch.empty(B, dtype=torch.int32, device=dev),
+                    kv_len=torch.empty(B, dtype=torch.int32, device=dev),
+                    p=torch.empty((B, K), dtype=torch.float32, device=dev),
+                    q=torch.empty((B, K), dtype=torch.float32, device=dev))
+
+    def latency(fn, n_sets):
+        """Per call: device us between events around it, and host wall us of launch + wait."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(20):
+            fn(i % n_sets)
+        torch.cuda.synchronize()
+        wall = []
+        for i in range(steps):
+            t0 = time.perf_counter()
+            ev[i][0].record()
+            fn(i % n_sets)
+            ev[i][1].record()
+            ev[i][1].synchronize()
+            wall.append((time.perf_counter() - t0) * 1e6)
+        dev_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        wall = np.array(wall)
+        return dict(device_us_median=round(float(np.median(dev_us)), 2),
+                    device_us_p90=round(float(np.percentile(dev_us, 90)), 2),
+                    wall_us_median=round(float(np.median(wall)), 2),
+                    wall_us_p90=round(float(np.percentile(wall, 90)), 2))
+
+    # ---- C1 (fp32, V=1000) and C2 (bf16, V=32000): one request per call
+    for cid, name in ((1, "c1_tiny"), (2, "c2_latency")):
+        log(f"C{cid} per-call latency")
+        n_sets = 64
+        wls = [make_workload(cid, r) for r in range(n_sets)]
+        ds = [upload(w) for w in wls]
+        B, K, V = wls[0].B, wls[0].K, wls[0].V
+        ws = sv.new_workspace(B, K, V)
+        out = outputs(B, K)
+        T = float(wls[0].T)
+
+        def samp(i):
+            s = ds[i]
+            sv.spec_verify_sample(s["t"], s["d"], s["x"], s["u"], s["kv"], T, ws, out=out)
+
+        def greedy(i):
+            s = ds[i]
+            sv.spec_verify_greedy(s["t"], s["x"], s["kv"], ws, out=out)
+
+        res[name] = dict(B=B, K=K, V=V, dtype=wls[0].dtype, T=T,
+                         sample_warm=latency(samp, 1), sample_rotated=latency(samp, n_sets),
+                         greedy_warm=latency(greedy, 1), greedy_rotated=latency(greedy, n_sets),
+                         rotated_sets=n_sets)
+
+    # ---- C4: B=256, K=8, V=152064 bf16, T=1; even requests accept every draft (bonus path).
+    # One input set of 1.32 GB, five times the Infinity Cache, so calls cannot hit it.
+    if not args.no_c4:
+        log("C4 large batch (generating 1.32 GB of logits on the host)")
+        w4 = make_workload(4, 0)
+        d4 = upload(w4)
+        B, K, V = w4.B, w4.K, w4.V
+        ws = sv.new_workspace(B, K, V)
+        out = outputs(B, K)
+        T = float(w4.T)
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n4 = max(20, args.steps // 4)
+        for fn_name in ("sample", "greedy"):
+            def fn():
+                if fn_name == "sample":
+                    sv.spec_verify_sample(d4["t"], d4["d"], d4["x"], d4["u"], d4["kv"], T, ws,
+                                          out=out)
+                else:
+                    sv.spec_verify_greedy(d4["t"], d4["x"], d4["kv"], ws, out=out)
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            start.record()
+            for _ in range(n4):
+                fn()
+            stop.record()
+            torch.cuda.synchronize()
+            ms = start.elapsed_time(stop) / n4
+            nbytes = B * ((2 * K + 1) if fn_name == "sample" else (K + 1)) * V * 2
+            tau = out["tau"].cpu().numpy()
+            res.setdefault("c4_large", dict(B=B, K=K, V=V, T=T))[fn_name] = dict(
+                ms_per_call=round(ms, 5), rows_per_s=round(B * K / (ms * 1e-3), 1),
+                bytes_per_call=nbytes, hbm_gbps=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                frac_of_hbm_peak=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                bonus_path_share=round(float(np.mean(tau == K + 1)), 4),
+                mean_tau=round(float(tau.mean()), 3))
+        del d4
+
+    # ---- C5 hit rates: keys (F=3, every slot, draft token kept) against the outcome of the
+    # verification of the same round; a round is a hit when a draft was rejected (a < K) and
+    # the placed token is one of slot a's keys (all-kept rounds have no key: misses)
+    log("C5 outcome-key hit rates")
+    F = 3
+    for mode, Tm in (("sample", 1.0), ("greedy", 0.0)):
+        hits = rej = tot = 0
+        for r in range(4):
+            w5 = make_workload(5, r, mode)
+            d5 = upload(w5)
+            B, K, V = w5.B, w5.K, w5.V
+            ws = sv.new_workspace(B, K, V, F)
+            out = outputs(B, K)
+            if mode == "sample":
+                sv.spec_verify_sample(d5["t"], d5["d"], d5["x"], d5["u"], d5["kv"], Tm, ws,
+                                      out=out)
+            else:
+                sv.spec_verify_greedy(d5["t"], d5["x"], d5["kv"], ws, out=out)
+            keys = sv.spec_predict_outcomes(d5["d"], F, Tm, ws)["keys"]
+            torch.cuda.synchronize()
+            tau = out["tau"].cpu().numpy()
+            tok = out["tokens"].cpu().numpy()
+            kk = keys.cpu().numpy()
+            for b in range(B):
+                a = int(tau[b]) - 1
+                tot += 1
+                if a < K:
+                    rej += 1
+                    hits += int(tok[b, a] in kk[b, a])
+        res[f"c5_hit_rate_T{Tm:g}"] = dict(rounds=4, requests=tot, hit_rate=round(hits / tot, 4),
+                                           hit_rate_rejected_rounds=round(hits / max(rej, 1), 4),
+                                           F=F, draft_token_skipped=False)
+    return res
 
 
 def secondary(sv, torch, dev, hip, sets, dsets, ws, args):
