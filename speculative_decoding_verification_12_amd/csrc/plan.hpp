@@ -52,6 +52,9 @@ SV_HD inline KernelPlan plan_rows(int rows, int V, int epv, int resident, int ma
   return KernelPlan{cv, ceil_div(nvec, cv)};
 }
 
+// MI355X's Infinity Cache (the memory-side cache in front of HBM), bytes
+constexpr long long kInfinityCacheBytes = 256ll << 20;
+
 // workgroups per CU at once, from the compiler's resource report for gfx950
 constexpr int kStatsResident = 8;
 constexpr int kGreedyResident = 8;

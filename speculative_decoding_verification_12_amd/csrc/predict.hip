@@ -58,10 +58,12 @@ __global__ __launch_bounds__(kBlock) void predict_stats_kernel(const TIn* __rest
   const RowSpan sp = row_span(row, V);
   const ChunkRange cr = chunk_range(sp, ch, nchunk, cv);
   float m, s, M, S;
+  // non-temporal loads: afterwards only the few waves that can hold a key are read again
+  // (measured ~1 us faster per C5 call than ordinary loads)
   if (c > 0.f)
-    thread_chunk_stats<TIn, true>(row, sp, cr, V, c, m, s);
+    thread_chunk_stats<TIn, true, true>(row, sp, cr, V, c, m, s);
   else
-    thread_chunk_stats<TIn, false>(row, sp, cr, V, c, m, s);
+    thread_chunk_stats<TIn, false, true>(row, sp, cr, V, c, m, s);
   const size_t pc = static_cast<size_t>(rk) * nchunk + ch;
   block_stats(m, s, c, sm, ss, M, S, wmax + pc * kWaves);
   if (threadIdx.x == 0) part[pc] = make_float2(M, S);

@@ -74,10 +74,10 @@ __device__ __forceinline__ uint4 neg_inf_vec() {
 }
 
 // Vector i of a logit row read with a non-temporal load (the `nt` hint), for passes after which
-// nothing reads the row again: greedy verification (measured ~4 % faster) and the greedy rows of
-// mixed batches. The statistics passes keep ordinary loads: the draw's re-read of row m (and
-// the key selection's re-read of a few waves) then hits the caches, which measured faster for
-// the whole call even though the statistics pass alone is ~2 us slower.
+// little or nothing of the row is read again: greedy verification (measured ~4 % faster), the
+// greedy rows of mixed batches, the outcome-key statistics pass, and the sampling statistics
+// pass when the call's rows exceed the Infinity Cache. Below that size the sampling statistics
+// pass keeps ordinary loads, so the draw's re-read of row m hits the cache.
 __device__ __forceinline__ uint4 load_stream(const uint4* p, int i) {
   typedef unsigned int v4u __attribute__((ext_vector_type(4)));
   const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p) + i);
