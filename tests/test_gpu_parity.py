@@ -170,6 +170,27 @@ def test_max_lookahead_k64():
     compare_predict(wl, gpu_predict(wl, 16, 1.0), 16, 1.0)
 
 
+def test_many_small_requests():
+    """A batch of 1500 short requests (V = 300): grids of thousands of workgroups with one chunk
+    per row, thousands of per-request arrival counters and published-mass slots, request-major
+    indexing far past one round of workgroups; sampling, greedy, keys and keys with
+    verification, every request against the oracle."""
+    B, K, V = 1500, 3, 300
+    wl = make_workload(3, 61, B=B, K=K, V=V)
+    dev = upload(wl)
+    ws = sv.new_workspace(B, K, V, 4)
+    announce(f"many requests B={B} K={K} V={V}")
+    plain = gpu_sample(wl, dev=dev, ws=ws)
+    compare_sample(wl, plain)
+    wg = make_workload(3, 61, "greedy", B=B, K=K, V=V)
+    compare_greedy(wg, gpu_greedy(wg, ws=ws))
+    compare_predict(wl, gpu_predict(wl, 4, 0.7, dev=dev, ws=ws), 4, 0.7)
+    g = gpu_sample_keys(wl, 3, True, dev=dev, ws=ws)
+    compare_sample_keys(wl, g, 3, True)
+    for k in plain:
+        assert np.array_equal(plain[k].view(np.int32), g[k].view(np.int32)), k
+
+
 @pytest.mark.parametrize("cid", [1, 2])
 def test_max_vocabulary(cid):
     """V = SPEC_MAX_V (2^22): the most draw chunks a row can have (1024 for f32 rows), with the
