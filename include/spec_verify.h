@@ -36,12 +36,16 @@
  *     keeps no mutable global state; calls only enqueue work on `stream` and return. Outputs
  *     are valid after the stream is synchronised. Every element of every non-null output is
  *     written.
- *   - Workspace: size from spec_workspace_bytes(B,K,V,F) (one size serves all three entry
- *     points), 256-byte aligned, zeroed once by spec_workspace_init before its first use. Each
- *     call leaves it ready for the next one (the completion counters it holds are reset on the
- *     device, and the sampling draw's published-mass words are cleared by the same call's
- *     streaming pass before the draw reads them). One workspace must not be used by two calls that may run concurrently (two
- *     streams, or two host threads on one stream without ordering): they would race.
+ *   - Workspace: size from spec_workspace_bytes(B,K,V,F) (one size serves every entry point),
+ *     256-byte aligned, zeroed once by spec_workspace_init before its first use. Each call
+ *     leaves it ready for the next one: the arrival counters it holds are reset on the device,
+ *     and the sampling draw's published-mass words are cleared by the same call's streaming
+ *     pass before the draw reads them. The counters live in the workspace's first half and
+ *     every other region in its second, so one workspace serves calls of any shapes whose
+ *     counters and data each fit in a half (a workspace sized for the largest B, K, V a caller
+ *     uses does; a call that does not fit returns SPEC_ERR_WORKSPACE). One workspace must not
+ *     be used by two calls that may run concurrently (two streams, or two host threads on one
+ *     stream without ordering): they would race.
  *   - Errors found on the host are returned synchronously, before anything is enqueued:
  *       SPEC_ERR_ARG         null required pointer, B < 1, K < 1 or K > SPEC_MAX_K, V < 2
  *                            or V > SPEC_MAX_V,
@@ -50,8 +54,8 @@
  *       SPEC_ERR_DTYPE       dtype not SPEC_F32 / SPEC_BF16;
  *       SPEC_ERR_TEMPERATURE sampling with T not finite or T <= 0 (or log2(e)/T not finite);
  *                            greedy with T != 0; prediction with T < 0 or not finite;
- *       SPEC_ERR_WORKSPACE   workspace null, smaller than spec_workspace_bytes, or not
- *                            256-byte aligned;
+ *       SPEC_ERR_WORKSPACE   workspace null, not 256-byte aligned, or too small for this
+ *                            call's counters and data (spec_workspace_bytes is always enough);
  *       SPEC_ERR_HIP         a launch failed (hipGetLastError after enqueueing).
  *   - Errors in device data are reported per request ("row error"): a draft token outside
  *     [0,V), or, when sampling, a draft token whose draft logit is -inf (it cannot be a sample

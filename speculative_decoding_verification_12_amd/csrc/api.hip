@@ -29,7 +29,7 @@ extern "C" const char* spec_status_string(int status) {
 
 extern "C" size_t spec_workspace_bytes(int B, int K, int V, int F) {
   if (sv::check_dims(B, K, V) != SPEC_OK || F < 1 || F > SPEC_MAX_F || F > V) return 0;
-  return sv::ws_layout(B, K, V, F).total;
+  return sv::ws_layout(B, K, V, F, 0).total;
 }
 
 extern "C" int spec_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {

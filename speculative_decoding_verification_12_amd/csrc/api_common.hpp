@@ -32,7 +32,7 @@ inline int check_logits(const void* p, int dtype) {
 }
 
 inline int check_workspace(const void* ws, size_t bytes, int B, int K, int V, int F) {
-  if (ws == nullptr || !is_aligned(ws, 256) || bytes < ws_layout(B, K, V, F).total)
+  if (ws == nullptr || !is_aligned(ws, 256) || !ws_layout(B, K, V, F, bytes).fits)
     return SPEC_ERR_WORKSPACE;
   return SPEC_OK;
 }
@@ -58,6 +58,6 @@ inline T* ws_ptr(void* ws, size_t off) {
 int greedy_point_entry(const void* target, int dtype, const int32_t* xtok, const int32_t* dlen,
                        const int32_t* kv_in, int B, int K, int V, int32_t* out_tok,
                        int32_t* out_tau, int32_t* out_kv, float* out_p, float* out_q, void* ws,
-                       hipStream_t stream);
+                       size_t ws_bytes, hipStream_t stream);
 
 }  // namespace sv

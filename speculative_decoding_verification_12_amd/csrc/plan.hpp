@@ -115,7 +115,9 @@ struct WsLayout {
   size_t part_pred;  // 8 B [B*K*nchunk]: outcome keys, chunk (max, scaled sum)
   size_t part_pwm;   // 4 B [B*K*nchunk*4]: outcome keys, wave maxima
   size_t part_vwm;   // 4 B [B*K*nchunk*4]: wave maxima of the draft rows (outcome keys)
-  size_t total;
+  size_t data_end;   // end of the last data region
+  size_t total;      // bytes this shape needs: twice the larger of counters and data
+  bool fits;         // the caller's workspace holds this shape's counters and data
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -126,8 +128,14 @@ inline size_t max_chunks(PlanFn fn, int B, int K, int V) {
   return static_cast<size_t>(a > b ? a : b);
 }
 
-// Layout covering both element types.
-inline WsLayout ws_layout(int B, int K, int V, int F) {
+// Layout covering both element types. The workspace is cut in two halves: the arrival counters
+// live in the first, every other region in the second. Counters are zero between calls (each
+// call resets the ones it used) and nothing else is ever written in the first half, so one
+// workspace can serve calls of different shapes in turn: no call writes data where a call of
+// another shape keeps a counter. `ws_bytes` is the caller's workspace size; `total`, the size
+// this shape needs, does not depend on it.
+inline WsLayout ws_layout(int B, int K, int V, int F, size_t ws_bytes) {
+  (void)F;   // the keys go to the caller's outputs
   const size_t b = static_cast<size_t>(B), k = static_cast<size_t>(K);
   const size_t ns = max_chunks(stats_plan, B, K, V);
   const size_t npt = max_chunks(point_plan, B, K, V);
@@ -142,22 +150,35 @@ inline WsLayout ws_layout(int B, int K, int V, int F) {
   L.cnt_b = off;
   off = align256(off + sizeof(unsigned) * stride * b);
   L.counters_end = off;
-  L.gathered = off;
-  off = align256(off + sizeof(float) * 2 * b * k);
-  L.part_stats = off;
-  off = align256(off + 8 * (b * (2 * k + 1) * ns > b * (k + 1) * npt ? b * (2 * k + 1) * ns
-                                                                      : b * (k + 1) * npt));
-  L.part_draw = off;
-  off = align256(off + 16 * b * nd);
-  L.part_greedy = off;
-  off = align256(off + 8 * b * (k + 1) * ng);
-  L.part_pred = off;
-  off = align256(off + 8 * b * k * np);
-  L.part_pwm = off;
-  off = align256(off + 4 * b * k * np * 4);
-  L.part_vwm = off;
-  off = align256(off + 4 * b * k * ns * 4);
-  L.total = off;
+  // data regions, first relative to the start of the second half
+  size_t d = 0;
+  L.gathered = d;
+  d = align256(d + sizeof(float) * 2 * b * k);
+  L.part_stats = d;
+  d = align256(d + 8 * (b * (2 * k + 1) * ns > b * (k + 1) * npt ? b * (2 * k + 1) * ns
+                                                                  : b * (k + 1) * npt));
+  L.part_draw = d;
+  d = align256(d + 16 * b * nd);
+  L.part_greedy = d;
+  d = align256(d + 8 * b * (k + 1) * ng);
+  L.part_pred = d;
+  d = align256(d + 8 * b * k * np);
+  L.part_pwm = d;
+  d = align256(d + 4 * b * k * np * 4);
+  L.part_vwm = d;
+  d = align256(d + 4 * b * k * ns * 4);
+  const size_t need_half = L.counters_end > d ? L.counters_end : d;
+  L.total = 2 * need_half;
+  const size_t half = (ws_bytes / 2) & ~static_cast<size_t>(255);
+  L.fits = L.counters_end <= half && half + d <= ws_bytes;
+  L.gathered += half;
+  L.part_stats += half;
+  L.part_draw += half;
+  L.part_greedy += half;
+  L.part_pred += half;
+  L.part_pwm += half;
+  L.part_vwm += half;
+  L.data_end = half + d;
   return L;
 }
 

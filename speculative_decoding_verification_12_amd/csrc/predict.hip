@@ -111,13 +111,13 @@ __global__ __launch_bounds__(kSelectWaves * kWave) void predict_select_kernel(
 template <typename TIn>
 int launch_predict(const void* draft, const int32_t* xtok, int B, int K, int V,
                    const FanoutTable& ft, float T, int32_t* out_keys, float* out_prob, void* ws,
-                   hipStream_t stream) {
+                   size_t ws_bytes, hipStream_t stream) {
   // chunking as for all K slots of every request, so the workspace sized by
   // spec_workspace_bytes(B, K, V, .) covers any P <= K
   const KernelPlan P = predict_plan(B, K, V, 16 / static_cast<int>(sizeof(TIn)));
   const size_t g = static_cast<size_t>(B) * ft.P * P.nchunk;
   if (!grid_fits(g)) return SPEC_ERR_ARG;
-  const WsLayout L = ws_layout(B, K, V, 1);
+  const WsLayout L = ws_layout(B, K, V, 1, ws_bytes);
   const float c = T > 0.f ? exp2_scale(T) : 0.f;
   float2* part = ws_ptr<float2>(ws, L.part_pred);
   float* wm = ws_ptr<float>(ws, L.part_pwm);
@@ -145,12 +145,12 @@ int check_predict_common(const void* draft_logits, int dtype, int B, int K, int 
 
 int run_predict(const void* draft_logits, int dtype, const int32_t* xtok, int B, int K, int V,
                 const FanoutTable& ft, float temperature, int32_t* out_keys, float* out_key_prob,
-                void* workspace, hipStream_t stream) {
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (dtype == SPEC_BF16)
     return launch_predict<uint16_t>(draft_logits, xtok, B, K, V, ft, temperature, out_keys,
-                                    out_key_prob, workspace, stream);
+                                    out_key_prob, workspace, workspace_bytes, stream);
   return launch_predict<float>(draft_logits, xtok, B, K, V, ft, temperature, out_keys,
-                               out_key_prob, workspace, stream);
+                               out_key_prob, workspace, workspace_bytes, stream);
 }
 
 // Builds the per-slot table; false when a fan-out is out of range.
@@ -217,7 +217,7 @@ extern "C" int spec_predict_outcomes(const void* draft_logits, int dtype, int B,
   FanoutTable ft;
   if (!fanout_table(fan, K, false, V, ft)) return SPEC_ERR_ARG;
   return run_predict(draft_logits, dtype, nullptr, B, K, V, ft, temperature, out_keys,
-                     out_key_prob, workspace, stream);
+                     out_key_prob, workspace, workspace_bytes, stream);
 }
 
 extern "C" int spec_predict_fanout(const void* draft_logits, int dtype,
@@ -233,7 +233,7 @@ extern "C" int spec_predict_fanout(const void* draft_logits, int dtype,
   if (!fanout_table(fanout, P, draft_tokens != nullptr, V, ft)) return SPEC_ERR_ARG;
   if ((rc = check_workspace(workspace, workspace_bytes, B, K, V, 1)) != SPEC_OK) return rc;
   return run_predict(draft_logits, dtype, draft_tokens, B, K, V, ft, temperature, out_keys,
-                     out_key_prob, workspace, stream);
+                     out_key_prob, workspace, workspace_bytes, stream);
 }
 
 extern "C" int spec_outcome_lookup(const int32_t* tau, const int32_t* tokens,

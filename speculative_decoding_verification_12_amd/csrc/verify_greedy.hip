@@ -166,11 +166,12 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
 template <typename TIn>
 int launch_greedy(const void* target, const int32_t* xtok, const int32_t* kv_in, int B, int K,
                   int V, int32_t* out_tok, int32_t* out_tau, int32_t* out_kv, void* ws,
-                  hipStream_t stream, const KernelPlan& P, const int32_t* dlen = nullptr,
+                  size_t ws_bytes, hipStream_t stream, const KernelPlan& P,
+                  const int32_t* dlen = nullptr,
                   float* out_p = nullptr, float* out_q = nullptr) {
   const size_t g = static_cast<size_t>(B) * (K + 1) * P.nchunk;
   if (!grid_fits(g)) return SPEC_ERR_ARG;
-  const WsLayout L = ws_layout(B, K, V, 1);
+  const WsLayout L = ws_layout(B, K, V, 1, ws_bytes);
   hipLaunchKernelGGL(greedy_kernel<TIn>, dim3(static_cast<unsigned>(g)), dim3(kBlock), 0, stream,
                      static_cast<const TIn*>(target), xtok, kv_in, K, V, P.nchunk, P.cv,
                      ws_ptr<ArgPart>(ws, L.part_greedy), ws_ptr<unsigned>(ws, L.cnt_a), out_tok,
@@ -183,12 +184,12 @@ int launch_greedy(const void* target, const int32_t* xtok, const int32_t* kv_in,
 int greedy_point_entry(const void* target, int dtype, const int32_t* xtok, const int32_t* dlen,
                        const int32_t* kv_in, int B, int K, int V, int32_t* out_tok,
                        int32_t* out_tau, int32_t* out_kv, float* out_p, float* out_q, void* ws,
-                       hipStream_t stream) {
+                       size_t ws_bytes, hipStream_t stream) {
   if (dtype == SPEC_BF16)
     return launch_greedy<uint16_t>(target, xtok, kv_in, B, K, V, out_tok, out_tau, out_kv, ws,
-                                   stream, greedy_plan(B, K, V, 8), dlen, out_p, out_q);
-  return launch_greedy<float>(target, xtok, kv_in, B, K, V, out_tok, out_tau, out_kv, ws, stream,
-                              greedy_plan(B, K, V, 4), dlen, out_p, out_q);
+                                   ws_bytes, stream, greedy_plan(B, K, V, 8), dlen, out_p, out_q);
+  return launch_greedy<float>(target, xtok, kv_in, B, K, V, out_tok, out_tau, out_kv, ws,
+                              ws_bytes, stream, greedy_plan(B, K, V, 4), dlen, out_p, out_q);
 }
 }  // namespace sv
 
@@ -208,8 +209,9 @@ extern "C" int spec_verify_greedy(const void* target_logits, int dtype,
   if ((rc = check_workspace(workspace, workspace_bytes, B, K, V, 1)) != SPEC_OK) return rc;
   if (dtype == SPEC_BF16)
     return launch_greedy<uint16_t>(target_logits, draft_tokens, kv_len_in, B, K, V, out_tokens,
-                                   out_tau, out_kv_len, workspace, stream,
+                                   out_tau, out_kv_len, workspace, workspace_bytes, stream,
                                    greedy_plan(B, K, V, 8));
   return launch_greedy<float>(target_logits, draft_tokens, kv_len_in, B, K, V, out_tokens,
-                              out_tau, out_kv_len, workspace, stream, greedy_plan(B, K, V, 4));
+                              out_tau, out_kv_len, workspace, workspace_bytes, stream,
+                              greedy_plan(B, K, V, 4));
 }

@@ -386,21 +386,23 @@ struct KeyArgs {
 // (W a power of two; lane i of the group holds chunks i, i + W, ...): every lane of the group
 // gets the same bits, wherever the group sits in the wave. has = false (a group without a row)
 // gives (-inf, 0).
-__device__ __forceinline__ void merge_row_stats(const float2* pr, bool has, int n, int W, int i,
-                                                float c, float& Mr, double& Sr) {
+// `rd(j)` returns chunk j's (max, sum).
+template <typename Rd>
+__device__ __forceinline__ void merge_row_stats_rd(Rd rd, bool has, int n, int W, int i, float c,
+                                                   float& Mr, double& Sr) {
   constexpr int kHeld = 4;   // chunks a lane keeps in registers between the two passes
   float hm[kHeld], hs[kHeld];
   float lm = -INFINITY;
 #pragma unroll
   for (int h = 0; h < kHeld; ++h) {
     const int j = i + h * W;
-    const float2 q = (has && j < n) ? pr[j] : make_float2(-INFINITY, 0.f);
+    const float2 q = (has && j < n) ? rd(j) : make_float2(-INFINITY, 0.f);
     hm[h] = q.x;
     hs[h] = q.y;
     lm = fmaxf(lm, hm[h]);
   }
   if (has)
-    for (int j = i + kHeld * W; j < n; j += W) lm = fmaxf(lm, pr[j].x);
+    for (int j = i + kHeld * W; j < n; j += W) lm = fmaxf(lm, rd(j).x);
   Mr = group_reduce(lm, W, OpMax{});
   const float mc = Mr * c;
   double ls = 0.0;
@@ -409,10 +411,15 @@ __device__ __forceinline__ void merge_row_stats(const float2* pr, bool has, int 
     if (hm[h] > -INFINITY) ls += static_cast<double>(hs[h]) * fast_exp2(hm[h] * c - mc);
   if (has)
     for (int j = i + kHeld * W; j < n; j += W) {
-      const float2 q = pr[j];
+      const float2 q = rd(j);
       if (q.x > -INFINITY) ls += static_cast<double>(q.y) * fast_exp2(q.x * c - mc);
     }
   Sr = group_reduce(ls, W, OpAdd{});
+}
+
+__device__ __forceinline__ void merge_row_stats(const float2* pr, bool has, int n, int W, int i,
+                                                float c, float& Mr, double& Sr) {
+  merge_row_stats_rd([pr](int j) { return pr[j]; }, has, n, W, i, c, Mr, Sr);
 }
 
 // the group width the merges use for rows of n chunks
@@ -420,6 +427,262 @@ __device__ __forceinline__ int merge_width(int n) {
   int W = 1;
   while (W < n && W < kWave) W <<= 1;
   return W;
+}
+
+// ------------------------------------------------------------------------------ draw phases
+// LDS of a workgroup drawing one chunk of row m.
+struct DrawShared {
+  double s_red[2][kWaves];
+  double2 s_cm[kMaxDrawChunks];            // every chunk's (residual mass, target mass)
+  int s_first[kWaves];
+  uint32_t s_raw[2][4 * kDrawVecs];        // one thread's target and draft vectors
+  int s_cs, s_usep, s_fallback;
+  double s_cb, s_t;
+  float row_m[2 * SPEC_MAX_K + 1];
+  double row_s[2 * SPEC_MAX_K + 1];
+  ReqState s_st;
+};
+
+// Chunk masses published with the sign bit of each float64 word as the "written" flag; the
+// words are zeroed by the statistics kernel of the same call, before the draw kernel starts.
+struct FlaggedMasses {
+  uint64_t* cm;   // [nchunk][2] of one request
+  __device__ void publish(int j, double R, double P) const {
+    store_coherent(&cm[2 * j], dbits(R) | kWrittenBit);
+    store_coherent(&cm[2 * j + 1], dbits(P) | kWrittenBit);
+  }
+  __device__ bool poll(int j, int polls, double& R, double& P) const {
+    return poll_mass(&cm[2 * j], polls, R, P);
+  }
+};
+
+// Wave 0 of a draw workgroup of request b, from the merged row statistics in sh.row_m/row_s and
+// each lane's slot (lane k < nb: draft token xk, uniform uk, gathered target and draft logits
+// lt, ld): every slot's acceptance ratio, the first rejection m by ballot; chunk 0 writes tau,
+// kv, the kept tokens, p and q. The draw's state goes to sh.s_st (m = -1 for a row error).
+template <bool kPoint>
+__device__ __forceinline__ void decide_slots(int b, int ch, int K, int V, float c, int nb,
+                                             bool nb_bad, bool valid, int xk, float uk, float lt,
+                                             float ld, int kv0, DrawShared& sh,
+                                             int32_t* __restrict__ out_tok,
+                                             int32_t* __restrict__ out_tau,
+                                             int32_t* __restrict__ out_kv,
+                                             float* __restrict__ out_p,
+                                             float* __restrict__ out_q) {
+  const int lane = threadIdx.x & (kWave - 1);
+  // a draft token must be a token the draft could have sampled
+  const bool bad = valid && (xk < 0 || xk >= V || (!kPoint && ld == -INFINITY));
+  bool keep = true;
+  double pk = 0.0, qk = 0.0;
+  if (valid && !bad) {
+    // p_k(x_k) and q_k(x_k): 2^(l*c - fl(M*c)) / S of each row; a point-mass draft has
+    // q_k(x_k) = 1
+    pk = exp2_wide(static_cast<double>(lt) * c - static_cast<double>(sh.row_m[lane] * c)) /
+         sh.row_s[lane];
+    if constexpr (kPoint)
+      qk = 1.0;
+    else
+      qk = exp2_wide(static_cast<double>(ld) * c -
+                     static_cast<double>(sh.row_m[K + 1 + lane] * c)) /
+           sh.row_s[K + 1 + lane];
+    // kept iff u < min(1, p/q): p >= q is kept for every u in [0,1)
+    keep = pk >= qk || static_cast<double>(uk) < pk / qk;
+  }
+  const bool err = nb_bad || __ballot(bad) != 0ull;
+  const unsigned long long rej = __ballot(valid && !keep);
+  const int mm = rej ? (__ffsll(static_cast<long long>(rej)) - 1) : nb;
+  const int xm = __shfl(xk, mm < nb ? mm : 0, kWave);   // the rejected draft token
+  if (ch == 0) {   // one workgroup of the request writes everything but the drawn token
+    if (lane < K) {   // slots past the request's drafts report NaN
+      const size_t o = static_cast<size_t>(b) * K + lane;
+      if (out_p) out_p[o] = (err || !valid) ? NAN : static_cast<float>(pk);
+      if (out_q) out_q[o] = (err || !valid) ? NAN : static_cast<float>(qk);
+    }
+    for (int j = lane; j <= K; j += kWave)
+      if (err || j != mm) out_tok[static_cast<size_t>(b) * (K + 1) + j] = (!err && j < mm) ? xk : -1;
+    if (lane == 0) {
+      out_tau[b] = err ? -1 : mm + 1;
+      if (out_kv) out_kv[b] = err ? kv0 : kv0 + mm + 1;
+    }
+  }
+  if (lane == 0) {
+    ReqState st;
+    st.m = err ? -1 : mm;
+    st.xm = (kPoint && mm < nb) ? xm : -1;
+    st.mc_t = sh.row_m[mm] * c;
+    st.inv_t = static_cast<float>(1.0 / sh.row_s[mm]);
+    st.mc_d = (!kPoint && mm < K) ? sh.row_m[K + 1 + mm] * c : 0.f;
+    st.inv_d = (!kPoint && mm < K) ? static_cast<float>(1.0 / sh.row_s[K + 1 + mm]) : 0.f;
+    sh.s_st = st;
+  }
+}
+
+// Rows m of request b as the draw reads them.
+template <typename TIn>
+__device__ __forceinline__ DrawRows<TIn> draw_rows(const TIn* tgt, const TIn* drf, int b, int K,
+                                                   int V, const ReqState& st, bool point) {
+  DrawRows<TIn> R;
+  R.resid = !point && st.m < K;
+  R.mask = st.xm;
+  R.t = tgt + (static_cast<size_t>(b) * (K + 1) + st.m) * static_cast<size_t>(V);
+  R.d = R.resid ? drf + (static_cast<size_t>(b) * K + st.m) * static_cast<size_t>(V) : R.t;
+  R.sp = row_span(R.t, V);
+  R.d_aligned = row_span(R.d, V).head == R.sp.head;
+  return R;
+}
+
+// Wave 0, once sh.s_cm holds every chunk's (residual mass, target mass): float64 prefix scan over
+// the chunks (lane l takes a contiguous run of them), total Z, threshold t = u*Z, and the chunk
+// holding it, left in sh (s_cs, s_usep, s_fallback, s_cb = the mass before that chunk, s_t).
+__device__ __forceinline__ void find_chunk(int nchunk, float u_draw, DrawShared& sh) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int per = (nchunk + kWave - 1) / kWave;
+  const int j0 = min(lane * per, nchunk), j1 = min(j0 + per, nchunk);
+  double rl = 0.0, pl = 0.0;
+  int lr = -1, lp = -1;
+  for (int j = j0; j < j1; ++j) {
+    const double2 m2 = sh.s_cm[j];
+    rl += m2.x;
+    pl += m2.y;
+    if (m2.x > 0.0) lr = j;
+    if (m2.y > 0.0) lp = j;
+  }
+  const double ri = wave_scan_incl(rl), pi = wave_scan_incl(pl);
+  const double zr = readlane_f64(ri, kWave - 1), zp = readlane_f64(pi, kWave - 1);
+  const bool usep = !(zr > 0.0);   // no residual mass left by round-off: draw from p
+  const double Z = usep ? zp : zr;
+  const double t = static_cast<double>(u_draw) * Z;
+  const double incl = usep ? pi : ri;
+  const double excl = wave_shift_up1(incl);
+  const unsigned long long cross = __ballot(incl > t);
+  const int last_pos = group_reduce(usep ? lp : lr, kWave, OpMax{});
+  if (cross) {
+    const int L = __ffsll(static_cast<long long>(cross)) - 1;
+    if (lane == L) {
+      double cum = excl;
+      int cs = -1, lastp = -1;
+      for (int j = j0; j < j1; ++j) {
+        const double mj = usep ? sh.s_cm[j].y : sh.s_cm[j].x;
+        if (mj > 0.0) lastp = j;
+        if (cum + mj > t) {
+          cs = j;
+          break;
+        }
+        cum += mj;
+      }
+      sh.s_cs = cs >= 0 ? cs : max(lastp, 0);
+      sh.s_fallback = cs >= 0 ? 0 : 1;
+      sh.s_cb = cum;
+    }
+  } else if (lane == 0) {   // round-off: the last chunk of positive weight
+    sh.s_cs = max(last_pos, 0);
+    sh.s_fallback = 1;
+    sh.s_cb = 0.0;
+  }
+  if (lane == 0) {
+    sh.s_usep = usep ? 1 : 0;
+    sh.s_t = t;
+  }
+}
+
+// The workgroup of the chunk holding u*Z (chunk `ch`, its threads' masses ws/ps and elements el
+// as thread_mass gave them): the thread holding it (block prefix scan of the thread masses), then
+// the token among that thread's elements, which the thread reads again (from the cache: holding
+// every thread's vectors in registers until here cost 32 registers per thread) and hands to
+// wave 0 through LDS; writes the token to *out_y. Called by the whole workgroup.
+template <typename TIn, bool kPoint>
+__device__ __forceinline__ void search_in_chunk(const DrawRows<TIn>& R, const ReqState& st,
+                                                float c, int V, int nchunk, int cv, int ch,
+                                                const ThreadElems& el, float ws, float ps,
+                                                DrawShared& sh, int32_t* __restrict__ out_y) {
+  using E = Elem<TIn>;
+  constexpr int N = E::N;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const bool use_p = sh.s_usep != 0;
+  const bool fb = sh.s_fallback != 0;
+  const double t = sh.s_t;
+  const float mine = use_p ? ps : ws;
+  const double wi = wave_scan_incl(static_cast<double>(mine));
+  if (lane == kWave - 1) sh.s_red[0][w] = wi;
+  const int lpos = group_reduce(mine > 0.f ? tid : -1, kWave, OpMax{});
+  if (lane == 0) sh.s_first[w] = lpos;
+  __syncthreads();
+  double off = sh.s_cb;
+  int last_thr = -1;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < w) off += sh.s_red[0][i];
+    last_thr = max(last_thr, sh.s_first[i]);
+  }
+  const double incl = off + wi;
+  const double excl = off + wave_shift_up1(wi);
+  const unsigned long long cross = fb ? 0ull : __ballot(incl > t);
+  __syncthreads();   // s_first is rewritten
+  if (lane == 0) sh.s_first[w] = cross ? w * kWave + __ffsll(static_cast<long long>(cross)) - 1 : -1;
+  __syncthreads();
+  int first = -1;
+#pragma unroll
+  for (int i = kWaves - 1; i >= 0; --i)
+    if (sh.s_first[i] >= 0) first = sh.s_first[i];
+  const bool walk_fb = first < 0;   // round-off (or fallback): the last thread of positive mass
+  if (walk_fb) first = max(last_thr, 0);
+  if (tid == first) {   // hand this thread's vectors and prefix to wave 0
+    uint4 qt[kDrawVecs], qd[kDrawVecs];
+#pragma unroll
+    for (int i = 0; i < kDrawVecs; ++i) load_pair(R, el.v0 + i, i < el.nv, qt[i], qd[i]);
+#pragma unroll
+    for (int i = 0; i < kDrawVecs; ++i) {
+      sh.s_raw[0][4 * i] = qt[i].x;
+      sh.s_raw[0][4 * i + 1] = qt[i].y;
+      sh.s_raw[0][4 * i + 2] = qt[i].z;
+      sh.s_raw[0][4 * i + 3] = qt[i].w;
+      sh.s_raw[1][4 * i] = qd[i].x;
+      sh.s_raw[1][4 * i + 1] = qd[i].y;
+      sh.s_raw[1][4 * i + 2] = qd[i].z;
+      sh.s_raw[1][4 * i + 3] = qd[i].w;
+    }
+    sh.s_cb = excl;
+  }
+  __syncthreads();
+
+  // ---- wave 0: one element of that thread per lane (at most 7 + 32 + 7 for bf16), in token
+  // order, weights as in its mass, float64 prefix scan, first element past u*Z
+  if (w == 0) {
+    const ThreadElems fe = thread_elems(R.sp, V, nchunk, cv, ch, first);
+    const int nvel = fe.nv * N;
+    const bool has = lane < fe.nh + nvel + fe.nt;
+    int tok = 0;
+    float lt = -INFINITY, ld = -INFINITY;
+    if (has) {
+      if (lane < fe.nh || lane >= fe.nh + nvel) {   // scalar head or tail element
+        tok = lane < fe.nh ? lane : fe.tail0 + (lane - fe.nh - nvel);
+        lt = E::one(R.t, tok);
+        if (R.resid) ld = E::one(R.d, tok);
+      } else {
+        const int k = lane - fe.nh, i = k / N, e = k % N;
+        tok = R.sp.head + (fe.v0 + i) * N + e;
+        lt = E::from_words(&sh.s_raw[0][4 * i], e);
+        if (R.resid) ld = R.d_aligned ? E::from_words(&sh.s_raw[1][4 * i], e) : E::one(R.d, tok);
+      }
+    }
+    float we = 0.f;
+    if (has) {
+      const float p = fast_exp2(fmaf(lt, c, -st.mc_t)) * st.inv_t;
+      if constexpr (kPoint)
+        we = (tok == R.mask && !use_p) ? 0.f : p;
+      else
+        we = (!R.resid || use_p) ? p
+                                 : fmaxf(p - fast_exp2(fmaf(ld, c, -st.mc_d)) * st.inv_d, 0.f);
+    }
+    const double cum = sh.s_cb + wave_scan_incl(static_cast<double>(we));
+    const unsigned long long pos = __ballot(we > 0.f);
+    const unsigned long long hit = walk_fb ? 0ull : __ballot(we > 0.f && cum > t);
+    int y;
+    if (hit) y = __shfl(tok, __ffsll(static_cast<long long>(hit)) - 1, kWave);
+    else if (pos) y = __shfl(tok, 63 - __clzll(static_cast<long long>(pos)), kWave);
+    else y = 0;   // no positive weight at all: only for rows without a finite logit
+    if (lane == 0) *out_y = y;
+  }
 }
 
 // Chunks of kBlock * kDrawVecs vectors (see draw_plan). cm holds the published (R, P) of every
@@ -433,17 +696,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     int32_t* __restrict__ out_tok, int32_t* __restrict__ out_tau, int32_t* __restrict__ out_kv,
     float* __restrict__ out_p, float* __restrict__ out_q, KeyArgs ka,
     const float* __restrict__ temps, const int32_t* __restrict__ dlen, int n_draw) {
-  using E = Elem<TIn>;
-  constexpr int N = E::N;
-  __shared__ double s_red[2][kWaves];
-  __shared__ double2 s_cm[kMaxDrawChunks];
-  __shared__ int s_first[kWaves];
-  __shared__ uint32_t s_raw[2][4 * kDrawVecs];   // one thread's target and draft vectors
-  __shared__ int s_cs, s_usep, s_fallback;
-  __shared__ double s_cb, s_t;
-  __shared__ float row_m[2 * SPEC_MAX_K + 1];
-  __shared__ double row_s[2 * SPEC_MAX_K + 1];
-  __shared__ ReqState s_st;
+  __shared__ DrawShared sh;
 
   if constexpr (kKeys) {
     // ---- the workgroups past the draw's select one draft slot's outcome keys each, alongside
@@ -569,253 +822,66 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       double Sr;
       merge_row_stats(pr, rr < rows, nchunk_s, W, i, c, Mr, Sr);
       if (i == 0 && rr < rows) {
-        row_m[rr] = Mr;
-        row_s[rr] = Sr;
+        sh.row_m[rr] = Mr;
+        sh.row_s[rr] = Sr;
       }
     }
     __syncthreads();
-    if (w == 0) {
-      // a draft token must be a token the draft could have sampled
-      const bool bad = valid && (xk < 0 || xk >= V || (!kPoint && ld == -INFINITY));
-      bool keep = true;
-      double pk = 0.0, qk = 0.0;
-      if (valid && !bad) {
-        // p_k(x_k) and q_k(x_k): 2^(l*c - fl(M*c)) / S of each row; a point-mass draft has
-        // q_k(x_k) = 1
-        pk = exp2_wide(static_cast<double>(lt) * c - static_cast<double>(row_m[lane] * c)) /
-             row_s[lane];
-        if constexpr (kPoint)
-          qk = 1.0;
-        else
-          qk = exp2_wide(static_cast<double>(ld) * c -
-                         static_cast<double>(row_m[K + 1 + lane] * c)) /
-               row_s[K + 1 + lane];
-        // kept iff u < min(1, p/q): p >= q is kept for every u in [0,1)
-        keep = pk >= qk || static_cast<double>(uk) < pk / qk;
-      }
-      const bool err = nb_bad || __ballot(bad) != 0ull;
-      const unsigned long long rej = __ballot(valid && !keep);
-      const int mm = rej ? (__ffsll(static_cast<long long>(rej)) - 1) : nb;
-      const int xm = __shfl(xk, mm < nb ? mm : 0, kWave);   // the rejected draft token
-      if (ch == 0) {   // one workgroup of the request writes everything but the drawn token
-        if (lane < K) {   // slots past the request's drafts report NaN
-          const size_t o = static_cast<size_t>(b) * K + lane;
-          if (out_p) out_p[o] = (err || !valid) ? NAN : static_cast<float>(pk);
-          if (out_q) out_q[o] = (err || !valid) ? NAN : static_cast<float>(qk);
-        }
-        for (int j = lane; j <= K; j += kWave)
-          if (err || j != mm) out_tok[static_cast<size_t>(b) * (K + 1) + j] = (!err && j < mm) ? xk : -1;
-        if (lane == 0) {
-          out_tau[b] = err ? -1 : mm + 1;
-          if (out_kv) out_kv[b] = err ? kv0 : kv0 + mm + 1;
-        }
-      }
-      if (lane == 0) {
-        ReqState st;
-        st.m = err ? -1 : mm;
-        st.xm = (kPoint && mm < nb) ? xm : -1;
-        st.mc_t = row_m[mm] * c;
-        st.inv_t = static_cast<float>(1.0 / row_s[mm]);
-        st.mc_d = (!kPoint && mm < K) ? row_m[K + 1 + mm] * c : 0.f;
-        st.inv_d = (!kPoint && mm < K) ? static_cast<float>(1.0 / row_s[K + 1 + mm]) : 0.f;
-        s_st = st;
-      }
-    }
+    if (w == 0)
+      decide_slots<kPoint>(b, ch, K, V, c, nb, nb_bad, valid, xk, uk, lt, ld, kv0, sh, out_tok,
+                           out_tau, out_kv, out_p, out_q);
     __syncthreads();
   }
-  const ReqState st = s_st;
-
+  const ReqState st = sh.s_st;
   if (st.m < 0) return;   // row error: nothing to draw (every workgroup of b agrees)
 
-  DrawRows<TIn> R;
-  R.resid = !kPoint && st.m < K;
-  R.mask = st.xm;
-  R.t = tgt + (static_cast<size_t>(b) * (K + 1) + st.m) * static_cast<size_t>(V);
-  R.d = R.resid ? drf + (static_cast<size_t>(b) * K + st.m) * static_cast<size_t>(V) : R.t;
-  R.sp = row_span(R.t, V);
-  R.d_aligned = row_span(R.d, V).head == R.sp.head;
-  uint64_t* cmb = cm + static_cast<size_t>(b) * nchunk * 2;
+  const DrawRows<TIn> R = draw_rows(tgt, drf, b, K, V, st, kPoint);
+  const float u_draw = uni[static_cast<size_t>(b) * (K + 1) + K];
+  const FlaggedMasses pub{cm + static_cast<size_t>(b) * nchunk * 2};
 
-  // ---- this chunk's masses, published tagged
+  // ---- this chunk's masses, published
   const ThreadElems el = thread_elems(R.sp, V, nchunk, cv, ch, tid);
-  uint4 qt[kDrawVecs], qd[kDrawVecs];
   float ws, ps;
-  thread_mass<kPoint>(R, st, c, V, el, qt, qd, ws, ps);
-  double R0, P0;
-  chunk_mass(ws, ps, s_red, R0, P0);
-  if (tid == 0) {
-    store_coherent(&cmb[2 * ch], dbits(R0) | kWrittenBit);
-    store_coherent(&cmb[2 * ch + 1], dbits(P0) | kWrittenBit);
+  {
+    uint4 qt[kDrawVecs], qd[kDrawVecs];
+    thread_mass<kPoint>(R, st, c, V, el, qt, qd, ws, ps);
   }
+  double R0, P0;
+  chunk_mass(ws, ps, sh.s_red, R0, P0);
+  if (tid == 0) pub.publish(ch, R0, P0);
 
   // ---- gather every chunk mass of the request into LDS; a chunk not published within the
   // poll budget is computed here (the same bits its owner publishes)
   bool missing = false;
   for (int j = tid; j < nchunk; j += kBlock) {
     double r = R0, q = P0;
-    if (j != ch && !poll_mass(&cmb[2 * j], wait_polls, r, q)) {
+    if (j != ch && !pub.poll(j, wait_polls, r, q)) {
       r = -1.0;   // marks the entry missing
       missing = true;
     }
-    s_cm[j] = make_double2(r, q);
+    sh.s_cm[j] = make_double2(r, q);
   }
   if (__syncthreads_or(missing)) {
     for (int j = 0; j < nchunk; ++j) {
-      if (!(s_cm[j].x < 0.0)) continue;   // uniform: read after a barrier
+      if (!(sh.s_cm[j].x < 0.0)) continue;   // uniform: read after a barrier
       uint4 ht[kDrawVecs], hd[kDrawVecs];
       float hw, hp;
       thread_mass<kPoint>(R, st, c, V, thread_elems(R.sp, V, nchunk, cv, j, tid), ht, hd, hw,
                           hp);
       double hr, hq;
-      chunk_mass(hw, hp, s_red, hr, hq);
-      if (tid == 0) s_cm[j] = make_double2(hr, hq);
+      chunk_mass(hw, hp, sh.s_red, hr, hq);
+      if (tid == 0) sh.s_cm[j] = make_double2(hr, hq);
       __syncthreads();
     }
   }
 
-  // ---- wave 0: float64 prefix scan over the chunks (lane l takes a contiguous run of them),
-  // total Z, threshold t = u*Z, and the chunk holding it
-  if (w == 0) {
-    const int per = (nchunk + kWave - 1) / kWave;
-    const int j0 = min(lane * per, nchunk), j1 = min(j0 + per, nchunk);
-    double rl = 0.0, pl = 0.0;
-    int lr = -1, lp = -1;
-    for (int j = j0; j < j1; ++j) {
-      const double2 m2 = s_cm[j];
-      rl += m2.x;
-      pl += m2.y;
-      if (m2.x > 0.0) lr = j;
-      if (m2.y > 0.0) lp = j;
-    }
-    const double ri = wave_scan_incl(rl), pi = wave_scan_incl(pl);
-    const double zr = readlane_f64(ri, kWave - 1), zp = readlane_f64(pi, kWave - 1);
-    const bool usep = !(zr > 0.0);   // no residual mass left by round-off: draw from p
-    const double Z = usep ? zp : zr;
-    const double t = static_cast<double>(uni[static_cast<size_t>(b) * (K + 1) + K]) * Z;
-    const double incl = usep ? pi : ri;
-    const double excl = wave_shift_up1(incl);
-    const unsigned long long cross = __ballot(incl > t);
-    const int last_pos = group_reduce(usep ? lp : lr, kWave, OpMax{});
-    if (cross) {
-      const int L = __ffsll(static_cast<long long>(cross)) - 1;
-      if (lane == L) {
-        double cum = excl;
-        int cs = -1, lastp = -1;
-        for (int j = j0; j < j1; ++j) {
-          const double mj = usep ? s_cm[j].y : s_cm[j].x;
-          if (mj > 0.0) lastp = j;
-          if (cum + mj > t) {
-            cs = j;
-            break;
-          }
-          cum += mj;
-        }
-        s_cs = cs >= 0 ? cs : max(lastp, 0);
-        s_fallback = cs >= 0 ? 0 : 1;
-        s_cb = cum;
-      }
-    } else if (lane == 0) {   // round-off: the last chunk of positive weight
-      s_cs = max(last_pos, 0);
-      s_fallback = 1;
-      s_cb = 0.0;
-    }
-    if (lane == 0) {
-      s_usep = usep ? 1 : 0;
-      s_t = t;
-    }
-  }
+  if (w == 0) find_chunk(nchunk, u_draw, sh);
   __syncthreads();
-  if (s_cs != ch) return;
-
-  // ---- the chunk holding u*Z: the thread holding it (block prefix scan of the thread masses),
-  // then the token, from the vectors this workgroup still holds
-  const bool use_p = s_usep != 0;
-  const bool fb = s_fallback != 0;
-  const double t = s_t;
-  const float mine = use_p ? ps : ws;
-  const double wi = wave_scan_incl(static_cast<double>(mine));
-  if (lane == kWave - 1) s_red[0][w] = wi;
-  const int lpos = group_reduce(mine > 0.f ? tid : -1, kWave, OpMax{});
-  if (lane == 0) s_first[w] = lpos;
-  __syncthreads();
-  double off = s_cb;
-  int last_thr = -1;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    if (i < w) off += s_red[0][i];
-    last_thr = max(last_thr, s_first[i]);
-  }
-  const double incl = off + wi;
-  const double excl = off + wave_shift_up1(wi);
-  const unsigned long long cross = fb ? 0ull : __ballot(incl > t);
-  __syncthreads();   // s_first is rewritten
-  if (lane == 0) s_first[w] = cross ? w * kWave + __ffsll(static_cast<long long>(cross)) - 1 : -1;
-  __syncthreads();
-  int first = -1;
-#pragma unroll
-  for (int i = kWaves - 1; i >= 0; --i)
-    if (s_first[i] >= 0) first = s_first[i];
-  const bool walk_fb = first < 0;   // round-off (or fallback): the last thread of positive mass
-  if (walk_fb) first = max(last_thr, 0);
-  if (tid == first) {   // hand this thread's vectors and prefix to wave 0
-    // read again (from the cache) rather than held in every thread's registers across the
-    // exchange: 32 fewer registers per thread, eight workgroups per CU instead of five
-#pragma unroll
-    for (int i = 0; i < kDrawVecs; ++i) load_pair(R, el.v0 + i, i < el.nv, qt[i], qd[i]);
-#pragma unroll
-    for (int i = 0; i < kDrawVecs; ++i) {
-      s_raw[0][4 * i] = qt[i].x;
-      s_raw[0][4 * i + 1] = qt[i].y;
-      s_raw[0][4 * i + 2] = qt[i].z;
-      s_raw[0][4 * i + 3] = qt[i].w;
-      s_raw[1][4 * i] = qd[i].x;
-      s_raw[1][4 * i + 1] = qd[i].y;
-      s_raw[1][4 * i + 2] = qd[i].z;
-      s_raw[1][4 * i + 3] = qd[i].w;
-    }
-    s_cb = excl;
-  }
-  __syncthreads();
-
-  // ---- wave 0: one element of that thread per lane (at most 7 + 32 + 7 for bf16), in token
-  // order, weights as in its mass, float64 prefix scan, first element past u*Z
-  if (w == 0) {
-    const ThreadElems fe = thread_elems(R.sp, V, nchunk, cv, ch, first);
-    const int nvel = fe.nv * N;
-    const bool has = lane < fe.nh + nvel + fe.nt;
-    int tok = 0;
-    float lt = -INFINITY, ld = -INFINITY;
-    if (has) {
-      if (lane < fe.nh || lane >= fe.nh + nvel) {   // scalar head or tail element
-        tok = lane < fe.nh ? lane : fe.tail0 + (lane - fe.nh - nvel);
-        lt = E::one(R.t, tok);
-        if (R.resid) ld = E::one(R.d, tok);
-      } else {
-        const int k = lane - fe.nh, i = k / N, e = k % N;
-        tok = R.sp.head + (fe.v0 + i) * N + e;
-        lt = E::from_words(&s_raw[0][4 * i], e);
-        if (R.resid) ld = R.d_aligned ? E::from_words(&s_raw[1][4 * i], e) : E::one(R.d, tok);
-      }
-    }
-    float we = 0.f;
-    if (has) {
-      const float p = fast_exp2(fmaf(lt, c, -st.mc_t)) * st.inv_t;
-      if constexpr (kPoint)
-        we = (tok == R.mask && !use_p) ? 0.f : p;
-      else
-        we = (!R.resid || use_p) ? p
-                                 : fmaxf(p - fast_exp2(fmaf(ld, c, -st.mc_d)) * st.inv_d, 0.f);
-    }
-    const double cum = s_cb + wave_scan_incl(static_cast<double>(we));
-    const unsigned long long pos = __ballot(we > 0.f);
-    const unsigned long long hit = walk_fb ? 0ull : __ballot(we > 0.f && cum > t);
-    int y;
-    if (hit) y = __shfl(tok, __ffsll(static_cast<long long>(hit)) - 1, kWave);
-    else if (pos) y = __shfl(tok, 63 - __clzll(static_cast<long long>(pos)), kWave);
-    else y = 0;   // no positive weight at all: only for rows without a finite logit
-    if (lane == 0) out_tok[static_cast<size_t>(b) * (K + 1) + st.m] = y;
-  }
+  if (sh.s_cs != ch) return;
+  search_in_chunk<TIn, kPoint>(R, st, c, V, nchunk, cv, ch, el, ws, ps, sh,
+                               out_tok + static_cast<size_t>(b) * (K + 1) + st.m);
 }
+
 
 struct SamplePlan {
   KernelPlan stats, draw;
@@ -840,6 +906,7 @@ template <typename TIn, bool kKeys, bool kMixed, bool kPoint = false>
 int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, const float* uni,
                     const int32_t* kv_in, int B, int K, int V, float T, int32_t* out_tok,
                     int32_t* out_tau, int32_t* out_kv, float* out_p, float* out_q, void* ws,
+                    size_t ws_bytes,
                     hipStream_t stream, hipEvent_t* ev, int wait_polls, const SamplePlan& P,
                     const KeyRequest& kr, const float* temps, const int32_t* dlen = nullptr) {
   const size_t g1 = static_cast<size_t>(B) * (kPoint ? K + 1 : 2 * K + 1) * P.stats.nchunk;
@@ -849,7 +916,7 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
   if (!grid_fits(g1) || !grid_fits(g2) || P.draw.cv != kBlock * kDrawVecs ||
       P.draw.nchunk > kMaxDrawChunks)
     return SPEC_ERR_ARG;
-  const WsLayout L = ws_layout(B, K, V, 1);
+  const WsLayout L = ws_layout(B, K, V, 1, ws_bytes);
   const float c = exp2_scale(T);
   const TIn* t = static_cast<const TIn*>(target);
   const TIn* d = static_cast<const TIn*>(draft);   // null for point-mass drafts
@@ -866,7 +933,8 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
   const int nd_wg = static_cast<int>(n_draw);
   // non-temporal loads in the statistics pass when the rows it streams exceed the Infinity Cache
   const long long streamed =
-      static_cast<long long>(B) * (kPoint ? K + 1 : 2 * K + 1) * V * static_cast<long long>(sizeof(TIn));
+      static_cast<long long>(B) * (kPoint ? K + 1 : 2 * K + 1) * V *
+      static_cast<long long>(sizeof(TIn));
   const int nt = streamed > kInfinityCacheBytes ? 1 : 0;
   if (ev == nullptr) {
     hipLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0, stream, t, d,
@@ -893,21 +961,22 @@ template <typename TIn>
 int launch_sample(const void* target, const void* draft, const int32_t* xtok, const float* uni,
                   const int32_t* kv_in, int B, int K, int V, float T, int32_t* out_tok,
                   int32_t* out_tau, int32_t* out_kv, float* out_p, float* out_q, void* ws,
-                  hipStream_t stream, hipEvent_t* ev, int wait_polls, const KeyRequest& kr,
+                  size_t ws_bytes, hipStream_t stream, hipEvent_t* ev, int wait_polls,
+                  const KeyRequest& kr,
                   const float* temps) {
   const bool keys = kr.F > 0;
   const SamplePlan P = default_sample_plan<TIn>(B, K, V, keys);
   if (temps != nullptr)
     return launch_sample_t<TIn, false, true>(target, draft, xtok, uni, kv_in, B, K, V, T, out_tok,
-                                             out_tau, out_kv, out_p, out_q, ws, stream, ev,
-                                             wait_polls, P, kr, temps);
+                                             out_tau, out_kv, out_p, out_q, ws, ws_bytes, stream,
+                                             ev, wait_polls, P, kr, temps);
   if (keys)
     return launch_sample_t<TIn, true, false>(target, draft, xtok, uni, kv_in, B, K, V, T, out_tok,
-                                             out_tau, out_kv, out_p, out_q, ws, stream, ev,
-                                             wait_polls, P, kr, nullptr);
+                                             out_tau, out_kv, out_p, out_q, ws, ws_bytes, stream,
+                                             ev, wait_polls, P, kr, nullptr);
   return launch_sample_t<TIn, false, false>(target, draft, xtok, uni, kv_in, B, K, V, T, out_tok,
-                                            out_tau, out_kv, out_p, out_q, ws, stream, ev,
-                                            wait_polls, P, kr, nullptr);
+                                            out_tau, out_kv, out_p, out_q, ws, ws_bytes, stream,
+                                            ev, wait_polls, P, kr, nullptr);
 }
 
 int verify_sample_entry(const void* target_logits, const void* draft_logits, int dtype,
@@ -938,10 +1007,11 @@ int verify_sample_entry(const void* target_logits, const void* draft_logits, int
   if (dtype == SPEC_BF16)
     return launch_sample<uint16_t>(target_logits, draft_logits, draft_tokens, uniforms, kv_len_in,
                                    B, K, V, temperature, out_tokens, out_tau, out_kv_len, out_p,
-                                   out_q, workspace, stream, events, wait_polls, kr, temps);
+                                   out_q, workspace, workspace_bytes, stream, events, wait_polls,
+                                   kr, temps);
   return launch_sample<float>(target_logits, draft_logits, draft_tokens, uniforms, kv_len_in, B,
                               K, V, temperature, out_tokens, out_tau, out_kv_len, out_p, out_q,
-                              workspace, stream, events, wait_polls, kr, temps);
+                              workspace, workspace_bytes, stream, events, wait_polls, kr, temps);
 }
 
 }  // namespace
@@ -1021,16 +1091,19 @@ extern "C" int spec_verify_point(const void* target_logits, int dtype,
   if ((rc = check_workspace(workspace, workspace_bytes, B, K, V, 1)) != SPEC_OK) return rc;
   if (temperature == 0.f)
     return greedy_point_entry(target_logits, dtype, draft_tokens, draft_len, kv_len_in, B, K, V,
-                              out_tokens, out_tau, out_kv_len, out_p, out_q, workspace, stream);
+                              out_tokens, out_tau, out_kv_len, out_p, out_q, workspace,
+                              workspace_bytes, stream);
   if (uniforms == nullptr) return SPEC_ERR_ARG;
   const KeyRequest none{0, 0, nullptr, nullptr};
   if (dtype == SPEC_BF16)
     return launch_sample_t<uint16_t, false, false, true>(
         target_logits, nullptr, draft_tokens, uniforms, kv_len_in, B, K, V, temperature,
-        out_tokens, out_tau, out_kv_len, out_p, out_q, workspace, stream, nullptr, -1,
-        SamplePlan{point_plan(B, K, V, 8), draw_plan(B, K, V, 8)}, none, nullptr, draft_len);
+        out_tokens, out_tau, out_kv_len, out_p, out_q, workspace, workspace_bytes, stream,
+        nullptr, -1, SamplePlan{point_plan(B, K, V, 8), draw_plan(B, K, V, 8)}, none, nullptr,
+        draft_len);
   return launch_sample_t<float, false, false, true>(
       target_logits, nullptr, draft_tokens, uniforms, kv_len_in, B, K, V, temperature,
-      out_tokens, out_tau, out_kv_len, out_p, out_q, workspace, stream, nullptr, -1,
-      SamplePlan{point_plan(B, K, V, 4), draw_plan(B, K, V, 4)}, none, nullptr, draft_len);
+      out_tokens, out_tau, out_kv_len, out_p, out_q, workspace, workspace_bytes, stream,
+      nullptr, -1, SamplePlan{point_plan(B, K, V, 4), draw_plan(B, K, V, 4)}, none, nullptr,
+      draft_len);
 }

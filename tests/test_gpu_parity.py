@@ -295,22 +295,33 @@ def _same_bits(a, b):
 
 
 def test_workspace_reuse_across_shapes():
-    """One workspace serves calls of other shapes and inputs in turn: partial results and
-    published masses left by an earlier call sit where a later call of another shape looks, and
-    must never be taken for its own. Every call must equal a call on a fresh workspace, also
-    with a zero poll budget (every draw workgroup then computes each chunk mass it does not find
-    already published)."""
+    """One workspace serves calls of other shapes and inputs in turn: partial results, published
+    masses and arrival counters left by an earlier call sit where a later call of another shape
+    looks, and must never be taken for its own (counters live in the workspace's first half and
+    every other region in its second, so no call writes data where another shape counts). Every
+    call (sampling, also with a zero poll budget; greedy; keys; mixed batches) must equal the
+    same call on a fresh workspace."""
     shapes = [(16, 40000, 41), (5, 12345, 42), (16, 40000, 43), (3, 40000, 44), (16, 999, 45),
-              (11, 40000, 46)]
-    ws = sv.new_workspace(16, 4, 40000)
+              (11, 40000, 46), (40, 3001, 47), (2, 40000, 48), (40, 3001, 49), (64, 20000, 50)]
+    ws = sv.new_workspace(64, 4, 40000, 4)
     for B, V, rnd in shapes:
         wl = make_workload(3, rnd, B=B, V=V)
         dev = upload(wl)
         announce(f"workspace reuse B={B} V={V}")
-        ref = gpu_sample(wl, dev=dev, ws=sv.new_workspace(B, wl.K, V))
+        fresh = sv.new_workspace(B, wl.K, V, 4)
+        ref = gpu_sample(wl, dev=dev, ws=fresh)
         for polls in (None, 0):
             _same_bits(ref, gpu_sample(wl, dev=dev, ws=ws, wait_polls=polls))
         compare_sample(wl, ref)
+        # the paths with per-request arrival counters, on the same shared workspace
+        wg = make_workload(3, rnd, "greedy", B=B, V=V)
+        dg = upload(wg, with_draft=False)
+        _same_bits(gpu_greedy(wg, dev=dg, ws=fresh), gpu_greedy(wg, dev=dg, ws=ws))
+        compare_greedy(wg, gpu_greedy(wg, dev=dg, ws=ws))
+        _same_bits(gpu_predict(wl, 4, 0.7, dev=dev, ws=fresh),
+                   gpu_predict(wl, 4, 0.7, dev=dev, ws=ws))
+        mixed_T = np.where(np.arange(B) % 2 == 0, 0.0, float(wl.T)).astype(np.float32)
+        _same_bits(gpu_mixed(wl, mixed_T, dev=dev, ws=fresh), gpu_mixed(wl, mixed_T, dev=dev, ws=ws))
 
 
 def test_graph_capture_replays():
