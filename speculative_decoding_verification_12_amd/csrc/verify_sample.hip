@@ -386,11 +386,13 @@ struct KeyArgs {
 // (W a power of two; lane i of the group holds chunks i, i + W, ...): every lane of the group
 // gets the same bits, wherever the group sits in the wave. has = false (a group without a row)
 // gives (-inf, 0).
+constexpr int kMergeHeld = 4;   // chunks a lane keeps in registers between the merge's two passes
+
 // `rd(j)` returns chunk j's (max, sum).
 template <typename Rd>
 __device__ __forceinline__ void merge_row_stats_rd(Rd rd, bool has, int n, int W, int i, float c,
                                                    float& Mr, double& Sr) {
-  constexpr int kHeld = 4;   // chunks a lane keeps in registers between the two passes
+  constexpr int kHeld = kMergeHeld;
   float hm[kHeld], hs[kHeld];
   float lm = -INFINITY;
 #pragma unroll
@@ -422,10 +424,16 @@ __device__ __forceinline__ void merge_row_stats(const float2* pr, bool has, int 
   merge_row_stats_rd([pr](int j) { return pr[j]; }, has, n, W, i, c, Mr, Sr);
 }
 
-// the group width the merges use for rows of n chunks
-__device__ __forceinline__ int merge_width(int n) {
+// The group width the merges use for `rows` rows of n chunks: the widest power of two (at most
+// 64, one chunk per lane) with which the block's waves take every row in one pass, but not so
+// narrow that a lane would hold more than kMergeHeld chunks (then the rows take several passes).
+// One pass issues every partial load at once; each pass costs a round trip.
+__device__ __forceinline__ int merge_width(int n, int rows) {
+  int lo = 1;
+  while (lo * kMergeHeld < n && lo < kWave) lo <<= 1;
   int W = 1;
   while (W < n && W < kWave) W <<= 1;
+  while (W > lo && kWaves * (kWave / W) < rows) W >>= 1;
   return W;
 }
 
@@ -709,7 +717,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       const int lane = threadIdx.x & (kWave - 1);
       const int xk = ka.exclude ? xtok[bk] : -1;
       const float2* pr = part_s + (static_cast<size_t>(kb) * (2 * K + 1) + K + 1 + kk) * nchunk_s;
-      const int Wk = merge_width(nchunk_s);
+      const int Wk = merge_width(nchunk_s, 2 * K + 1);   // as the draw's merge below
       auto row_stat = [&]() {
         float Mr;
         double Sr;
@@ -810,10 +818,10 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       if constexpr (!kPoint) ld = gath[static_cast<size_t>(b) * 2 * K + K + lane];
     }
     const int kv0 = (ch == 0 && tid == 0 && kv_in) ? kv_in[b] : 0;
-    // Rows are merged in groups of W lanes (W = nchunk_s rounded up to a power of two, at most
-    // 64), 64/W rows per wave, so one pass over the block issues every partial load at once.
-    // Lanes past nchunk_s (or past the last row) carry (-inf, 0).
-    const int W = merge_width(nchunk_s);
+    // Rows are merged in groups of W lanes (merge_width), 64/W rows per wave, so one pass over
+    // the block issues every partial load at once. Lanes past nchunk_s (or past the last row)
+    // carry (-inf, 0).
+    const int W = merge_width(nchunk_s, rows);
     const int per_wave = kWave / W, g = lane / W, i = lane % W;
     for (int base = 0; base < rows; base += kWaves * per_wave) {
       const int rr = base + w * per_wave + g;
