@@ -72,6 +72,23 @@ def test_workspace_bytes(lib):
     assert lib.spec_workspace_bytes(1, 4, sv.SPEC_MAX_V, 1) > 0
 
 
+def test_workspace_too_small_for_shape(lib):
+    """A workspace sized for one shape is rejected (before anything is enqueued) by a call of a
+    shape whose counters or data do not fit in its halves; spec_workspace_bytes of the larger
+    shape is always enough for the smaller one."""
+    code = {v: k for k, v in sv.STATUS.items()}
+    small = lib.spec_workspace_bytes(2, 4, 1000, 1)
+    big = lib.spec_workspace_bytes(64, 4, 128256, 1)
+    assert big >= 2 * small > 0
+    ws = ctypes.c_void_p(0x100000)   # 256-byte aligned, never dereferenced
+    assert sample_call(lib, B=64, V=128256, ws=ws, wsb=small) == code["SPEC_ERR_WORKSPACE"]
+    assert sample_call(lib, B=2, V=1000, ws=ws, wsb=0) == code["SPEC_ERR_WORKSPACE"]
+    # many requests of a tiny vocabulary need many counters: the first half must hold them
+    many = lib.spec_workspace_bytes(4096, 8, 2, 1)
+    assert many >= 2 * 4096 * 9 * 256
+    assert sample_call(lib, B=4096, K=8, V=2, ws=ws, wsb=small) == code["SPEC_ERR_WORKSPACE"]
+
+
 FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: every call fails validation first
 FAKE_ODD = ctypes.c_void_p(0x10001)   # misaligned for any logit dtype
 NULL = None
