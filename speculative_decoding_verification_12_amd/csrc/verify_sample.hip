@@ -700,7 +700,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     const TIn* __restrict__ tgt, const TIn* __restrict__ drf, const int32_t* __restrict__ xtok,
     const float* __restrict__ uni, const int32_t* __restrict__ kv_in, int K, int V, float c_call,
     int nchunk_s, const float2* __restrict__ part_s, const float* __restrict__ gath,
-    int nchunk, int cv, uint64_t* __restrict__ cm, int wait_polls,
+    int nchunk, int cv, int aligned, uint64_t* __restrict__ cm, int wait_polls,
     int32_t* __restrict__ out_tok, int32_t* __restrict__ out_tau, int32_t* __restrict__ out_kv,
     float* __restrict__ out_p, float* __restrict__ out_q, KeyArgs ka,
     const float* __restrict__ temps, const int32_t* __restrict__ dlen, int n_draw) {
@@ -845,6 +845,40 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
 
   const DrawRows<TIn> R = draw_rows(tgt, drf, b, K, V, st, kPoint);
   const float u_draw = uni[static_cast<size_t>(b) * (K + 1) + K];
+
+  // ---- every draft kept (the weights are p_m of the extra row): when the statistics pass cut
+  // the row into the draw's chunks, chunk j's mass is S_j 2^(fl(M_j c) - fl(M c)) / S from its
+  // partial, so no chunk is read for the masses and nothing is exchanged; only the workgroup of
+  // the chunk holding u*Z reads its chunk, to find the token
+  if (aligned && st.m == nb && !R.resid && R.mask < 0) {
+    if (w == 0) {
+      const float2* pr = part_s + (static_cast<size_t>(b) * rows + st.m) * nchunk_s;
+      for (int j = lane; j < nchunk; j += kWave) {
+        const float2 q = pr[j];
+        const double P = q.x > -INFINITY
+                             ? static_cast<double>(q.y) *
+                                   exp2_wide(static_cast<double>(q.x * c) -
+                                             static_cast<double>(st.mc_t)) *
+                                   static_cast<double>(st.inv_t)
+                             : 0.0;
+        sh.s_cm[j] = make_double2(P, P);
+      }
+    }
+    __syncthreads();
+    if (w == 0) find_chunk(nchunk, u_draw, sh);
+    __syncthreads();
+    if (sh.s_cs != ch) return;
+    const ThreadElems el = thread_elems(R.sp, V, nchunk, cv, ch, tid);
+    float ws, ps;
+    {
+      uint4 qt[kDrawVecs], qd[kDrawVecs];
+      thread_mass<kPoint>(R, st, c, V, el, qt, qd, ws, ps);
+    }
+    search_in_chunk<TIn, kPoint>(R, st, c, V, nchunk, cv, ch, el, ws, ps, sh,
+                                 out_tok + static_cast<size_t>(b) * (K + 1) + st.m);
+    return;
+  }
+
   const FlaggedMasses pub{cm + static_cast<size_t>(b) * nchunk * 2};
 
   // ---- this chunk's masses, published
@@ -944,13 +978,16 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
       static_cast<long long>(B) * (kPoint ? K + 1 : 2 * K + 1) * V *
       static_cast<long long>(sizeof(TIn));
   const int nt = streamed > kInfinityCacheBytes ? 1 : 0;
+  // the statistics pass cut every row into the draw's chunks (chunk masses of an extra row can be
+  // taken from its partials)
+  const int aligned = (ns == nd && cs == cd) ? 1 : 0;
   if (ev == nullptr) {
     hipLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0, stream, t, d,
                        xtok, K, V, c, ns, cs, part1, gath, cm, nclear, kwmax, temps, dlen, nt);
     hipLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint>), grid2, block, 0, stream, t, d,
                        xtok, uni, kv_in, K, V, c, ns, static_cast<const float2*>(part1),
-                       static_cast<const float*>(gath), nd, cd, cm, polls, out_tok, out_tau,
-                       out_kv, out_p, out_q, ka, temps, dlen, nd_wg);
+                       static_cast<const float*>(gath), nd, cd, aligned, cm, polls, out_tok,
+                       out_tau, out_kv, out_p, out_q, ka, temps, dlen, nd_wg);
   } else {
     // profiling: the runtime records the events at each kernel's start and end
     hipExtLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0, stream,
@@ -959,8 +996,8 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
     hipExtLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint>), grid2, block, 0, stream,
                           ev[2], ev[3], 0, t, d, xtok, uni, kv_in, K, V, c, ns,
                           static_cast<const float2*>(part1), static_cast<const float*>(gath), nd,
-                          cd, cm, polls, out_tok, out_tau, out_kv, out_p, out_q, ka, temps,
-                          dlen, nd_wg);
+                          cd, aligned, cm, polls, out_tok, out_tau, out_kv, out_p, out_q, ka,
+                          temps, dlen, nd_wg);
   }
   return launch_status();
 }
