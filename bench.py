@@ -377,6 +377,27 @@ def other_configs(sv, torch, dev, args):
                          sample_warm=latency(samp, 1), sample_rotated=latency(samp, n_sets),
                          greedy_warm=latency(greedy, 1), greedy_rotated=latency(greedy, n_sets),
                          rotated_sets=n_sets)
+        # the same sampling call captured once into a HIP graph and replayed (the caller's way
+        # of removing host launch cost from a latency-bound loop; the library records no
+        # memset node, so replays are exact)
+        static = {k: v.clone() for k, v in ds[0].items()}
+
+        def samp_static():
+            sv.spec_verify_sample(static["t"], static["d"], static["x"], static["u"],
+                                  static["kv"], T, ws, out=out)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            samp_static()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            samp_static()
+        torch.cuda.synchronize()
+        res[name]["sample_graph_replay"] = latency(lambda i: graph.replay(), 1)
+        del graph
 
     # ---- C4: B=256, K=8, V=152064 bf16, T=1; even requests accept every draft (bonus path).
     # One input set of 1.32 GB, five times the Infinity Cache, so calls cannot hit it.
