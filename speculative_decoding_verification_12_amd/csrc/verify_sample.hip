@@ -21,12 +21,17 @@
 //     re-reads its chunk of row m of the target (and of the draft when m < K), sums the draw
 //     weights per thread and per chunk and publishes the chunk's mass, tagged as written. Every
 //     workgroup of the request gathers all chunk masses, runs the same float64 prefix scan and
-//     so learns which chunk holds u*Z; that chunk's own workgroup finds the thread, then the
-//     token, from the values still in its registers. A workgroup that has polled for a mass too
-//     long computes that chunk's mass itself (bit for bit what its owner publishes), so no
-//     workgroup ever waits on one that has not been scheduled.
+//     so learns which chunk holds u*Z; that chunk's own workgroup finds the thread (block scan
+//     of the thread masses), which reads its few vectors again, then the token. A workgroup
+//     that has polled for a mass too long computes that chunk's mass itself (bit for bit what
+//     its owner publishes), so no workgroup ever waits on one that has not been scheduled.
+//     When every draft was kept and the statistics pass cut the extra row into the draw's
+//     chunks, the chunk masses come from its partials instead: nothing is re-read but the
+//     chunk holding u*Z, and nothing is exchanged.
 // With outcome keys (kKeys) the statistics pass also keeps the draft rows' wave maxima, and the
 // draw's grid has one more workgroup per draft slot that selects the slot's keys meanwhile.
+// The statistics pass reads with non-temporal loads when the rows it streams exceed the
+// Infinity Cache (the draw's re-read of row m then comes from HBM whatever the hint).
 #include <hip/hip_ext.h>
 
 #include "api_common.hpp"
