@@ -486,20 +486,23 @@ __device__ __forceinline__ void decide_slots(int b, int ch, int K, int V, float 
   // a draft token must be a token the draft could have sampled
   const bool bad = valid && (xk < 0 || xk >= V || (!kPoint && ld == -INFINITY));
   bool keep = true;
-  double pk = 0.0, qk = 0.0;
+  float pk = 0.f, qk = 0.f;
   if (valid && !bad) {
-    // p_k(x_k) and q_k(x_k): 2^(l*c - fl(M*c)) / S of each row; a point-mass draft has
-    // q_k(x_k) = 1
-    pk = exp2_wide(static_cast<double>(lt) * c - static_cast<double>(sh.row_m[lane] * c)) /
-         sh.row_s[lane];
-    if constexpr (kPoint)
-      qk = 1.0;
-    else
-      qk = exp2_wide(static_cast<double>(ld) * c -
-                     static_cast<double>(sh.row_m[K + 1 + lane] * c)) /
-           sh.row_s[K + 1 + lane];
+    // log2 p_k(x_k) = l*c - fl(M*c) - log2 S of the target row, log2 q_k(x_k) likewise (0 for a
+    // point-mass draft). In float32 and the log domain: accurate to ~3e-6 relative in p, q and
+    // the ratio (inside the 1e-5 margin that flags a decision as a near-tie), and neither p nor
+    // q can underflow the ratio (a float64 evaluation cost ~1 us on every draw workgroup's
+    // critical path). S >= 1: the row's maximum contributes 2^0.
+    const float lp = fmaf(lt, c, -(sh.row_m[lane] * c)) -
+                     __builtin_amdgcn_logf(static_cast<float>(sh.row_s[lane]));
+    float lq = 0.f;
+    if constexpr (!kPoint)
+      lq = fmaf(ld, c, -(sh.row_m[K + 1 + lane] * c)) -
+           __builtin_amdgcn_logf(static_cast<float>(sh.row_s[K + 1 + lane]));
+    pk = fast_exp2(lp);
+    qk = kPoint ? 1.f : fast_exp2(lq);
     // kept iff u < min(1, p/q): p >= q is kept for every u in [0,1)
-    keep = pk >= qk || static_cast<double>(uk) < pk / qk;
+    keep = lp >= lq || uk < fast_exp2(lp - lq);
   }
   const bool err = nb_bad || __ballot(bad) != 0ull;
   const unsigned long long rej = __ballot(valid && !keep);
@@ -508,8 +511,8 @@ __device__ __forceinline__ void decide_slots(int b, int ch, int K, int V, float 
   if (ch == 0) {   // one workgroup of the request writes everything but the drawn token
     if (lane < K) {   // slots past the request's drafts report NaN
       const size_t o = static_cast<size_t>(b) * K + lane;
-      if (out_p) out_p[o] = (err || !valid) ? NAN : static_cast<float>(pk);
-      if (out_q) out_q[o] = (err || !valid) ? NAN : static_cast<float>(qk);
+      if (out_p) out_p[o] = (err || !valid) ? NAN : pk;
+      if (out_q) out_q[o] = (err || !valid) ? NAN : qk;
     }
     for (int j = lane; j <= K; j += kWave)
       if (err || j != mm) out_tok[static_cast<size_t>(b) * (K + 1) + j] = (!err && j < mm) ? xk : -1;
@@ -523,9 +526,9 @@ __device__ __forceinline__ void decide_slots(int b, int ch, int K, int V, float 
     st.m = err ? -1 : mm;
     st.xm = (kPoint && mm < nb) ? xm : -1;
     st.mc_t = sh.row_m[mm] * c;
-    st.inv_t = static_cast<float>(1.0 / sh.row_s[mm]);
+    st.inv_t = 1.f / static_cast<float>(sh.row_s[mm]);
     st.mc_d = (!kPoint && mm < K) ? sh.row_m[K + 1 + mm] * c : 0.f;
-    st.inv_d = (!kPoint && mm < K) ? static_cast<float>(1.0 / sh.row_s[K + 1 + mm]) : 0.f;
+    st.inv_d = (!kPoint && mm < K) ? 1.f / static_cast<float>(sh.row_s[K + 1 + mm]) : 0.f;
     sh.s_st = st;
   }
 }
