@@ -603,9 +603,10 @@ __device__ __forceinline__ void find_chunk(int nchunk, float u_draw, DrawShared&
 
 // The workgroup of the chunk holding u*Z (chunk `ch`, its threads' masses ws/ps and elements el
 // as thread_mass gave them): the thread holding it (block prefix scan of the thread masses), then
-// the token among that thread's elements, which the thread reads again (from the cache: holding
-// every thread's vectors in registers until here cost 32 registers per thread) and hands to
-// wave 0 through LDS; writes the token to *out_y. Called by the whole workgroup.
+// the token among that thread's elements, which it hands to wave 0 through LDS; writes the token
+// to *out_y. Called by the whole workgroup. The vectors are read again here (from the cache):
+// holding every thread's vectors in registers across the mass exchange cost 32 registers per
+// thread in every draw workgroup.
 template <typename TIn, bool kPoint>
 __device__ __forceinline__ void search_in_chunk(const DrawRows<TIn>& R, const ReqState& st,
                                                 float c, int V, int nchunk, int cv, int ch,
@@ -614,6 +615,11 @@ __device__ __forceinline__ void search_in_chunk(const DrawRows<TIn>& R, const Re
   using E = Elem<TIn>;
   constexpr int N = E::N;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  // every thread reads its vectors again now (cache hits), so the one that turns out to hold
+  // u*Z has them when the block scan below has named it
+  uint4 qt[kDrawVecs], qd[kDrawVecs];
+#pragma unroll
+  for (int i = 0; i < kDrawVecs; ++i) load_pair(R, el.v0 + i, i < el.nv, qt[i], qd[i]);
   const bool use_p = sh.s_usep != 0;
   const bool fb = sh.s_fallback != 0;
   const double t = sh.s_t;
@@ -643,9 +649,6 @@ __device__ __forceinline__ void search_in_chunk(const DrawRows<TIn>& R, const Re
   const bool walk_fb = first < 0;   // round-off (or fallback): the last thread of positive mass
   if (walk_fb) first = max(last_thr, 0);
   if (tid == first) {   // hand this thread's vectors and prefix to wave 0
-    uint4 qt[kDrawVecs], qd[kDrawVecs];
-#pragma unroll
-    for (int i = 0; i < kDrawVecs; ++i) load_pair(R, el.v0 + i, i < el.nv, qt[i], qd[i]);
 #pragma unroll
     for (int i = 0; i < kDrawVecs; ++i) {
       sh.s_raw[0][4 * i] = qt[i].x;
