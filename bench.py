@@ -128,9 +128,9 @@ def cpu_baseline(wl, repeats):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build runs the verification step on a single "
-              "MI355X (requests shard across GPUs with no exchange; see the design notes). "
-              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
+        print("bench.py measures one GPU only: the verification step runs on a single MI355X "
+              "(requests are independent, so a batch splits across GPUs by request with no "
+              f"exchange). --gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
 
     log(f"generating {args.sets} C3 input sets")
