@@ -30,8 +30,10 @@
 //     chunk holding u*Z, and nothing is exchanged.
 // With outcome keys (kKeys) the statistics pass also keeps the draft rows' wave maxima, and the
 // draw's grid has one more workgroup per draft slot that selects the slot's keys meanwhile.
-// The statistics pass reads with non-temporal loads when the rows it streams exceed the
-// Infinity Cache (the draw's re-read of row m then comes from HBM whatever the hint).
+// Load hints of the statistics pass: non-temporal loads everywhere when the rows it streams
+// exceed the Infinity Cache (the draw's re-read of row m then comes from HBM whatever the hint);
+// for a large pass that fits, non-temporal loads on the draft rows and the extra target row
+// only, so the draw re-reads target row m from the cache and draft row m from HBM at once.
 #include <hip/hip_ext.h>
 
 #include "api_common.hpp"
@@ -114,6 +116,13 @@ __device__ __forceinline__ void chunk_argmax(const TIn* row, const RowSpan& sp,
   }
 }
 
+// Load hint of a launch of the statistics pass (uniform over the grid).
+enum LoadHint : int {
+  kHintCached = 0,       // ordinary loads: the rows stay in the Infinity Cache for the draw
+  kHintStream = 1,       // non-temporal loads on every row
+  kHintStreamDraft = 2,  // non-temporal loads on the draft rows and the extra target row
+};
+
 template <typename TIn, bool kKeys, bool kMixed, bool kPoint>
 __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
     const TIn* __restrict__ tgt, const TIn* __restrict__ drf, const int32_t* __restrict__ xtok,
@@ -184,12 +193,14 @@ __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
   }
 
   float m, s, M, S;
-  // The draw re-reads row m right after this pass. While the call's rows fit in the Infinity
-  // Cache, ordinary loads leave row m there for it (non-temporal loads made the pass ~1 us
-  // faster and the draw slower, the call level at 148 MB and a mixed batch 1.6 us slower); when
-  // they do not fit, the re-read comes from HBM either way and non-temporal loads only speed up
-  // the pass (C4, 1.32 GB: 253 instead of 275 us per call). `nt` is uniform.
-  if (nt)
+  // The draw re-reads target row m (and draft row m below the extra row) right after this pass.
+  // When the rows do not fit in the Infinity Cache, the re-read comes from HBM either way and
+  // non-temporal loads only speed up the pass. When they fit, ordinary loads on every row keep
+  // both re-read rows in the cache, which is best while the re-read is latency-bound (small
+  // batches, mixed batches); for a large batch, streaming the draft rows and the extra target
+  // row (whose re-read, on the all-kept path, is one chunk) makes the pass faster and splits
+  // the draw's re-read between the cache and HBM. `nt` is uniform.
+  if (nt == kHintStream || (nt == kHintStreamDraft && r >= K))
     thread_chunk_stats<TIn, true, true>(row, sp, cr, V, c, m, s);
   else
     thread_chunk_stats<TIn, true, false>(row, sp, cr, V, c, m, s);
@@ -984,11 +995,17 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
   const int pick = kr.F + (kr.exclude ? 1 : 0);
   const KeyArgs ka{pick, kr.F, kr.exclude, cs, kwmax, kr.out_keys, kr.out_prob};
   const int nd_wg = static_cast<int>(n_draw);
-  // non-temporal loads in the statistics pass when the rows it streams exceed the Infinity Cache
+  // load hint of the statistics pass, from the bytes it streams (measured at C3 shapes cut to B
+  // requests, alternating A/B: draft rows streamed at B = 32 (74 MB) and B = 64 (148 MB) saved
+  // 0.5 and 0.9-1.3 us per call; at B <= 16 (37 MB and less) the call is latency-bound and
+  // nothing changed, at B = 1 it lost 0.4 us; a mixed batch lost 1 us)
   const long long streamed =
       static_cast<long long>(B) * (kPoint ? K + 1 : 2 * K + 1) * V *
       static_cast<long long>(sizeof(TIn));
-  const int nt = streamed > kInfinityCacheBytes ? 1 : 0;
+  const int nt = streamed > kInfinityCacheBytes ? kHintStream
+                 : (!kMixed && !kPoint && streamed >= kInfinityCacheBytes / 4)
+                     ? kHintStreamDraft
+                     : kHintCached;
   // the statistics pass cut every row into the draw's chunks (chunk masses of an extra row can be
   // taken from its partials)
   const int aligned = (ns == nd && cs == cd) ? 1 : 0;
