@@ -38,14 +38,15 @@
  *     written.
  *   - Workspace: size from spec_workspace_bytes(B,K,V,F) (one size serves every entry point),
  *     256-byte aligned, zeroed once by spec_workspace_init before its first use. Each call
- *     leaves it ready for the next one: the arrival counters it holds are reset on the device,
- *     and the sampling draw's published-mass words are cleared by the same call's streaming
- *     pass before the draw reads them. The counters live in the workspace's first half and
- *     every other region in its second, so one workspace serves calls of any shapes whose
- *     counters and data each fit in a half (a workspace sized for the largest B, K, V a caller
- *     uses does; a call that does not fit returns SPEC_ERR_WORKSPACE). One workspace must not
- *     be used by two calls that may run concurrently (two streams, or two host threads on one
- *     stream without ordering): they would race.
+ *     leaves it ready for the next one: the greedy path's published words are cleared on the
+ *     device by the workgroups that read them, and the sampling draw's published-mass words
+ *     are cleared by the same call's streaming pass before the draw reads them. The greedy
+ *     words live in the workspace's first half and every other region in its second, so one
+ *     workspace serves calls of any shapes for which it holds at least spec_workspace_bytes
+ *     (a workspace sized for the largest B, K, V a caller uses does; a call for which it is
+ *     smaller returns SPEC_ERR_WORKSPACE). One workspace must not be used by two calls that
+ *     may run concurrently (two streams, or two host threads on one stream without ordering):
+ *     they would race.
  *   - Errors found on the host are returned synchronously, before anything is enqueued:
  *       SPEC_ERR_ARG         null required pointer, B < 1, K < 1 or K > SPEC_MAX_K, V < 2
  *                            or V > SPEC_MAX_V,
@@ -54,8 +55,8 @@
  *       SPEC_ERR_DTYPE       dtype not SPEC_F32 / SPEC_BF16;
  *       SPEC_ERR_TEMPERATURE sampling with T not finite or T <= 0 (or log2(e)/T not finite);
  *                            greedy with T != 0; prediction with T < 0 or not finite;
- *       SPEC_ERR_WORKSPACE   workspace null, not 256-byte aligned, or too small for this
- *                            call's counters and data (spec_workspace_bytes is always enough);
+ *       SPEC_ERR_WORKSPACE   workspace null, not 256-byte aligned, or smaller than
+ *                            spec_workspace_bytes for this call's sizes;
  *       SPEC_ERR_HIP         a launch failed (hipGetLastError after enqueueing).
  *   - Errors in device data are reported per request ("row error"): a draft token outside
  *     [0,V), or, when sampling, a draft token whose draft logit is -inf (it cannot be a sample
@@ -73,7 +74,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 7
+#define SPEC_ABI_VERSION 8
 #define SPEC_MAX_K 64
 #define SPEC_MAX_NGRAM 64
 #define SPEC_MAX_CONTEXT 1073741824 /* 2^30 tokens per context row */
@@ -104,8 +105,9 @@ const char* spec_status_string(int status);
  * the sizes are invalid (same rules as SPEC_ERR_ARG). */
 size_t spec_workspace_bytes(int B, int K, int V, int F);
 
-/* Zeroes the workspace's completion counters on `stream` (one small kernel). Call once after
- * allocating a workspace. */
+/* Zeroes the workspace on `stream` (one small fill kernel): the greedy path's published words
+ * and its mark. Call once after allocating a workspace, and again to clear the mark a greedy
+ * decider leaves when it runs out of polls (spec_verify_greedy_ex). */
 int spec_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Speculative-sampling verification at temperature T > 0 ([SD] stages 3-4; [D3D] 検証のまとめ).
@@ -238,6 +240,21 @@ int spec_verify_greedy(const void* target_logits, int dtype, const int32_t* draf
                        const int32_t* kv_len_in, int B, int K, int V, float temperature,
                        int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* spec_verify_greedy with the deciders' poll budget, for testing. Results are identical to
+ * spec_verify_greedy, bit for bit, whatever the budget is.
+ *   wait_polls the chunk workgroups publish their (max, lowest id) and one deciding workgroup
+ *              per request, launched after all of them, polls for these at most this many times
+ *              per word (a short sleep apart). Negative selects SPEC_DEFAULT_WAIT_POLLS (what
+ *              spec_verify_greedy uses). A decider that runs out streams its request's rows
+ *              itself and marks the workspace: from then on every greedy call on it does the
+ *              same (same results, more time) until spec_workspace_init clears the mark. 0 makes
+ *              every decider that does not find all its words already published take that path. */
+int spec_verify_greedy_ex(const void* target_logits, int dtype, const int32_t* draft_tokens,
+                          const int32_t* kv_len_in, int B, int K, int V, float temperature,
+                          int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream,
+                          int wait_polls);
 
 /* Outcome-key prediction ([SSD] "1. Outcome Prediction"; [D3D] "答え:…").
  * For every request b and slot k < K: out_keys[b,k,0..F-1] = the F token ids with the largest

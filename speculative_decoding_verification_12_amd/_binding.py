@@ -25,6 +25,7 @@ STATUS = {0: "SPEC_OK", -1: "SPEC_ERR_ARG", -2: "SPEC_ERR_DTYPE", -3: "SPEC_ERR_
 EXPORTS = ("spec_abi_version", "spec_status_string", "spec_workspace_bytes",
            "spec_workspace_init", "spec_verify_sample", "spec_verify_sample_ex",
            "spec_verify_sample_keys", "spec_verify_mixed", "spec_verify_greedy",
+           "spec_verify_greedy_ex",
            "spec_predict_outcomes",
            "spec_predict_fanout", "spec_outcome_lookup", "spec_kv_rewind", "spec_ngram_draft",
            "spec_verify_point")
@@ -46,6 +47,8 @@ _SIGNATURES = {
                                _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_greedy": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _f,
                                 _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_verify_greedy_ex": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _f,
+                                   _vp, _vp, _vp, _vp, _sz, _vp, _i]),
     "spec_predict_outcomes": (_i, [_vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "spec_predict_fanout": (_i, [_vp, _i, _vp, _i, _i, _i, _i, _vp, _f, _vp, _vp, _vp, _sz,
                                  _vp]),
@@ -163,6 +166,13 @@ def new_workspace(B: int, K: int, V: int, F: int = 1, device="cuda"):
     return ws
 
 
+def spec_workspace_init(workspace):
+    """Clear a workspace tensor again (the greedy path's published words and mark)."""
+    _check("spec_workspace_init", load_library().spec_workspace_init(
+        _ptr(workspace), workspace.numel(), _stream(workspace.device)))
+    return workspace
+
+
 def spec_verify_sample(target, draft, draft_tokens, uniforms, kv_len, temperature, workspace,
                        out=None, events=None, wait_polls=None):
     """Speculative-sampling verification. Returns dict(tokens, tau, kv_len, p, q).
@@ -262,8 +272,12 @@ def spec_verify_mixed(target, draft, draft_tokens, uniforms, kv_len, temperature
     return out
 
 
-def spec_verify_greedy(target, draft_tokens, kv_len, workspace, temperature=0.0, out=None):
-    """Greedy verification. Returns dict(tokens, tau, kv_len)."""
+def spec_verify_greedy(target, draft_tokens, kv_len, workspace, temperature=0.0, out=None,
+                       wait_polls=None):
+    """Greedy verification. Returns dict(tokens, tau, kv_len).
+
+    `wait_polls` (optional) bounds the deciders' polling for the chunk results and routes the
+    call through spec_verify_greedy_ex."""
     torch = _torch()
     B, K1, V = target.shape
     K = K1 - 1
@@ -276,11 +290,14 @@ def spec_verify_greedy(target, draft_tokens, kv_len, workspace, temperature=0.0,
         out = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
                    tau=torch.empty(B, dtype=torch.int32, device=dev),
                    kv_len=torch.empty(B, dtype=torch.int32, device=dev))
-    rc = load_library().spec_verify_greedy(
-        _ptr(target), _dtype_code(target), _ptr(draft_tokens), _ptr(kv_len), B, K, V,
-        float(temperature), _ptr(out["tokens"]), _ptr(out["tau"]), _ptr(out.get("kv_len")),
-        _ptr(workspace), workspace.numel(), _stream(dev))
-    _check("spec_verify_greedy", rc)
+    args = (_ptr(target), _dtype_code(target), _ptr(draft_tokens), _ptr(kv_len), B, K, V,
+            float(temperature), _ptr(out["tokens"]), _ptr(out["tau"]), _ptr(out.get("kv_len")),
+            _ptr(workspace), workspace.numel(), _stream(dev))
+    lib = load_library()
+    if wait_polls is None:
+        _check("spec_verify_greedy", lib.spec_verify_greedy(*args))
+    else:
+        _check("spec_verify_greedy_ex", lib.spec_verify_greedy_ex(*args, int(wait_polls)))
     return out
 
 

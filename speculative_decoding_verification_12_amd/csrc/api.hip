@@ -34,7 +34,8 @@ extern "C" size_t spec_workspace_bytes(int B, int K, int V, int F) {
 
 extern "C" int spec_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
   // Clears the whole workspace with a fill kernel (no memset node, so the call may also be
-  // recorded in a graph). It holds the arrival counters; it is small and this runs once.
+  // recorded in a graph). It holds the greedy path's published words and mark; it is small and
+  // this runs rarely.
   if (workspace == nullptr || !sv::is_aligned(workspace, 256)) return SPEC_ERR_WORKSPACE;
   const size_t words = workspace_bytes / sizeof(unsigned);
   if (words == 0) return SPEC_ERR_WORKSPACE;

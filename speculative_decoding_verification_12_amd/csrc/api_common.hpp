@@ -31,9 +31,12 @@ inline int check_logits(const void* p, int dtype) {
   return (p != nullptr && is_aligned(p, elem_bytes(dtype))) ? SPEC_OK : SPEC_ERR_ARG;
 }
 
+// The workspace must hold at least spec_workspace_bytes for the call's sizes; its halves then
+// hold this shape's words and data whatever size it was allocated for.
 inline int check_workspace(const void* ws, size_t bytes, int B, int K, int V, int F) {
-  if (ws == nullptr || !is_aligned(ws, 256) || !ws_layout(B, K, V, F, bytes).fits)
-    return SPEC_ERR_WORKSPACE;
+  if (ws == nullptr || !is_aligned(ws, 256)) return SPEC_ERR_WORKSPACE;
+  const WsLayout L = ws_layout(B, K, V, F, bytes);
+  if (bytes < L.total || !L.fits) return SPEC_ERR_WORKSPACE;
   return SPEC_OK;
 }
 

@@ -21,7 +21,6 @@ constexpr int kBlock = 256;            // threads per workgroup, every kernel
 constexpr int kVecPerThread = 4;       // 16-byte vectors a thread holds per pass
 constexpr int kPassVecs = kBlock * kVecPerThread;
 constexpr int kCUs = 256;              // MI355X compute units
-constexpr int kCounterStride = 64;     // words between arrival counters (256 bytes apart)
 
 // Streaming plan of one kernel: every row is cut into `nchunk` chunks of `cv` vectors (the last
 // one shorter); one workgroup per (row, chunk).
@@ -78,8 +77,10 @@ SV_HD inline KernelPlan draw_plan(int B, int K, int V, int epv) {
 SV_HD inline KernelPlan point_plan(int B, int K, int V, int epv) {
   return plan_rows(B * (K + 1), V, epv, kStatsResident, kPassVecs);
 }
+// greedy verification: chunks of at most one pass of the block, so that even a batch that would
+// fill the GPU once with larger chunks runs in several rounds (no workgroup waits on another)
 SV_HD inline KernelPlan greedy_plan(int B, int K, int V, int epv) {
-  return plan_rows(B * (K + 1), V, epv, kGreedyResident);
+  return plan_rows(B * (K + 1), V, epv, kGreedyResident, kPassVecs);
 }
 // outcome keys: chunks of at most kPredictVecs vectors, so that even a batch that would fill the
 // GPU once with larger chunks runs in several rounds and the workgroups' arithmetic overlaps the
@@ -99,25 +100,20 @@ struct ReqState {
   float inv_d;
 };
 
-struct ArgPart {   // (value, index) partial of an argmax or top-F list
-  float v;
-  int i;
-};
-
 struct WsLayout {
-  size_t cnt_a;      // unsigned[max(B*K, B) * kCounterStride]: per-request or per-row counters
-  size_t cnt_b;      // unsigned[B * kCounterStride]: counters of the residual/bonus draw
-  size_t counters_end;
+  size_t greedy_mark;   // unsigned at offset 0 for every shape: set once a greedy decider
+                        // stopped waiting (cleared only by spec_workspace_init)
+  size_t greedy_words;  // 8 B [B*(K+1)*nchunk]: greedy, published chunk (max, lowest index)
+  size_t words_end;     // end of the first half's regions
   size_t gathered;   // float [B*2K]: target and draft logit of each slot's draft token
   size_t part_stats; // 8 B [B*(2K+1)*nchunk] (point drafts: [B*(K+1)*nchunk]): chunk (max, sum)
   size_t part_draw;  // 16 B [B*nchunk]: published chunk (residual mass, target mass)
-  size_t part_greedy;// 8 B [B*(K+1)*nchunk]: chunk (max, lowest index)
   size_t part_pred;  // 8 B [B*K*nchunk]: outcome keys, chunk (max, scaled sum)
   size_t part_pwm;   // 4 B [B*K*nchunk*4]: outcome keys, wave maxima
   size_t part_vwm;   // 4 B [B*K*nchunk*4]: wave maxima of the draft rows (outcome keys)
   size_t data_end;   // end of the last data region
-  size_t total;      // bytes this shape needs: twice the larger of counters and data
-  bool fits;         // the caller's workspace holds this shape's counters and data
+  size_t total;      // bytes this shape needs: twice the larger of the two halves' regions
+  bool fits;         // the caller's workspace holds this shape's words and data
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -128,12 +124,12 @@ inline size_t max_chunks(PlanFn fn, int B, int K, int V) {
   return static_cast<size_t>(a > b ? a : b);
 }
 
-// Layout covering both element types. The workspace is cut in two halves: the arrival counters
-// live in the first, every other region in the second. Counters are zero between calls (each
-// call resets the ones it used) and nothing else is ever written in the first half, so one
-// workspace can serve calls of different shapes in turn: no call writes data where a call of
-// another shape keeps a counter. `ws_bytes` is the caller's workspace size; `total`, the size
-// this shape needs, does not depend on it.
+// Layout covering both element types. The workspace is cut in two halves. The first holds the
+// greedy path's published words, zero between calls (each decider clears the words it read), and
+// the greedy mark at offset 0 whatever the shape, so that calls of every shape see it. The
+// second holds every other region, which each call writes before it reads. One workspace can
+// therefore serve calls of different shapes in turn. `ws_bytes` is the caller's workspace size;
+// `total`, the size this shape needs, does not depend on it.
 inline WsLayout ws_layout(int B, int K, int V, int F, size_t ws_bytes) {
   (void)F;   // the keys go to the caller's outputs
   const size_t b = static_cast<size_t>(B), k = static_cast<size_t>(K);
@@ -142,14 +138,10 @@ inline WsLayout ws_layout(int B, int K, int V, int F, size_t ws_bytes) {
   const size_t nd = max_chunks(draw_plan, B, K, V);
   const size_t ng = max_chunks(greedy_plan, B, K, V);
   const size_t np = max_chunks(predict_plan, B, K, V);
-  const size_t stride = kCounterStride;
   WsLayout L;
-  size_t off = 0;
-  L.cnt_a = off;
-  off = align256(off + sizeof(unsigned) * stride * (b * k > b ? b * k : b));
-  L.cnt_b = off;
-  off = align256(off + sizeof(unsigned) * stride * b);
-  L.counters_end = off;
+  L.greedy_mark = 0;
+  L.greedy_words = 256;
+  L.words_end = align256(L.greedy_words + 8 * b * (k + 1) * ng);
   // data regions, first relative to the start of the second half
   size_t d = 0;
   L.gathered = d;
@@ -159,22 +151,19 @@ inline WsLayout ws_layout(int B, int K, int V, int F, size_t ws_bytes) {
                                                                   : b * (k + 1) * npt));
   L.part_draw = d;
   d = align256(d + 16 * b * nd);
-  L.part_greedy = d;
-  d = align256(d + 8 * b * (k + 1) * ng);
   L.part_pred = d;
   d = align256(d + 8 * b * k * np);
   L.part_pwm = d;
   d = align256(d + 4 * b * k * np * 4);
   L.part_vwm = d;
   d = align256(d + 4 * b * k * ns * 4);
-  const size_t need_half = L.counters_end > d ? L.counters_end : d;
+  const size_t need_half = L.words_end > d ? L.words_end : d;
   L.total = 2 * need_half;
   const size_t half = (ws_bytes / 2) & ~static_cast<size_t>(255);
-  L.fits = L.counters_end <= half && half + d <= ws_bytes;
+  L.fits = L.words_end <= half && half + d <= ws_bytes;
   L.gathered += half;
   L.part_stats += half;
   L.part_draw += half;
-  L.part_greedy += half;
   L.part_pred += half;
   L.part_pwm += half;
   L.part_vwm += half;

@@ -295,13 +295,12 @@ __device__ __forceinline__ double exp2_wide(double x) {
   return ldexp(static_cast<double>(fast_exp2(static_cast<float>(x - n))), static_cast<int>(n));
 }
 
-// ------------------------------------------------------------------------------ arrival
-// Workgroups of one group (a request or a row) publish partial results and count themselves in;
-// the last to arrive merges them. The eight XCDs have separate L2 caches, so the partials are
-// written and read with device-scope (agent) atomic stores/loads, which are coherent across
-// XCDs by themselves; no L2 writeback or invalidate is needed. A device-scope __threadfence()
-// would write back the whole L2 of the XCD for every workgroup, which serialises thousands of
-// small workgroups.
+// ------------------------------------------------------------------------------ exchange
+// Workgroups of one launch publish partial results that another workgroup of the same launch
+// reads. The eight XCDs have separate L2 caches, so such words are written and read with
+// device-scope (agent) atomic stores/loads, which are coherent across XCDs by themselves; no L2
+// writeback or invalidate is needed. A device-scope __threadfence() would write back the whole
+// L2 of the XCD for every workgroup, which serialises thousands of small workgroups.
 __device__ __forceinline__ void store_coherent(void* p, uint64_t v) {
   __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -349,26 +348,6 @@ __device__ __forceinline__ uint64_t dbits(double d) {
 }
 __device__ __forceinline__ double bits_d(uint64_t x) {
   return __longlong_as_double(static_cast<long long>(x));
-}
-
-// Counts this workgroup in; true (in every thread) for the last of `expected` to arrive. Every
-// wave first waits for its own memory operations (the coherent partial stores among them) to
-// complete, so when the counter moves, this workgroup's partials are at the device coherence
-// point; the last workgroup then reads them with load_coherent.
-__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected, int* s_flag) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev =
-        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = (prev == expected - 1u) ? 1 : 0;
-  }
-  __syncthreads();
-  return *s_flag != 0;
-}
-
-__device__ __forceinline__ void reset_counter(unsigned* counter) {
-  __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace sv

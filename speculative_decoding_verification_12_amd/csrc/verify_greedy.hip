@@ -11,20 +11,28 @@
 // n_b is appended.
 //
 // One launch: a workgroup per (request, row, chunk) streams its chunk once, tracks the largest
-// logit and its lowest id per thread, and reduces (value desc, id asc) across the workgroup. The
-// request's last workgroup to arrive merges the chunks, compares g_k with x_k in one wave
-// (lane k = slot k, ballot for the first mismatch) and writes the outputs.
+// logit and its lowest id per thread, reduces (value desc, id asc) across the workgroup and
+// publishes the result as a self-flagged word in the part of the workspace that is zero between
+// calls; it waits for nothing. The grid ends with one deciding workgroup per request: it polls
+// the request's words, merges each row's chunks, clears the words, compares g_k with x_k in one
+// wave (lane k = slot k, ballot for the first mismatch) and writes the outputs. The deciders are
+// the last workgroups of the grid, so every streaming workgroup has been dispatched before they
+// start, and those never wait: the polls end. They are still bounded: a decider that runs out of
+// polls marks the workspace and streams its request's rows itself (the same maxima and lowest
+// ids). Words published after that are never cleared, so while the mark is set (until
+// spec_workspace_init) every decider streams its own rows and trusts no published word.
 #include "api_common.hpp"
 #include "spec_common.hpp"
 
 namespace sv {
 namespace {
 
-// The (max, lowest id) of chunk `ch` of row `rb`, stored as that chunk's partial.
+// The (max, lowest id) of chunk `ch` of row `rb`; the result is valid in thread 0. A caller that
+// runs it again first passes a barrier (s_v, s_i are reused).
 template <typename TIn>
 __device__ __forceinline__ void greedy_chunk(const TIn* __restrict__ tgt, int rb, int ch, int V,
-                                             int nchunk, int cv, ArgPart* __restrict__ part,
-                                             float* s_v, int* s_i) {
+                                             int nchunk, int cv, float* s_v, int* s_i, float& M,
+                                             int& I) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
@@ -78,35 +86,37 @@ __device__ __forceinline__ void greedy_chunk(const TIn* __restrict__ tgt, int rb
   }
   __syncthreads();
   if (tid == 0) {
-    float v = s_v[0];
-    int i = s_i[0];
+    M = s_v[0];
+    I = s_i[0];
     for (int k = 1; k < kWaves; ++k)
-      if (better(s_v[k], s_i[k], v, i)) {
-        v = s_v[k];
-        i = s_i[k];
+      if (better(s_v[k], s_i[k], M, I)) {
+        M = s_v[k];
+        I = s_i[k];
       }
-    store_coherent(&part[static_cast<size_t>(rb) * nchunk + ch], pack2(v, i));
   }
 }
+
+// Published word of a chunk: (max, lowest id) with bit 31 of the id set as the written flag
+// (ids are below 2^31; an all -inf chunk keeps the id 0x7fffffff).
+constexpr uint64_t kArgFlag = 1ull << 63;
 
 template <typename TIn>
 __global__ __launch_bounds__(kBlock) void greedy_kernel(
     const TIn* __restrict__ tgt, const int32_t* __restrict__ xtok,
-    const int32_t* __restrict__ kv_in, int K, int V, int nchunk, int cv,
-    ArgPart* __restrict__ part, unsigned* __restrict__ cnt_base, int32_t* __restrict__ out_tok,
-    int32_t* __restrict__ out_tau, int32_t* __restrict__ out_kv,
+    const int32_t* __restrict__ kv_in, int K, int V, int nchunk, int cv, int nstream,
+    uint64_t* __restrict__ words, unsigned* __restrict__ mark, int wait_polls,
+    int32_t* __restrict__ out_tok, int32_t* __restrict__ out_tau, int32_t* __restrict__ out_kv,
     const int32_t* __restrict__ dlen, float* __restrict__ out_p, float* __restrict__ out_q) {
   __shared__ float s_v[kWaves];
   __shared__ int s_i[kWaves];
-  __shared__ int s_flag;
   __shared__ int row_g[SPEC_MAX_K + 1];
+  __shared__ int s_late;
 
   const int rows = K + 1;
-  const int ch = blockIdx.x % nchunk;
-  const int rb = blockIdx.x / nchunk;   // b * (K+1) + row
-  const int b = rb / rows;
+  const bool decider = static_cast<int>(blockIdx.x) >= nstream;
+  const int rb = decider ? 0 : static_cast<int>(blockIdx.x) / nchunk;   // b * (K+1) + row
+  const int b = decider ? static_cast<int>(blockIdx.x) - nstream : rb / rows;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  unsigned* cnt = cnt_base + static_cast<size_t>(b) * kCounterStride;
   // drafts in this request: K, or the first dlen[b] slots (outside [0, K]: a row error)
   int nb = K;
   bool nb_bad = false;
@@ -115,27 +125,74 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
     nb_bad = nb < 0 || nb > K;
     if (nb_bad) nb = -1;
   }
-  // a row past n_b is never used by an outcome: it is not read, but its workgroups still arrive
-  if (rb % rows <= nb) greedy_chunk<TIn>(tgt, rb, ch, V, nchunk, cv, part, s_v, s_i);
-  if (!arrive_last(cnt, static_cast<unsigned>(rows * nchunk), &s_flag)) return;
 
-  // ---- last workgroup of request b: per-row argmax over chunks (rows up to n_b)
+  if (!decider) {
+    // a row past n_b is never used by an outcome: it is not read and publishes nothing
+    if (rb % rows > nb) return;
+    const int ch = static_cast<int>(blockIdx.x) % nchunk;
+    float M;
+    int I;
+    greedy_chunk<TIn>(tgt, rb, ch, V, nchunk, cv, s_v, s_i, M, I);
+    if (tid == 0) store_coherent(words + static_cast<size_t>(rb) * nchunk + ch, pack2(M, I) | kArgFlag);
+    return;
+  }
+
+  // ---- decider of request b: per-row argmax over the published chunks (rows up to n_b); each
+  // wave takes rows w, w + 4, ... and clears each word it has read. Every call's chunk
+  // workgroups publish their words, so the polls end whether or not the mark is set; the mark,
+  // read alongside them, only decides afterwards whether the words are trusted.
+  if (tid == 0) s_late = 0;
+  __syncthreads();
+  const bool marked = load_coherent_u32(mark) != 0u;
+  bool late = false;
   for (int rr = w; rr < rows && rr <= nb; rr += kWaves) {
-    const ArgPart* pr = part + (static_cast<size_t>(b) * rows + rr) * nchunk;
+    uint64_t* pw = words + (static_cast<size_t>(b) * rows + rr) * nchunk;
     float v = -INFINITY;
     int i = 0x7fffffff;
     for (int j = lane; j < nchunk; j += kWave) {
-      const uint64_t a = load_coherent(&pr[j]);
+      uint64_t a = load_coherent(pw + j);
+      for (int polls = wait_polls; (a & kArgFlag) == 0ull && polls > 0; --polls) {
+        __builtin_amdgcn_s_sleep(2);
+        a = load_coherent(pw + j);
+      }
+      if ((a & kArgFlag) == 0ull) {
+        late = true;
+        continue;
+      }
+      a &= ~kArgFlag;
       if (better(lo_float(a), hi_int(a), v, i)) {
         v = lo_float(a);
         i = hi_int(a);
       }
+      store_coherent(pw + j, 0ull);   // read: back to zero for the next call
     }
     wave_argmax(v, i);
-    // a row whose logits are all -inf keeps no index: its first token is the lowest id
-    if (lane == 0) row_g[rr] = (i == 0x7fffffff) ? 0 : i;
+    if (lane == 0) row_g[rr] = (i == 0x7fffffff) ? 0 : i;   // an all -inf row: the lowest id
   }
+  if (__any(late || marked) && lane == 0) s_late = 1;
   __syncthreads();
+  if (s_late != 0) {
+    // a row's words did not all arrive within the poll budget, or the mark was set: stream the
+    // request's rows here, chunk by chunk in order (so the same maximum and lowest id); words
+    // that arrive later stay set, which the mark covers
+    if (tid == 0) store_coherent_u32(mark, 1u);
+    for (int rr = 0; rr < rows && rr <= nb; ++rr) {
+      float v = -INFINITY;
+      int i = 0x7fffffff;
+      for (int ch = 0; ch < nchunk; ++ch) {
+        float M;
+        int I;
+        greedy_chunk<TIn>(tgt, b * rows + rr, ch, V, nchunk, cv, s_v, s_i, M, I);
+        if (tid == 0 && better(M, I, v, i)) {
+          v = M;
+          i = I;
+        }
+        __syncthreads();   // s_v, s_i are reused
+      }
+      if (tid == 0) row_g[rr] = (i == 0x7fffffff) ? 0 : i;
+    }
+    __syncthreads();
+  }
   if (w != 0) return;
 
   const int k = lane;
@@ -159,23 +216,26 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
     const int kv0 = kv_in ? kv_in[b] : 0;
     out_tau[b] = err ? -1 : mm + 1;
     if (out_kv) out_kv[b] = err ? kv0 : kv0 + mm + 1;
-    reset_counter(cnt);
   }
 }
 
 template <typename TIn>
 int launch_greedy(const void* target, const int32_t* xtok, const int32_t* kv_in, int B, int K,
                   int V, int32_t* out_tok, int32_t* out_tau, int32_t* out_kv, void* ws,
-                  size_t ws_bytes, hipStream_t stream, const KernelPlan& P,
-                  const int32_t* dlen = nullptr,
-                  float* out_p = nullptr, float* out_q = nullptr) {
-  const size_t g = static_cast<size_t>(B) * (K + 1) * P.nchunk;
+                  size_t ws_bytes, hipStream_t stream, int wait_polls,
+                  const int32_t* dlen = nullptr, float* out_p = nullptr,
+                  float* out_q = nullptr) {
+  const KernelPlan P = greedy_plan(B, K, V, 16 / static_cast<int>(sizeof(TIn)));
+  const size_t nstream = static_cast<size_t>(B) * (K + 1) * P.nchunk;
+  const size_t g = nstream + static_cast<size_t>(B);   // the deciders come last
   if (!grid_fits(g)) return SPEC_ERR_ARG;
   const WsLayout L = ws_layout(B, K, V, 1, ws_bytes);
   hipLaunchKernelGGL(greedy_kernel<TIn>, dim3(static_cast<unsigned>(g)), dim3(kBlock), 0, stream,
                      static_cast<const TIn*>(target), xtok, kv_in, K, V, P.nchunk, P.cv,
-                     ws_ptr<ArgPart>(ws, L.part_greedy), ws_ptr<unsigned>(ws, L.cnt_a), out_tok,
-                     out_tau, out_kv, dlen, out_p, out_q);
+                     static_cast<int>(nstream), ws_ptr<uint64_t>(ws, L.greedy_words),
+                     ws_ptr<unsigned>(ws, L.greedy_mark),
+                     wait_polls < 0 ? SPEC_DEFAULT_WAIT_POLLS : wait_polls, out_tok, out_tau,
+                     out_kv, dlen, out_p, out_q);
   return launch_status();
 }
 
@@ -187,17 +247,17 @@ int greedy_point_entry(const void* target, int dtype, const int32_t* xtok, const
                        size_t ws_bytes, hipStream_t stream) {
   if (dtype == SPEC_BF16)
     return launch_greedy<uint16_t>(target, xtok, kv_in, B, K, V, out_tok, out_tau, out_kv, ws,
-                                   ws_bytes, stream, greedy_plan(B, K, V, 8), dlen, out_p, out_q);
+                                   ws_bytes, stream, -1, dlen, out_p, out_q);
   return launch_greedy<float>(target, xtok, kv_in, B, K, V, out_tok, out_tau, out_kv, ws,
-                              ws_bytes, stream, greedy_plan(B, K, V, 4), dlen, out_p, out_q);
+                              ws_bytes, stream, -1, dlen, out_p, out_q);
 }
 }  // namespace sv
 
-extern "C" int spec_verify_greedy(const void* target_logits, int dtype,
-                                  const int32_t* draft_tokens, const int32_t* kv_len_in, int B,
-                                  int K, int V, float temperature, int32_t* out_tokens,
-                                  int32_t* out_tau, int32_t* out_kv_len, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream) {
+extern "C" int spec_verify_greedy_ex(const void* target_logits, int dtype,
+                                     const int32_t* draft_tokens, const int32_t* kv_len_in, int B,
+                                     int K, int V, float temperature, int32_t* out_tokens,
+                                     int32_t* out_tau, int32_t* out_kv_len, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream, int wait_polls) {
   using namespace sv;
   int rc = check_dtype(dtype);
   if (rc != SPEC_OK) return rc;
@@ -210,8 +270,17 @@ extern "C" int spec_verify_greedy(const void* target_logits, int dtype,
   if (dtype == SPEC_BF16)
     return launch_greedy<uint16_t>(target_logits, draft_tokens, kv_len_in, B, K, V, out_tokens,
                                    out_tau, out_kv_len, workspace, workspace_bytes, stream,
-                                   greedy_plan(B, K, V, 8));
+                                   wait_polls);
   return launch_greedy<float>(target_logits, draft_tokens, kv_len_in, B, K, V, out_tokens,
-                              out_tau, out_kv_len, workspace, workspace_bytes, stream,
-                              greedy_plan(B, K, V, 4));
+                              out_tau, out_kv_len, workspace, workspace_bytes, stream, wait_polls);
+}
+
+extern "C" int spec_verify_greedy(const void* target_logits, int dtype,
+                                  const int32_t* draft_tokens, const int32_t* kv_len_in, int B,
+                                  int K, int V, float temperature, int32_t* out_tokens,
+                                  int32_t* out_tau, int32_t* out_kv_len, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return spec_verify_greedy_ex(target_logits, dtype, draft_tokens, kv_len_in, B, K, V,
+                               temperature, out_tokens, out_tau, out_kv_len, workspace,
+                               workspace_bytes, stream, -1);
 }

@@ -66,13 +66,14 @@ def gpu_sample(wl, dev=None, ws=None, wait_polls=None):
     return {k: _np(v) for k, v in out.items()}
 
 
-def gpu_greedy(wl, dev=None, ws=None):
+def gpu_greedy(wl, dev=None, ws=None, wait_polls=None):
     dev = dev or upload(wl, with_draft=False)
     B, K = wl.B, wl.K
     ws = ws if ws is not None else sv.new_workspace(B, K, wl.V)
     out = dict(tokens=poisoned((B, K + 1), torch.int32), tau=poisoned((B,), torch.int32),
                kv_len=poisoned((B,), torch.int32))
-    sv.spec_verify_greedy(dev["target"], dev["tokens"], dev["kv"], ws, out=out)
+    sv.spec_verify_greedy(dev["target"], dev["tokens"], dev["kv"], ws, out=out,
+                          wait_polls=wait_polls)
     torch.cuda.synchronize()
     return {k: _np(v) for k, v in out.items()}
 

@@ -74,8 +74,8 @@ def test_workspace_bytes(lib):
 
 def test_workspace_too_small_for_shape(lib):
     """A workspace sized for one shape is rejected (before anything is enqueued) by a call of a
-    shape whose counters or data do not fit in its halves; spec_workspace_bytes of the larger
-    shape is always enough for the smaller one."""
+    shape whose published words or data do not fit in its halves; spec_workspace_bytes of the
+    larger shape is always enough for the smaller one."""
     code = {v: k for k, v in sv.STATUS.items()}
     small = lib.spec_workspace_bytes(2, 4, 1000, 1)
     big = lib.spec_workspace_bytes(64, 4, 128256, 1)
@@ -83,9 +83,10 @@ def test_workspace_too_small_for_shape(lib):
     ws = ctypes.c_void_p(0x100000)   # 256-byte aligned, never dereferenced
     assert sample_call(lib, B=64, V=128256, ws=ws, wsb=small) == code["SPEC_ERR_WORKSPACE"]
     assert sample_call(lib, B=2, V=1000, ws=ws, wsb=0) == code["SPEC_ERR_WORKSPACE"]
-    # many requests of a tiny vocabulary need many counters: the first half must hold them
+    # many requests of a tiny vocabulary: the first half must hold the greedy mark and one
+    # published 8-byte word per row (one chunk each)
     many = lib.spec_workspace_bytes(4096, 8, 2, 1)
-    assert many >= 2 * 4096 * 9 * 256
+    assert many >= 2 * (256 + 4096 * 9 * 8)
     assert sample_call(lib, B=4096, K=8, V=2, ws=ws, wsb=small) == code["SPEC_ERR_WORKSPACE"]
 
 

@@ -289,6 +289,26 @@ def test_draw_help_path_bit_identical(cid, B, V, rnd):
     compare_sample(wl, h, requests=range(min(wl.B, 16)))
 
 
+@pytest.mark.parametrize("cid,B,V,rnd", [(3, 64, None, 25), (2, 1, None, 26), (3, 7, 1003, 27)])
+def test_greedy_decider_help_path(cid, B, V, rnd):
+    """wait_polls=0: a decider that does not find every chunk word of its request already
+    published streams the request's rows itself and marks the workspace; while the mark is set
+    every greedy call on that workspace does so, and spec_workspace_init clears it. All three
+    states must give the default path's outputs bit for bit (and the oracle's)."""
+    kw = dict(B=B) if V is None else dict(B=B, V=V)
+    wl = make_workload(cid, rnd, "greedy", **kw)
+    dev = upload(wl, with_draft=False)
+    ws = sv.new_workspace(wl.B, wl.K, wl.V)
+    announce(f"greedy help path C{cid} B={wl.B} V={wl.V}")
+    ref = gpu_greedy(wl, dev=dev, ws=sv.new_workspace(wl.B, wl.K, wl.V))
+    _same_bits(ref, gpu_greedy(wl, dev=dev, ws=ws, wait_polls=0))
+    _same_bits(ref, gpu_greedy(wl, dev=dev, ws=ws))   # marked if a decider helped
+    sv.spec_workspace_init(ws)
+    _same_bits(ref, gpu_greedy(wl, dev=dev, ws=ws))
+    _same_bits(ref, gpu_greedy(wl, dev=dev, ws=ws))   # words cleared by the previous call
+    compare_greedy(wl, ref)
+
+
 def _same_bits(a, b):
     for k in a:
         assert np.array_equal(a[k].view(np.int32), b[k].view(np.int32)), k
