@@ -19,7 +19,7 @@
 // the last workgroups of the grid, so every streaming workgroup has been dispatched before they
 // start, and those never wait: the polls end. They are still bounded: a decider that runs out of
 // polls marks the workspace and streams its request's rows itself (the same maxima and lowest
-// ids). Words published after that are never cleared, so while the mark is set (until
+// ids). Words published after that may stay set, so while the mark is set (until
 // spec_workspace_init) every decider streams its own rows and trusts no published word.
 #include "api_common.hpp"
 #include "spec_common.hpp"
@@ -133,7 +133,8 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
     float M;
     int I;
     greedy_chunk<TIn>(tgt, rb, ch, V, nchunk, cv, s_v, s_i, M, I);
-    if (tid == 0) store_coherent(words + static_cast<size_t>(rb) * nchunk + ch, pack2(M, I) | kArgFlag);
+    if (tid == 0)
+      store_coherent(words + static_cast<size_t>(rb) * nchunk + ch, pack2(M, I) | kArgFlag);
     return;
   }
 

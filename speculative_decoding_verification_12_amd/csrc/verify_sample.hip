@@ -189,7 +189,8 @@ __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
     const int x = xtok[static_cast<size_t>(b) * K + slot];
     const int lo = cr.first ? 0 : sp.head + cr.vbeg * N;
     const int hi = cr.last ? V : sp.head + cr.vend * N;
-    if (x >= lo && x < hi) gath[static_cast<size_t>(b) * 2 * K + (r < K ? slot : K + slot)] = E::one(row, x);
+    if (x >= lo && x < hi)
+      gath[static_cast<size_t>(b) * 2 * K + (r < K ? slot : K + slot)] = E::one(row, x);
   }
 
   float m, s, M, S;
@@ -526,7 +527,8 @@ __device__ __forceinline__ void decide_slots(int b, int ch, int K, int V, float 
       if (out_q) out_q[o] = (err || !valid) ? NAN : qk;
     }
     for (int j = lane; j <= K; j += kWave)
-      if (err || j != mm) out_tok[static_cast<size_t>(b) * (K + 1) + j] = (!err && j < mm) ? xk : -1;
+      if (err || j != mm)
+        out_tok[static_cast<size_t>(b) * (K + 1) + j] = (!err && j < mm) ? xk : -1;
     if (lane == 0) {
       out_tau[b] = err ? -1 : mm + 1;
       if (out_kv) out_kv[b] = err ? kv0 : kv0 + mm + 1;
@@ -651,7 +653,8 @@ __device__ __forceinline__ void search_in_chunk(const DrawRows<TIn>& R, const Re
   const double excl = off + wave_shift_up1(wi);
   const unsigned long long cross = fb ? 0ull : __ballot(incl > t);
   __syncthreads();   // s_first is rewritten
-  if (lane == 0) sh.s_first[w] = cross ? w * kWave + __ffsll(static_cast<long long>(cross)) - 1 : -1;
+  if (lane == 0)
+    sh.s_first[w] = cross ? w * kWave + __ffsll(static_cast<long long>(cross)) - 1 : -1;
   __syncthreads();
   int first = -1;
 #pragma unroll
@@ -1010,17 +1013,18 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
   // taken from its partials)
   const int aligned = (ns == nd && cs == cd) ? 1 : 0;
   if (ev == nullptr) {
-    hipLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0, stream, t, d,
-                       xtok, K, V, c, ns, cs, part1, gath, cm, nclear, kwmax, temps, dlen, nt);
-    hipLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint>), grid2, block, 0, stream, t, d,
-                       xtok, uni, kv_in, K, V, c, ns, static_cast<const float2*>(part1),
+    hipLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0, stream,
+                       t, d, xtok, K, V, c, ns, cs, part1, gath, cm, nclear, kwmax, temps, dlen,
+                       nt);
+    hipLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint>), grid2, block, 0, stream,
+                       t, d, xtok, uni, kv_in, K, V, c, ns, static_cast<const float2*>(part1),
                        static_cast<const float*>(gath), nd, cd, aligned, cm, polls, out_tok,
                        out_tau, out_kv, out_p, out_q, ka, temps, dlen, nd_wg);
   } else {
     // profiling: the runtime records the events at each kernel's start and end
-    hipExtLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0, stream,
-                          ev[0], ev[1], 0, t, d, xtok, K, V, c, ns, cs, part1, gath, cm, nclear,
-                          kwmax, temps, dlen, nt);
+    hipExtLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0,
+                          stream, ev[0], ev[1], 0, t, d, xtok, K, V, c, ns, cs, part1, gath, cm,
+                          nclear, kwmax, temps, dlen, nt);
     hipExtLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint>), grid2, block, 0, stream,
                           ev[2], ev[3], 0, t, d, xtok, uni, kv_in, K, V, c, ns,
                           static_cast<const float2*>(part1), static_cast<const float*>(gath), nd,
