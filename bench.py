@@ -6,15 +6,16 @@ B=64 requests, K=4 drafts, V=128256, bf16 logits, T=0.7 (the C3 batched-serving 
 target N(0,3^2) + Zipf bias, draft noise std per request ~ U(0.3,2.0)). Four seeded input sets,
 each held in three device copies (12 buffers, 1.77 GB), are rotated so the 256 MB Infinity Cache
 cannot serve any part of a call from an earlier one (the statistics pass leaves only some rows
-in it). The default warmup is long (1000 steps, ~40 ms): the GPU takes several milliseconds of
-sustained load to reach its steady clocks, and 20 steps left the first timed ones ~10 % slower.
+in it). Before the warm-up steps the bench runs the same calls for --settle-ms (default 100 ms,
+untimed, reported as extra.settle_ms): the GPU takes several milliseconds of sustained load to
+reach its steady clocks, and 20 warm-up steps alone left the timed ones ~10 % slower.
 
 Prints ONE JSON line on stdout: verified draft rows/s (B*K per call), the whole call's
 algorithmic HBM rate, the roofline of the dominant kernel (the streaming statistics kernel,
 timed with start/stop events on its own launches inside the timed region), and the fp64 oracle
 timed on this host's cores as a CPU baseline. Diagnostics go to stderr.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 1000]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--settle-ms 100]
 """
 from __future__ import annotations
 
@@ -46,7 +47,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed calls before the warm-up steps, until this much time has passed")
     ap.add_argument("--sets", type=int, default=4, help="distinct input sets")
     ap.add_argument("--copies", type=int, default=3,
                     help="device copies of each input set (all of them are rotated)")
@@ -217,6 +220,15 @@ def main():
         if hip.hipEventCreate(ev_ptr(i)) != 0:
             raise SystemExit("hipEventCreate failed")
 
+    # settle the device's clocks under sustained load (untimed), then the W warm-up steps
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(64):
+            call(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
@@ -266,7 +278,8 @@ def main():
     rows_per_s = B * K / (ms_per_step * 1e-3)
     call_gbps = bytes_per_call / (ms_per_step * 1e-3) / 1e9
 
-    extra = dict(ms_per_step_timed_entry=round(ms_timed_entry, 5),
+    extra = dict(settle_ms=round(settle_ms, 1), settle_calls=n_settle,
+                 ms_per_step_timed_entry=round(ms_timed_entry, 5),
                  ms_per_step_hot_one_set=round(ms_hot, 5),
                  wall_ms_per_step=round(wall / args.steps * 1e3, 5),
                  stats_kernel_us=dict(mean=round(float(stats_ms.mean()) * 1e3, 3),
