@@ -27,9 +27,15 @@ Sources (page titles and sections):
          "パック", "ヒット", "ミス" and the table under "用意を増やせばいい、わけではない".
 
 Pin status: every function is pinned by a CPU test except the parts the pages give no formula
-for (Saguaro's fan-out optimiser and Saguaro sampling), which are not implemented here.
+for (Saguaro's fan-out optimiser and Saguaro sampling), which are not implemented here. The
+near-tie margins and flags are pinned by hand-worked margins on both sides of the 1e-5 threshold
+(accept decisions, bonus and residual draws, the normalisation by the residual mass) and by flag
+counts over seeded uniforms against the exact flag probability in closed form; the accept ratio
+at tiny temperatures by cases where p and q both underflow.
 """
-from .reference import (NEAR_TIE, decode_logits, softmax, residual_weights, inverse_cdf,
+from .reference import (NEAR_TIE, decode_logits, softmax, log_softmax, residual_weights,
+                        inverse_cdf, cdf_margin, accept_ratio, sample_draw_weights,
+                        point_draw_weights, draw_weights, point_weights,
                         verify_sample_request, verify_greedy_request, predict_request,
                         verify_sample, verify_greedy, predict_outcomes, outcome_hit,
                         fanout_offsets, predict_fanout_request, predict_fanout, outcome_slot,
@@ -37,7 +43,9 @@ from .reference import (NEAR_TIE, decode_logits, softmax, residual_weights, inve
                         verify_mixed, ngram_draft_request, ngram_draft, verify_point_request,
                         verify_point)
 
-__all__ = ["NEAR_TIE", "decode_logits", "softmax", "residual_weights", "inverse_cdf",
+__all__ = ["NEAR_TIE", "decode_logits", "softmax", "log_softmax", "residual_weights",
+           "inverse_cdf", "cdf_margin", "accept_ratio", "sample_draw_weights",
+           "point_draw_weights", "draw_weights", "point_weights",
            "verify_sample_request", "verify_greedy_request", "predict_request", "verify_sample",
            "verify_greedy", "predict_outcomes", "outcome_hit", "fanout_offsets",
            "predict_fanout_request", "predict_fanout", "outcome_slot", "fanout_budget",

@@ -8,13 +8,17 @@ m is the first rejected slot (0-based, so m drafts were accepted); tau = m + 1 t
 Readings where the pages leave a step open:
   * temperature: p = softmax(l / T); T = 0 is the greedy rule and has its own entry point;
   * accept slot k iff u_k < r_k with r_k = 1 when p_k(x_k) >= q_k(x_k), else p/q, so a draft the
-    target likes at least as much is always kept whatever u_k in [0,1) is;
+    target likes at least as much is always kept whatever u_k in [0,1) is (evaluated from the
+    log-probabilities, so it holds at any positive T);
   * the residual (or bonus) draw uses the one extra uniform u_K by inverse CDF: the smallest v
     whose running sum C_v exceeds u_K * Z; if round-off leaves none, the last v of positive
     weight; a zero-weight token is never drawn;
   * a draft token outside [0,V), or (sampling) one whose draft logit is -inf, is a row error:
     tau = -1, tokens all -1, kv unchanged, reported probabilities NaN;
-  * kv_out = kv_in + tau (the round advances the committed length by tau).
+  * kv_out = kv_in + tau (the round advances the committed length by tau);
+  * a request is flagged as a near-tie when a decision it took has a margin below NEAR_TIE:
+    |u_k - r_k| for an accept decision, the draw's threshold distance from the ends of the drawn
+    token's interval of the running sum relative to the total mass for the draw.
 """
 from __future__ import annotations
 
@@ -49,6 +53,16 @@ def softmax(logits: np.ndarray, T: float) -> np.ndarray:
     return e / np.sum(e)
 
 
+def log_softmax(logits: np.ndarray, T: float) -> np.ndarray:
+    """Natural log of the temperature softmax: log p_v = l_v/T - max_w l_w/T - log sum_w
+    exp(l_w/T - max l/T). The same quantity as log(softmax(l, T)), but finite wherever p_v > 0 in
+    exact arithmetic: at a tiny T both p_k(x_k) and q_k(x_k) underflow to 0 in float64 while
+    their ratio does not."""
+    z = np.asarray(logits, dtype=np.float64) / np.float64(T)
+    top = np.max(z)
+    return z - top - np.log(np.sum(np.exp(z - top)))
+
+
 def residual_weights(p: np.ndarray, q: np.ndarray) -> np.ndarray:
     """Residual weights max(0, p - q) at the first rejected slot ([SD] stage 4: the replacement
     is drawn from a residual distribution adjusted by both models' probabilities)."""
@@ -73,9 +87,18 @@ def inverse_cdf(w: np.ndarray, u: float):
     return y, C, Z, t
 
 
-def _cdf_margin(C: np.ndarray, Z: float, t: float, y: int) -> float:
+def cdf_margin(C: np.ndarray, Z: float, t: float, y: int) -> float:
+    """Distance of the draw's threshold t = u*Z from the nearer end of token y's interval
+    [C_{y-1}, C_y) of the running sum, as a fraction of the total mass Z (C_{-1} = 0): the
+    relative change of u that would move the draw to another token."""
     lo = float(C[y - 1]) if y > 0 else 0.0
     return min(float(C[y]) - t, t - lo) / Z
+
+
+def accept_ratio(lp: float, lq: float) -> float:
+    """r = min(1, p/q) from log p and log q ([SD] stage 3: a draft the target likes at least as
+    much as the draft model is always kept; otherwise it is kept with probability p/q)."""
+    return 1.0 if lp >= lq else float(np.exp(lp - lq))
 
 
 # ----------------------------------------------------------------------------------------------
@@ -85,51 +108,80 @@ def verify_sample_request(t_rows: np.ndarray, d_rows: np.ndarray, x, u, kv_in: i
 
     t_rows [K+1,V], d_rows [K,V] float64 logits; x [K] draft tokens; u [K+1] uniforms; T > 0.
     Returns a dict with tokens [K+1], tau, kv_out, p_x [K], q_x [K], m (first rejected slot or
-    K), y, resid_mass (Z), margin (smallest decision margin) and flagged.
+    K), y, resid_mass (Z), accept_margins [K] (|u_k - r_k| for the slots decided, NaN for the
+    rest), cdf_margin, margin (the smallest of them), flag_accept, flag_cdf and flagged.
+
+    The ratio r_k = min(1, p_k(x_k)/q_k(x_k)) is taken from the float64 log-probabilities: at a
+    tiny T both probabilities can underflow to 0 while their ratio is still far from 1.
     """
     K = len(x)
     V = t_rows.shape[1]
     x = [int(v) for v in x]
     u = np.asarray(u, dtype=np.float64)
-    out = dict(tokens=np.full(K + 1, -1, np.int64), tau=-1, kv_out=int(kv_in),
-               p_x=np.full(K, np.nan), q_x=np.full(K, np.nan), m=-1, y=-1,
-               resid_mass=np.nan, margin=np.inf, flagged=False, row_error=False)
+    out = _empty_result(K, kv_in)
 
     # a draft token must be a token the draft could have sampled
     if any(v < 0 or v >= V for v in x) or any(np.isneginf(d_rows[k, x[k]]) for k in range(K)):
         out["row_error"] = True
         return out
 
-    p = [softmax(t_rows[k], T) for k in range(K + 1)]
-    q = [softmax(d_rows[k], T) for k in range(K)]
-    P = np.array([p[k][x[k]] for k in range(K)])
-    Q = np.array([q[k][x[k]] for k in range(K)])
-    out["p_x"], out["q_x"] = P, Q
+    lP = np.array([log_softmax(t_rows[k], T)[x[k]] for k in range(K)])
+    lQ = np.array([log_softmax(d_rows[k], T)[x[k]] for k in range(K)])
+    out["p_x"], out["q_x"] = np.exp(lP), np.exp(lQ)
 
     # stage 3: left to right; p >= q always kept, otherwise kept with probability p/q
-    margins = []
+    acc = np.full(K, np.nan)
     m = K
     for k in range(K):
-        r = 1.0 if P[k] >= Q[k] else P[k] / Q[k]
-        margins.append(abs(u[k] - r))
+        r = accept_ratio(lP[k], lQ[k])
+        acc[k] = abs(u[k] - r)
         if not (u[k] < r):
             m = k
             break
 
     # stage 4: residual at the first rejection, or the bonus row when all K drafts were kept
-    w = residual_weights(p[m], q[m]) if m < K else p[K]
-    if not np.sum(w) > 0.0:
-        w = p[m]        # cannot happen in exact arithmetic after a rejection; p_m as fallback
+    w = sample_draw_weights(t_rows, d_rows, m, T)
     y, C, Z, t = inverse_cdf(w, u[K])
-    margins.append(_cdf_margin(C, Z, t, y))
-
     tokens = np.full(K + 1, -1, np.int64)
     tokens[:m] = x[:m]
     tokens[m] = y
-    tau = m + 1
-    out.update(tokens=tokens, tau=tau, kv_out=int(kv_in) + tau, m=m, y=y, resid_mass=Z,
-               margin=float(min(margins)), flagged=bool(min(margins) < NEAR_TIE))
+    out.update(tokens=tokens, tau=m + 1, kv_out=int(kv_in) + m + 1, m=m, y=y, resid_mass=Z)
+    _set_margins(out, acc, cdf_margin(C, Z, t, y))
     return out
+
+
+def sample_draw_weights(t_rows: np.ndarray, d_rows: np.ndarray, m: int, T: float) -> np.ndarray:
+    """The weights the token placed at slot m is drawn from ([SD] stage 4): the residual
+    max(0, p_m - q_m) when the draft at m was rejected (m < K), the extra target row p_K when all
+    K drafts were kept (m = K); p_m if round-off leaves a residual without mass (impossible in
+    exact arithmetic: a rejection means q_m(x_m) > p_m(x_m), so the residual holds at least
+    q_m(x_m) - p_m(x_m))."""
+    K = d_rows.shape[0]
+    p = softmax(t_rows[m], T)
+    w = residual_weights(p, softmax(d_rows[m], T)) if m < K else p
+    return w if np.sum(w) > 0.0 else p
+
+
+def _empty_result(K: int, kv_in: int) -> dict:
+    """A request's outputs before anything is decided (also those of a row error)."""
+    return dict(tokens=np.full(K + 1, -1, np.int64), tau=-1, kv_out=int(kv_in),
+                p_x=np.full(K, np.nan), q_x=np.full(K, np.nan), m=-1, y=-1,
+                resid_mass=np.nan, accept_margins=np.full(K, np.nan), cdf_margin=np.inf,
+                margin=np.inf, flagged=False, flag_accept=False, flag_cdf=False,
+                row_error=False)
+
+
+def _set_margins(out: dict, accept_margins: np.ndarray, cdf: float) -> None:
+    """Decision margins and near-tie flags of a request: accept_margins[k] = |u_k - r_k| for the
+    slots actually decided (NaN for the others), cdf = the draw's normalised CDF gap. A margin
+    below NEAR_TIE flags the request: its decisions then depend on rounding below the agreed
+    precision, and only their validity is comparable."""
+    taken = accept_margins[~np.isnan(accept_margins)]
+    flag_accept = bool(taken.size and np.min(taken) < NEAR_TIE)
+    flag_cdf = bool(cdf < NEAR_TIE)
+    out.update(accept_margins=accept_margins, cdf_margin=float(cdf),
+               margin=float(min(np.min(taken) if taken.size else np.inf, cdf)),
+               flag_accept=flag_accept, flag_cdf=flag_cdf, flagged=flag_accept or flag_cdf)
 
 
 def verify_greedy_request(t_rows: np.ndarray, x, kv_in: int):
@@ -184,12 +236,14 @@ def verify_mixed_request(t_rows: np.ndarray, d_rows: np.ndarray, x, u, kv_in: in
         else:
             p_x = np.array([1.0 if int(x[k]) == r["g"][k] else 0.0 for k in range(K)])
             q_x = np.ones(K)
-        r.update(p_x=p_x, q_x=q_x, margin=np.inf, flagged=False, resid_mass=np.nan)
-        return r
+        out = _empty_result(K, kv_in)
+        out.update(r)
+        out.update(p_x=p_x, q_x=q_x)
+        return out
     if not temperature_is_valid(T):
-        return dict(tokens=np.full(K + 1, -1, np.int64), tau=-1, kv_out=int(kv_in),
-                    p_x=np.full(K, np.nan), q_x=np.full(K, np.nan), m=-1, y=-1,
-                    resid_mass=np.nan, margin=np.inf, flagged=False, row_error=True)
+        out = _empty_result(K, kv_in)
+        out["row_error"] = True
+        return out
     return verify_sample_request(t_rows, d_rows, x, u, kv_in, float(T))
 
 
@@ -372,9 +426,7 @@ def verify_point_request(t_rows: np.ndarray, x, n: int, u, kv_in: int, T: float)
     V = t_rows.shape[1]
     x = [int(v) for v in x]
     u = np.asarray(u, dtype=np.float64)
-    out = dict(tokens=np.full(K + 1, -1, np.int64), tau=-1, kv_out=int(kv_in),
-               p_x=np.full(K, np.nan), q_x=np.full(K, np.nan), m=-1, y=-1,
-               resid_mass=np.nan, margin=np.inf, flagged=False, row_error=False)
+    out = _empty_result(K, kv_in)
     n = int(n)
     if n < 0 or n > K or any(v < 0 or v >= V for v in x[:n]):
         out["row_error"] = True
@@ -390,39 +442,41 @@ def verify_point_request(t_rows: np.ndarray, x, n: int, u, kv_in: int, T: float)
         y = g[m]
         out["p_x"][:n] = [1.0 if x[k] == g[k] else 0.0 for k in range(n)]
         out["q_x"][:n] = 1.0
-        margin = np.inf
         Z = np.nan
     else:
-        p = [softmax(t_rows[k], T) for k in range(n + 1)]
-        P = np.array([p[k][x[k]] for k in range(n)])
-        out["p_x"][:n] = P
+        lP = np.array([log_softmax(t_rows[k], T)[x[k]] for k in range(n)])
+        out["p_x"][:n] = np.exp(lP)
         out["q_x"][:n] = 1.0
-        margins = []
+        acc = np.full(K, np.nan)
         m = n
         for k in range(n):
-            r = min(1.0, P[k])          # q_k(x_k) = 1
-            margins.append(abs(u[k] - r))
+            r = accept_ratio(lP[k], 0.0)          # log q_k(x_k) = 0
+            acc[k] = abs(u[k] - r)
             if not (u[k] < r):
                 m = k
                 break
-        if m < n:
-            q_m = np.zeros(V)
-            q_m[x[m]] = 1.0
-            w = residual_weights(p[m], q_m)
-            if not np.sum(w) > 0.0:
-                w = p[m]
-        else:
-            w = p[n]
+        w = point_draw_weights(t_rows, x, n, m, T)
         y, C, Z, t = inverse_cdf(w, u[K])
-        margins.append(_cdf_margin(C, Z, t, y))
-        margin = float(min(margins))
+        _set_margins(out, acc, cdf_margin(C, Z, t, y))
 
     tokens = np.full(K + 1, -1, np.int64)
     tokens[:m] = x[:m]
     tokens[m] = y
-    out.update(tokens=tokens, tau=m + 1, kv_out=int(kv_in) + m + 1, m=m, y=y, resid_mass=Z,
-               margin=margin, flagged=bool(margin < NEAR_TIE))
+    out.update(tokens=tokens, tau=m + 1, kv_out=int(kv_in) + m + 1, m=m, y=y, resid_mass=Z)
     return out
+
+
+def point_draw_weights(t_rows: np.ndarray, x, n: int, m: int, T: float) -> np.ndarray:
+    """Weights of the token placed at slot m for a point-mass draft of n tokens: the residual
+    max(0, p_m - q_m) with q_m the point mass at x_m, i.e. p_m without x_m, when m < n; the row
+    p_n when all n drafts were kept; p_m if round-off leaves the residual without mass."""
+    p = softmax(t_rows[m], T)
+    if m >= n:
+        return p
+    q = np.zeros_like(p)
+    q[int(x[m])] = 1.0
+    w = residual_weights(p, q)
+    return w if np.sum(w) > 0.0 else p
 
 
 # ----------------------------------------------------------------------------------------------
@@ -507,6 +561,19 @@ def verify_point(target, dtype, tokens, lens, uniforms, kv_len, T, requests=None
     return _stack(res, idx, K, sample=True)
 
 
+def draw_weights(target, draft, dtype, b: int, m: int, T):
+    """The sampling draw's weights for request b had m drafts been kept (sample_draw_weights on
+    the stored logits at the float32 temperature the device gets)."""
+    return sample_draw_weights(decode_logits(target[b], dtype), decode_logits(draft[b], dtype), m,
+                               float(np.float32(T)))
+
+
+def point_weights(target, dtype, tokens, n: int, b: int, m: int, T):
+    """point_draw_weights of request b (n drafts) had m of them been kept."""
+    return point_draw_weights(decode_logits(target[b], dtype), tokens[b], n, m,
+                              float(np.float32(T)))
+
+
 def _stack(res, idx, K, sample):
     d = dict(requests=np.array(idx),
              tokens=np.stack([r["tokens"] for r in res]),
@@ -518,6 +585,10 @@ def _stack(res, idx, K, sample):
     if sample:
         d.update(p_x=np.stack([r["p_x"] for r in res]), q_x=np.stack([r["q_x"] for r in res]),
                  margin=np.array([r["margin"] for r in res]),
+                 accept_margins=np.stack([r["accept_margins"] for r in res]),
+                 cdf_margin=np.array([r["cdf_margin"] for r in res]),
+                 flag_accept=np.array([r["flag_accept"] for r in res]),
+                 flag_cdf=np.array([r["flag_cdf"] for r in res]),
                  flagged=np.array([r["flagged"] for r in res]),
                  resid_mass=np.array([r["resid_mass"] for r in res]))
     else:
