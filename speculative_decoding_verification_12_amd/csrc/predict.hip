@@ -17,7 +17,7 @@
 //  1. predict_stats_kernel: a workgroup per (request, slot, chunk), in chunks small enough that
 //     the grid runs in several rounds of workgroups (so one workgroup's arithmetic overlaps the
 //     loads of others). It streams its chunk once and stores the chunk's maximum, at T > 0 its
-//     sum of 2^(l*c - fl(max*c)), and the maxima of its four waves. No workgroup waits for
+//     sum of 2^((l - max) c), and the maxima of its four waves. No workgroup waits for
 //     another: the kernel boundary is the only synchronisation.
 //  2. predict_select_kernel: a workgroup of eight waves per slot merges the chunk statistics into
 //     the row's (M, S) and selects the keys from the wave maxima (select_keys: only the waves
@@ -90,13 +90,12 @@ __global__ __launch_bounds__(kSelectWaves * kWave) void predict_select_kernel(
     float lm = a0.x;
     for (int j = lane + kWave; j < nchunk; j += kWave) lm = fmaxf(lm, pr[j].x);
     const float Mr = wave_max(lm);
-    const float mc = Mr * c;
     double ls = 0.0;
     if (c > 0.f) {
-      if (a0.x > -INFINITY) ls += static_cast<double>(a0.y) * fast_exp2(a0.x * c - mc);
+      if (a0.x > -INFINITY) ls += static_cast<double>(a0.y) * rel_exp2(a0.x, Mr, c);
       for (int j = lane + kWave; j < nchunk; j += kWave) {
         const float2 a = pr[j];
-        if (a.x > -INFINITY) ls += static_cast<double>(a.y) * fast_exp2(a.x * c - mc);
+        if (a.x > -INFINITY) ls += static_cast<double>(a.y) * rel_exp2(a.x, Mr, c);
       }
     }
     return RowStat{Mr, 0.f, wave_sum(ls)};

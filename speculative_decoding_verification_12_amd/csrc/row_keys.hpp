@@ -1,7 +1,7 @@
 // Row statistics and top-key selection shared by the verification and outcome-key kernels.
 //
 // The statistics of a logit row at temperature T (c = log2(e)/T): its maximum M and
-// S = sum 2^(l*c - fl(M*c)), streamed in chunks (one workgroup each) and merged afterwards. The
+// S = sum 2^((l - M) c), streamed in chunks (one workgroup each) and merged afterwards. The
 // key selection picks a row's top tokens from the per-wave maxima that pass left behind,
 // re-reading only the waves that can hold one.
 #pragma once
@@ -12,7 +12,7 @@
 namespace sv {
 
 // ------------------------------------------------------------------------------ statistics
-// Folds n values into a running (m, s) where s = sum 2^(l*c - fl32(m*c)).
+// Folds n values into a running (m, s) where s = sum 2^((l - m) c).
 // With kSum false only the maximum is kept (s stays 0).
 template <bool kSum = true, int n>
 __device__ __forceinline__ void absorb(const float (&v)[n], float c, float& m, float& s) {
@@ -24,13 +24,12 @@ __device__ __forceinline__ void absorb(const float (&v)[n], float c, float& m, f
     return;
   }
   if (bm > m) {
-    s *= fast_exp2(m * c - bm * c);   // s is 0 while m is -inf, so the factor is then moot
+    s *= rel_exp2(m, bm, c);   // s is 0 while m is -inf, so the factor (0) is then moot
     m = bm;
   }
   if (m > -INFINITY) {
-    const float mc = m * c;
 #pragma unroll
-    for (int j = 0; j < n; ++j) s += fast_exp2(fmaf(v[j], c, -mc));
+    for (int j = 0; j < n; ++j) s += rel_exp2(v[j], m, c);
   }
 }
 
@@ -84,7 +83,7 @@ __device__ __forceinline__ void block_stats(float m, float s, float c, float* sm
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   const float wm = wave_max(m);
   if (wave_max_out != nullptr && lane == 0) wave_max_out[w] = wm;
-  const float sc = (m > -INFINITY) ? s * fast_exp2(m * c - wm * c) : 0.f;
+  const float sc = (m > -INFINITY) ? s * rel_exp2(m, wm, c) : 0.f;
   const float ws = wave_sum(sc);
   if (lane == 0) {
     sm[w] = wm;
@@ -98,7 +97,7 @@ __device__ __forceinline__ void block_stats(float m, float s, float c, float* sm
     S = 0.f;
 #pragma unroll
     for (int i = 0; i < kWaves; ++i)
-      if (sm[i] > -INFINITY) S += ss[i] * fast_exp2(sm[i] * c - M * c);
+      if (sm[i] > -INFINITY) S += ss[i] * rel_exp2(sm[i], M, c);
   }
 }
 
@@ -151,7 +150,7 @@ __device__ __forceinline__ void merge_running(float& rv, int& ri, int Fp, Offer 
   ri = ni;
 }
 
-struct RowStat {   // a row's merged statistics: max and sum of 2^(l*c - fl(max*c))
+struct RowStat {   // a row's merged statistics: max and sum of 2^((l - max) c)
   float M;
   float pad;
   double S;
@@ -160,7 +159,7 @@ struct RowStat {   // a row's merged statistics: max and sum of 2^(l*c - fl(max*
 
 // The keys of one row: the best Fp tokens in the order (value desc, id asc), the token xk
 // skipped (xk < 0: none), the first nkeys of the rest written to keys_out[0..nkeys) with, when
-// prob_out is given, q(key) = 2^(l*c - fl(M*c)) / S from the row's statistics (c > 0), or at
+// prob_out is given, q(key) = 2^((l - M) c) / S from the row's statistics (c > 0), or at
 // c = 0 the temperature-zero probability: 1 for the rank-0 token, 0 for any other. The row's
 // statistics come from row_stat(), called by the 64 lanes of wave 0 just before the keys are
 // written (so a caller can merge them there, after its loads have long arrived).
@@ -357,7 +356,7 @@ __device__ __forceinline__ void select_keys(const TIn* __restrict__ row, int V, 
     if (prob_out)
       prob_out[pos] =
           c > 0.f ? static_cast<float>(
-                        exp2_wide(static_cast<double>(pvv) * c - static_cast<double>(rs.M * c)) /
+                        exp2_wide(static_cast<double>(pvv - rs.M) * static_cast<double>(c)) /
                         rs.S)
                   : (lane == 0 ? 1.f : 0.f);
   }

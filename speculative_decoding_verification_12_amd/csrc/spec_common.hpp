@@ -88,6 +88,15 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p, int i) {
 // below the resolution any sum here can see)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 2^((l - M) c): the weight of logit l against a reference M (a row's or a running maximum) at
+// c = log2(e)/T. The difference is taken before the scaling, so the reference's own term is
+// exactly 1 and a logit below it gives a value in [0, 1] at every temperature: with the product
+// fl(M c) as the reference instead, its rounding error (|M c| 2^-24) becomes the exponent of the
+// maximum's own term, which overflows or underflows once c is large (T below ~1e-9 at |M| ~ 10).
+__device__ __forceinline__ float rel_exp2(float l, float M, float c) {
+  return fast_exp2((l - M) * c);
+}
+
 // ------------------------------------------------------------------------------ row layout
 struct RowSpan {
   int head;   // elements [0, head) precede the first 16-byte boundary

@@ -9,7 +9,7 @@
 //
 // Two launches, both HBM-streaming, no matrix cores (nothing here is a contraction):
 //  1. sample_stats_kernel: one workgroup per (request, row, chunk of 16-byte vectors). Each
-//     thread keeps a running max m and a sum of 2^(l*c - fl(m*c)), c = log2(e)/T, with one
+//     thread keeps a running max m and a sum of 2^((l - m) c), c = log2(e)/T, with one
 //     hardware exp2 per element; wave butterflies and LDS reduce to the chunk's (M, S), written
 //     with a plain store. The workgroup whose chunk holds a slot's draft token also records
 //     that token's logit. No workgroup waits on another: the kernel boundary is the only
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
 
 // ------------------------------------------------------------------------------ draw
 // Weights of the draw over row m: w = max(0, p - q) (residual, m < K) or w = p (bonus, m == K),
-// with p = 2^(l*c - mc_t) / S_t and q likewise. `use_p` switches to w = p, the fallback when
+// with p = 2^((l - M_t) c) / S_t and q likewise. `use_p` switches to w = p, the fallback when
 // round-off leaves no residual mass.
 // With a point-mass draft (kMask) the residual max(0, p - q) is p with the draft token `mask`
 // removed (mask < 0: the bonus row, w = p).
@@ -233,10 +233,10 @@ struct DrawRows {
 template <bool kMask, typename TIn>
 __device__ __forceinline__ float weight_one(const DrawRows<TIn>& R, const ReqState& st, float c,
                                             int tok, bool use_p, float& p) {
-  p = fast_exp2(fmaf(Elem<TIn>::one(R.t, tok), c, -st.mc_t)) * st.inv_t;
+  p = rel_exp2(Elem<TIn>::one(R.t, tok), st.M_t, c) * st.inv_t;
   if constexpr (kMask) return (tok == R.mask && !use_p) ? 0.f : p;
   if (!R.resid || use_p) return p;
-  const float q = fast_exp2(fmaf(Elem<TIn>::one(R.d, tok), c, -st.mc_d)) * st.inv_d;
+  const float q = rel_exp2(Elem<TIn>::one(R.d, tok), st.M_d, c) * st.inv_d;
   return fmaxf(p - q, 0.f);
 }
 
@@ -250,7 +250,7 @@ __device__ __forceinline__ void weight_group(const DrawRows<TIn>& R, const ReqSt
   float lt[N];
   E::unpack(qt, lt);
 #pragma unroll
-  for (int j = 0; j < N; ++j) p[j] = fast_exp2(fmaf(lt[j], c, -st.mc_t)) * st.inv_t;
+  for (int j = 0; j < N; ++j) p[j] = rel_exp2(lt[j], st.M_t, c) * st.inv_t;
   if constexpr (kMask) {
     const int tok0 = R.sp.head + v * N;
 #pragma unroll
@@ -271,7 +271,7 @@ __device__ __forceinline__ void weight_group(const DrawRows<TIn>& R, const ReqSt
   }
 #pragma unroll
   for (int j = 0; j < N; ++j)
-    w[j] = fmaxf(p[j] - fast_exp2(fmaf(ld[j], c, -st.mc_d)) * st.inv_d, 0.f);
+    w[j] = fmaxf(p[j] - rel_exp2(ld[j], st.M_d, c) * st.inv_d, 0.f);
 }
 
 template <typename TIn>
@@ -423,15 +423,14 @@ __device__ __forceinline__ void merge_row_stats_rd(Rd rd, bool has, int n, int W
   if (has)
     for (int j = i + kHeld * W; j < n; j += W) lm = fmaxf(lm, rd(j).x);
   Mr = group_reduce(lm, W, OpMax{});
-  const float mc = Mr * c;
   double ls = 0.0;
 #pragma unroll
   for (int h = 0; h < kHeld; ++h)
-    if (hm[h] > -INFINITY) ls += static_cast<double>(hs[h]) * fast_exp2(hm[h] * c - mc);
+    if (hm[h] > -INFINITY) ls += static_cast<double>(hs[h]) * rel_exp2(hm[h], Mr, c);
   if (has)
     for (int j = i + kHeld * W; j < n; j += W) {
       const float2 q = rd(j);
-      if (q.x > -INFINITY) ls += static_cast<double>(q.y) * fast_exp2(q.x * c - mc);
+      if (q.x > -INFINITY) ls += static_cast<double>(q.y) * rel_exp2(q.x, Mr, c);
     }
   Sr = group_reduce(ls, W, OpAdd{});
 }
@@ -500,21 +499,29 @@ __device__ __forceinline__ void decide_slots(int b, int ch, int K, int V, float 
   bool keep = true;
   float pk = 0.f, qk = 0.f;
   if (valid && !bad) {
-    // log2 p_k(x_k) = l*c - fl(M*c) - log2 S of the target row, log2 q_k(x_k) likewise (0 for a
-    // point-mass draft). In float32 and the log domain: accurate to ~3e-6 relative in p, q and
-    // the ratio (inside the 1e-5 margin that flags a decision as a near-tie), and neither p nor
-    // q can underflow the ratio (a float64 evaluation cost ~1 us on every draw workgroup's
-    // critical path). S >= 1: the row's maximum contributes 2^0.
-    const float lp = fmaf(lt, c, -(sh.row_m[lane] * c)) -
-                     __builtin_amdgcn_logf(static_cast<float>(sh.row_s[lane]));
-    float lq = 0.f;
-    if constexpr (!kPoint)
-      lq = fmaf(ld, c, -(sh.row_m[K + 1 + lane] * c)) -
-           __builtin_amdgcn_logf(static_cast<float>(sh.row_s[K + 1 + lane]));
+    // log2 p_k(x_k) = (l - M) c - log2 S of the target row, with l - M the draft token's gap
+    // below the row maximum; log2 q_k(x_k) likewise (0 for a point-mass draft), and
+    // log2(p/q) = (g_t - g_d) c + log2 S_d - log2 S_t from the two gaps, which stays finite (or
+    // -inf for a masked target logit) at every temperature. In float32 and the log domain:
+    // accurate to ~3e-6 relative in p, q and the ratio (inside the 1e-5 margin that flags a
+    // decision as a near-tie), and neither p nor q can underflow the ratio (a float64
+    // evaluation cost ~1 us on every draw workgroup's critical path). S >= 1: the row's maximum
+    // contributes 2^0.
+    const float gt = lt - sh.row_m[lane];
+    const float lst = __builtin_amdgcn_logf(static_cast<float>(sh.row_s[lane]));
+    const float lp = gt * c - lst;
+    float lr = lp;   // log2 (p/q)
+    if constexpr (!kPoint) {
+      const float gd = ld - sh.row_m[K + 1 + lane];
+      const float lsd = __builtin_amdgcn_logf(static_cast<float>(sh.row_s[K + 1 + lane]));
+      qk = fast_exp2(gd * c - lsd);
+      lr = (gt - gd) * c + (lsd - lst);
+    } else {
+      qk = 1.f;
+    }
     pk = fast_exp2(lp);
-    qk = kPoint ? 1.f : fast_exp2(lq);
     // kept iff u < min(1, p/q): p >= q is kept for every u in [0,1)
-    keep = lp >= lq || uk < fast_exp2(lp - lq);
+    keep = lr >= 0.f || uk < fast_exp2(lr);
   }
   const bool err = nb_bad || __ballot(bad) != 0ull;
   const unsigned long long rej = __ballot(valid && !keep);
@@ -538,9 +545,9 @@ __device__ __forceinline__ void decide_slots(int b, int ch, int K, int V, float 
     ReqState st;
     st.m = err ? -1 : mm;
     st.xm = (kPoint && mm < nb) ? xm : -1;
-    st.mc_t = sh.row_m[mm] * c;
+    st.M_t = sh.row_m[mm];
     st.inv_t = 1.f / static_cast<float>(sh.row_s[mm]);
-    st.mc_d = (!kPoint && mm < K) ? sh.row_m[K + 1 + mm] * c : 0.f;
+    st.M_d = (!kPoint && mm < K) ? sh.row_m[K + 1 + mm] : 0.f;
     st.inv_d = (!kPoint && mm < K) ? 1.f / static_cast<float>(sh.row_s[K + 1 + mm]) : 0.f;
     sh.s_st = st;
   }
@@ -700,12 +707,12 @@ __device__ __forceinline__ void search_in_chunk(const DrawRows<TIn>& R, const Re
     }
     float we = 0.f;
     if (has) {
-      const float p = fast_exp2(fmaf(lt, c, -st.mc_t)) * st.inv_t;
+      const float p = rel_exp2(lt, st.M_t, c) * st.inv_t;
       if constexpr (kPoint)
         we = (tok == R.mask && !use_p) ? 0.f : p;
       else
         we = (!R.resid || use_p) ? p
-                                 : fmaxf(p - fast_exp2(fmaf(ld, c, -st.mc_d)) * st.inv_d, 0.f);
+                                 : fmaxf(p - rel_exp2(ld, st.M_d, c) * st.inv_d, 0.f);
     }
     const double cum = sh.s_cb + wave_scan_incl(static_cast<double>(we));
     const unsigned long long pos = __ballot(we > 0.f);
@@ -872,7 +879,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
   const float u_draw = uni[static_cast<size_t>(b) * (K + 1) + K];
 
   // ---- every draft kept (the weights are p_m of the extra row): when the statistics pass cut
-  // the row into the draw's chunks, chunk j's mass is S_j 2^(fl(M_j c) - fl(M c)) / S from its
+  // the row into the draw's chunks, chunk j's mass is S_j 2^((M_j - M) c) / S from its
   // partial, so no chunk is read for the masses and nothing is exchanged; only the workgroup of
   // the chunk holding u*Z reads its chunk, to find the token
   if (aligned && st.m == nb && !R.resid && R.mask < 0) {
@@ -882,8 +889,8 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
         const float2 q = pr[j];
         const double P = q.x > -INFINITY
                              ? static_cast<double>(q.y) *
-                                   exp2_wide(static_cast<double>(q.x * c) -
-                                             static_cast<double>(st.mc_t)) *
+                                   exp2_wide(static_cast<double>(q.x - st.M_t) *
+                                             static_cast<double>(c)) *
                                    static_cast<double>(st.inv_t)
                              : 0.0;
         sh.s_cm[j] = make_double2(P, P);

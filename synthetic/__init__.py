@@ -8,9 +8,9 @@ histories for prompt-lookup drafting (no matching code).
 """
 from .bf16 import f32_to_bf16_bits, bf16_bits_to_f32
 from .workloads import (CONFIGS, Workload, make_workload, make_tiny_random, config_by_name,
-                        WORKLOAD_SEED_ROOT)
+                        WORKLOAD_SEED_ROOT, as_greedy)
 from .contexts import make_contexts, make_runs
 
 __all__ = ["f32_to_bf16_bits", "bf16_bits_to_f32", "CONFIGS", "Workload", "make_workload",
            "make_tiny_random", "config_by_name", "WORKLOAD_SEED_ROOT", "make_contexts",
-           "make_runs"]
+           "make_runs", "as_greedy"]

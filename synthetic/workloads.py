@@ -31,7 +31,7 @@ The generators hold no verification arithmetic; they only create inputs.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 from typing import Optional
 
 import numpy as np
@@ -196,6 +196,14 @@ def make_workload(cid: int, round_idx: int = 0, mode: str = "sample", *, B: int 
     return Workload(config=cfg, round=round_idx, mode=mode, B=B, K=K, V=V, dtype=dtype, T=T32,
                     target=target, draft=draft, tokens=tokens, uniforms=uniforms,
                     kv_len=kv_len, F=cfg.F, forced=forced, sigma=sigma)
+
+
+def as_greedy(wl: Workload) -> Workload:
+    """The greedy-mode workload of the same seeds: identical logits, uniforms and KV lengths, T = 0
+    and the draft tokens the draft's top choices (what make_workload(..., "greedy") builds, without
+    generating the logits again)."""
+    tokens = np.argmax(_values(wl.draft, wl.dtype), axis=-1).astype(np.int32)
+    return replace(wl, mode="greedy", T=np.float32(0.0), tokens=tokens)
 
 
 def make_tiny_random(seed: int, B: int, K: int, V: int, *, mode: str = "sample",

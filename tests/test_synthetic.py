@@ -109,3 +109,15 @@ def test_tiny_random_has_ties_and_masks():
     vals = wl.target_values()
     assert np.isneginf(vals).any() and np.isfinite(vals).all(axis=-1).sum() < vals.shape[0] * 4
     assert ((wl.tokens < 0) | (wl.tokens >= 8)).any()
+
+
+@pytest.mark.parametrize("cid,kw", [(1, {}), (3, dict(B=4, V=3001)), (4, dict(B=4, V=2000)),
+                                    (5, dict(B=3, V=1001))])
+def test_as_greedy_equals_generated_greedy(cid, kw):
+    """The greedy view of a sampling workload is the greedy workload of the same seeds."""
+    from synthetic import as_greedy
+    a = as_greedy(make_workload(cid, 3, **kw))
+    b = make_workload(cid, 3, "greedy", **kw)
+    for f in ("target", "draft", "tokens", "uniforms", "kv_len", "forced"):
+        assert np.array_equal(getattr(a, f), getattr(b, f)), f
+    assert a.T == b.T == 0 and a.mode == b.mode == "greedy"
