@@ -33,7 +33,8 @@
  *   - -inf logits are masked tokens (probability 0). NaN or +inf logits, or a row whose logits
  *     are all -inf, give undefined (but in-bounds, terminating) results.
  *   - The caller owns every buffer, including the workspace. The library allocates nothing and
- *     keeps no mutable global state; calls only enqueue work on `stream` and return. Outputs
+ *     keeps no mutable global state (the one exception is spec_verify_sample_noalloc's fixed
+ *     per-GPU scratch array, below); calls only enqueue work on `stream` and return. Outputs
  *     are valid after the stream is synchronised. Every element of every non-null output is
  *     written.
  *   - Workspace: size from spec_workspace_bytes(B,K,V,F) (one size serves every entry point),
@@ -74,13 +75,14 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 8
+#define SPEC_ABI_VERSION 9
 #define SPEC_MAX_K 64
 #define SPEC_MAX_NGRAM 64
 #define SPEC_MAX_CONTEXT 1073741824 /* 2^30 tokens per context row */
 #define SPEC_MAX_F 16
 #define SPEC_MAX_V 4194304 /* 2^22 */
 #define SPEC_DEFAULT_WAIT_POLLS 16384
+#define SPEC_NOALLOC_SCRATCH_BYTES 16777216 /* 16 MiB per GPU, spec_verify_sample_noalloc */
 
 /* logit element types */
 #define SPEC_F32 0
@@ -93,6 +95,7 @@ extern "C" {
 #define SPEC_ERR_TEMPERATURE (-3)
 #define SPEC_ERR_WORKSPACE (-4)
 #define SPEC_ERR_HIP (-5)
+#define SPEC_ERR_SCRATCH (-6)
 
 /* Returns SPEC_ABI_VERSION of the built library. */
 int spec_abi_version(void);
@@ -148,6 +151,28 @@ int spec_verify_sample_ex(const void* target_logits, const void* draft_logits, i
                           float* out_p, float* out_q,
                           void* workspace, size_t workspace_bytes, hipStream_t stream,
                           hipEvent_t* events, int wait_polls);
+
+/* spec_verify_sample without a workspace argument, for callers that cannot allocate one: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine): its workspace is a
+ * fixed array of SPEC_NOALLOC_SCRATCH_BYTES (16 MiB) in device memory, one per GPU, loaded with
+ * the library's code and held until the process ends; its device address is looked up once
+ * per device on the first call there. Every other argument, every output and every result are
+ * those of spec_verify_sample, bit for bit (the same kernels).
+ *   Limit: sizes for which spec_workspace_bytes(B, K, V, 1) exceeds SPEC_NOALLOC_SCRATCH_BYTES
+ *   (e.g. B = 64, K = 4, V = 128256 needs 1 MiB; B = 256, K = 8, V = 152064 needs 8.8 MiB) are
+ *   rejected with SPEC_ERR_SCRATCH before anything touches the device.
+ *   Concurrency: every call on one GPU shares that GPU's array, which keeps the last call's
+ *   contents (nothing in it needs clearing: each call clears what its draw polls). Calls that
+ *   may overlap on one GPU (two streams, or two host threads without ordering) race; use
+ *   spec_verify_sample with a workspace of each caller's own for those.
+ *   Errors: as spec_verify_sample (without SPEC_ERR_WORKSPACE), SPEC_ERR_SCRATCH as above, and
+ *   SPEC_ERR_HIP if the device or the array's address cannot be obtained. */
+int spec_verify_sample_noalloc(const void* target_logits, const void* draft_logits, int dtype,
+                               const int32_t* draft_tokens, const float* uniforms,
+                               const int32_t* kv_len_in, int B, int K, int V, float temperature,
+                               int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len,
+                               float* out_p, float* out_q, hipStream_t stream);
 
 /* spec_verify_sample plus the outcome keys of every slot, computed from the same pass over the
  * draft rows ([SSD] section "1. Outcome Prediction": the keys are the draft's top logits; reading

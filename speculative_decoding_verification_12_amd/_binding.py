@@ -19,8 +19,9 @@ SPEC_MAX_V = 1 << 22
 SPEC_MAX_NGRAM = 64
 SPEC_MAX_CONTEXT = 1 << 30
 SPEC_DEFAULT_WAIT_POLLS = 16384
+SPEC_NOALLOC_SCRATCH_BYTES = 16 << 20
 STATUS = {0: "SPEC_OK", -1: "SPEC_ERR_ARG", -2: "SPEC_ERR_DTYPE", -3: "SPEC_ERR_TEMPERATURE",
-          -4: "SPEC_ERR_WORKSPACE", -5: "SPEC_ERR_HIP"}
+          -4: "SPEC_ERR_WORKSPACE", -5: "SPEC_ERR_HIP", -6: "SPEC_ERR_SCRATCH"}
 
 EXPORTS = ("spec_abi_version", "spec_status_string", "spec_workspace_bytes",
            "spec_workspace_init", "spec_verify_sample", "spec_verify_sample_ex",
@@ -28,7 +29,7 @@ EXPORTS = ("spec_abi_version", "spec_status_string", "spec_workspace_bytes",
            "spec_verify_greedy_ex",
            "spec_predict_outcomes",
            "spec_predict_fanout", "spec_outcome_lookup", "spec_kv_rewind", "spec_ngram_draft",
-           "spec_verify_point")
+           "spec_verify_point", "spec_verify_sample_noalloc")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _ll = ctypes.c_longlong
@@ -41,6 +42,8 @@ _SIGNATURES = {
                                 _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_sample_ex": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _f,
                                    _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _i]),
+    "spec_verify_sample_noalloc": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _f,
+                                        _vp, _vp, _vp, _vp, _vp, _vp]),
     "spec_verify_sample_keys": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _f, _i, _i,
                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_mixed": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i,
@@ -207,6 +210,34 @@ def spec_verify_sample(target, draft, draft_tokens, uniforms, kv_len, temperatur
         ev = None if events is None else ctypes.cast(events, ctypes.c_void_p)
         polls = -1 if wait_polls is None else int(wait_polls)
         _check("spec_verify_sample_ex", lib.spec_verify_sample_ex(*args, ev, polls))
+    return out
+
+
+def spec_verify_sample_noalloc(target, draft, draft_tokens, uniforms, kv_len, temperature,
+                               out=None):
+    """spec_verify_sample on the library's fixed per-GPU scratch array instead of a workspace
+    (the call allocates nothing). Returns dict(tokens, tau, kv_len, p, q); the caller may pass
+    preallocated outputs in `out`."""
+    torch = _torch()
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    _need(target, "target_logits", (B, K + 1, V), target.dtype, dev)
+    _need(draft, "draft_logits", (B, K, V), target.dtype, dev)
+    _need(draft_tokens, "draft_tokens", (B, K), torch.int32, dev)
+    _need(uniforms, "uniforms", (B, K + 1), torch.float32, dev)
+    if kv_len is not None:
+        _need(kv_len, "kv_len", (B,), torch.int32, dev)
+    if out is None:
+        out = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                   tau=torch.empty(B, dtype=torch.int32, device=dev),
+                   kv_len=torch.empty(B, dtype=torch.int32, device=dev),
+                   p=torch.empty((B, K), dtype=torch.float32, device=dev),
+                   q=torch.empty((B, K), dtype=torch.float32, device=dev))
+    _check("spec_verify_sample_noalloc", load_library().spec_verify_sample_noalloc(
+        _ptr(target), _ptr(draft), _dtype_code(target), _ptr(draft_tokens), _ptr(uniforms),
+        _ptr(kv_len), B, K, V, float(temperature), _ptr(out["tokens"]), _ptr(out["tau"]),
+        _ptr(out.get("kv_len")), _ptr(out.get("p")), _ptr(out.get("q")), _stream(dev)))
     return out
 
 

@@ -23,6 +23,9 @@ extern "C" const char* spec_status_string(int status) {
     case SPEC_ERR_TEMPERATURE: return "invalid temperature for this entry point";
     case SPEC_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case SPEC_ERR_HIP: return "HIP launch failed";
+    case SPEC_ERR_SCRATCH:
+      return "sizes need more scratch than spec_verify_sample_noalloc's fixed per-GPU array "
+             "(SPEC_NOALLOC_SCRATCH_BYTES) holds";
     default: return "unknown status";
   }
 }

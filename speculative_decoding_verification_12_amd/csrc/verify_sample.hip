@@ -36,6 +36,8 @@
 // only, so the draw re-reads target row m from the cache and draft row m from HBM at once.
 #include <hip/hip_ext.h>
 
+#include <mutex>
+
 #include "api_common.hpp"
 #include "row_keys.hpp"
 #include "spec_common.hpp"
@@ -1063,13 +1065,12 @@ int launch_sample(const void* target, const void* draft, const int32_t* xtok, co
                                             ev, wait_polls, P, kr, nullptr);
 }
 
-int verify_sample_entry(const void* target_logits, const void* draft_logits, int dtype,
-                        const int32_t* draft_tokens, const float* uniforms,
-                        const int32_t* kv_len_in, int B, int K, int V, float temperature,
-                        int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len, float* out_p,
-                        float* out_q, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream, hipEvent_t* events, int wait_polls,
-                        const KeyRequest& kr, const float* temps = nullptr) {
+// Host-side checks of a sampling call's arguments other than its workspace, in the order the
+// header documents.
+int check_sample_args(const void* target_logits, const void* draft_logits, int dtype,
+                      const int32_t* draft_tokens, const float* uniforms, int B, int K, int V,
+                      float temperature, const int32_t* out_tokens, const int32_t* out_tau,
+                      const KeyRequest& kr, const float* temps) {
   int rc = check_dtype(dtype);
   if (rc != SPEC_OK) return rc;
   if ((rc = check_dims(B, K, V)) != SPEC_OK) return rc;
@@ -1084,6 +1085,19 @@ int verify_sample_entry(const void* target_logits, const void* draft_logits, int
   if (temps == nullptr && (!std::isfinite(temperature) || !(temperature > 0.f) ||
                            !std::isfinite(exp2_scale(temperature))))
     return SPEC_ERR_TEMPERATURE;
+  return SPEC_OK;
+}
+
+int verify_sample_entry(const void* target_logits, const void* draft_logits, int dtype,
+                        const int32_t* draft_tokens, const float* uniforms,
+                        const int32_t* kv_len_in, int B, int K, int V, float temperature,
+                        int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len, float* out_p,
+                        float* out_q, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream, hipEvent_t* events, int wait_polls,
+                        const KeyRequest& kr, const float* temps = nullptr) {
+  int rc = check_sample_args(target_logits, draft_logits, dtype, draft_tokens, uniforms, B, K,
+                             V, temperature, out_tokens, out_tau, kr, temps);
+  if (rc != SPEC_OK) return rc;
   if ((rc = check_workspace(workspace, workspace_bytes, B, K, V, 1)) != SPEC_OK) return rc;
   if (events != nullptr)
     for (int i = 0; i < 4; ++i)
@@ -1111,6 +1125,62 @@ extern "C" int spec_verify_sample(const void* target_logits, const void* draft_l
                                  kv_len_in, B, K, V, temperature, out_tokens, out_tau,
                                  out_kv_len, out_p, out_q, workspace, workspace_bytes, stream,
                                  nullptr, -1, sv::KeyRequest{0, 0, nullptr, nullptr});
+}
+
+// ------------------------------------------------------------------------------ no allocation
+// The workspace of spec_verify_sample_noalloc, for callers that cannot allocate one: one array
+// per GPU, loaded with the code object and held until the process ends. In host code this name
+// is a host-side stand-in, not a device address; the device address comes from
+// hipGetSymbolAddress, once per device (scratch_address below), and only that address is ever
+// passed to a kernel. Nothing in it has to start at zero: the call's streaming kernel clears the
+// published-mass words its draw polls, and every other region is written before it is read.
+static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+
+namespace sv {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on its first use there).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPEC_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return SPEC_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPEC_OK;
+}
+
+}  // namespace
+}  // namespace sv
+
+extern "C" int spec_verify_sample_noalloc(const void* target_logits, const void* draft_logits,
+                                          int dtype, const int32_t* draft_tokens,
+                                          const float* uniforms, const int32_t* kv_len_in, int B,
+                                          int K, int V, float temperature, int32_t* out_tokens,
+                                          int32_t* out_tau, int32_t* out_kv_len, float* out_p,
+                                          float* out_q, hipStream_t stream) {
+  using namespace sv;
+  // every host-side check first, so a call that cannot run touches no device
+  const KeyRequest none{0, 0, nullptr, nullptr};
+  int rc = check_sample_args(target_logits, draft_logits, dtype, draft_tokens, uniforms, B, K, V,
+                             temperature, out_tokens, out_tau, none, nullptr);
+  if (rc != SPEC_OK) return rc;
+  if (ws_layout(B, K, V, 1, 0).total > static_cast<size_t>(SPEC_NOALLOC_SCRATCH_BYTES))
+    return SPEC_ERR_SCRATCH;
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws)) != SPEC_OK) return rc;
+  return verify_sample_entry(target_logits, draft_logits, dtype, draft_tokens, uniforms,
+                             kv_len_in, B, K, V, temperature, out_tokens, out_tau, out_kv_len,
+                             out_p, out_q, ws, SPEC_NOALLOC_SCRATCH_BYTES, stream, nullptr, -1,
+                             none);
 }
 
 extern "C" int spec_verify_sample_ex(const void* target_logits, const void* draft_logits,

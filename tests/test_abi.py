@@ -49,6 +49,7 @@ def test_constants_match_header(lib):
     assert sv.SPEC_DEFAULT_WAIT_POLLS == header_define("SPEC_DEFAULT_WAIT_POLLS")
     assert sv.SPEC_MAX_NGRAM == header_define("SPEC_MAX_NGRAM")
     assert sv.SPEC_MAX_CONTEXT == header_define("SPEC_MAX_CONTEXT") == 1 << 30
+    assert sv.SPEC_NOALLOC_SCRATCH_BYTES == header_define("SPEC_NOALLOC_SCRATCH_BYTES")
     for code, name in sv.STATUS.items():
         assert header_define(name) == code
 
@@ -306,3 +307,32 @@ def test_workspace_init_rejects_bad_pointer(lib):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         sv.load_library(str(tmp_path / "nope.so"))
+
+
+def noalloc_call(lib, **kw):
+    a = dict(t=FAKE, d=FAKE, dtype=1, x=FAKE, u=FAKE, kv=NULL, B=2, K=4, V=1000, T=1.0,
+             tok=FAKE, tau=FAKE, kvo=NULL, p=NULL, q=NULL, s=NULL)
+    a.update(kw)
+    return lib.spec_verify_sample_noalloc(a["t"], a["d"], a["dtype"], a["x"], a["u"], a["kv"],
+                                          a["B"], a["K"], a["V"], a["T"], a["tok"], a["tau"],
+                                          a["kvo"], a["p"], a["q"], a["s"])
+
+
+def test_noalloc_validation(lib):
+    """The no-allocation entry point checks its arguments as spec_verify_sample does and rejects
+    sizes its fixed scratch array cannot hold, all before touching the device."""
+    code = {v: k for k, v in sv.STATUS.items()}
+    assert noalloc_call(lib, dtype=7) == code["SPEC_ERR_DTYPE"]
+    for kw in [dict(B=0), dict(K=65), dict(V=1), dict(t=NULL), dict(d=NULL), dict(x=NULL),
+               dict(u=NULL), dict(tok=NULL), dict(tau=NULL), dict(t=FAKE_ODD)]:
+        assert noalloc_call(lib, **kw) == code["SPEC_ERR_ARG"], kw
+    for T in [0.0, -1.0, float("nan"), 1e-45]:
+        assert noalloc_call(lib, T=T) == code["SPEC_ERR_TEMPERATURE"], T
+    cap = sv.SPEC_NOALLOC_SCRATCH_BYTES
+    for B, K, V in [(1024, 8, 128256), (512, 8, 152064), (64, 64, 128256 * 2)]:
+        assert lib.spec_workspace_bytes(B, K, V, 1) > cap
+        assert noalloc_call(lib, B=B, K=K, V=V) == code["SPEC_ERR_SCRATCH"], (B, K, V)
+    # the workloads it is meant for fit
+    for B, K, V in [(64, 4, 128256), (256, 8, 152064), (1, 64, sv.SPEC_MAX_V)]:
+        assert 0 < lib.spec_workspace_bytes(B, K, V, 1) <= cap, (B, K, V)
+    assert "SPEC_NOALLOC_SCRATCH_BYTES" in lib.spec_status_string(code["SPEC_ERR_SCRATCH"]).decode()
