@@ -109,8 +109,9 @@ const char* spec_status_string(int status);
 size_t spec_workspace_bytes(int B, int K, int V, int F);
 
 /* Zeroes the workspace on `stream` (one small fill kernel): the greedy path's published words
- * and its mark. Call once after allocating a workspace, and again to clear the mark a greedy
- * decider leaves when it runs out of polls (spec_verify_greedy_ex). */
+ * and its mark. Call once after allocating a workspace. Every call leaves the workspace ready
+ * for the next; only the greedy path's last-resort mark (spec_verify_greedy_ex) needs this call
+ * again to be cleared. */
 int spec_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Speculative-sampling verification at temperature T > 0 ([SD] stages 3-4; [D3D] 検証のまとめ).
@@ -272,9 +273,14 @@ int spec_verify_greedy(const void* target_logits, int dtype, const int32_t* draf
  *              per request, launched after all of them, polls for these at most this many times
  *              per word (a short sleep apart). Negative selects SPEC_DEFAULT_WAIT_POLLS (what
  *              spec_verify_greedy uses). A decider that runs out streams its request's rows
- *              itself and marks the workspace: from then on every greedy call on it does the
- *              same (same results, more time) until spec_workspace_init clears the mark. 0 makes
- *              every decider that does not find all its words already published take that path. */
+ *              itself, then waits (up to SPEC_DEFAULT_WAIT_POLLS polls per word) for the words it
+ *              gave up on and clears them, so the workspace is left as after any other call and
+ *              the next call takes the normal path. 0 makes every decider that does not find all
+ *              its words already published take that path. Only if a word has still not arrived
+ *              after the second wait (its workgroup was dispatched before the decider, so this
+ *              does not happen in practice) does the decider mark the workspace: from then on
+ *              every greedy call on it streams its rows inside its deciders (same results, more
+ *              time) until spec_workspace_init clears the mark. */
 int spec_verify_greedy_ex(const void* target_logits, int dtype, const int32_t* draft_tokens,
                           const int32_t* kv_len_in, int B, int K, int V, float temperature,
                           int32_t* out_tokens, int32_t* out_tau, int32_t* out_kv_len,

@@ -338,6 +338,15 @@ __device__ __forceinline__ uint64_t load_coherent(const void* p) {
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Device-scope compare-and-swap of a 64-bit word; returns the value found (== expected when
+// the swap happened).
+__device__ __forceinline__ uint64_t cas_coherent(void* p, uint64_t expected, uint64_t desired) {
+  __hip_atomic_compare_exchange_strong(static_cast<uint64_t*>(p), &expected, desired,
+                                       __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return expected;
+}
+
 __device__ __forceinline__ uint64_t pack2(float a, float b) {
   return static_cast<uint64_t>(__float_as_uint(a)) |
          (static_cast<uint64_t>(__float_as_uint(b)) << 32);

@@ -18,9 +18,12 @@
 // wave (lane k = slot k, ballot for the first mismatch) and writes the outputs. The deciders are
 // the last workgroups of the grid, so every streaming workgroup has been dispatched before they
 // start, and those never wait: the polls end. They are still bounded: a decider that runs out of
-// polls marks the workspace and streams its request's rows itself (the same maxima and lowest
-// ids). Words published after that may stay set, so while the mark is set (until
-// spec_workspace_init) every decider streams its own rows and trusts no published word.
+// polls on a word swaps a sentinel into it (or takes the word, if it landed meanwhile), streams
+// its request's rows itself (the same maxima and lowest ids), and then waits for each word it
+// gave up on (its workgroup was dispatched before the decider, so it comes) and clears it: the
+// workspace is left as clean as after any other call, and the next call takes the fast path.
+// Only if that second wait runs out too does the decider mark the workspace; while the mark is
+// set (until spec_workspace_init) every decider streams its own rows and trusts no word.
 #include "api_common.hpp"
 #include "spec_common.hpp"
 
@@ -99,6 +102,8 @@ __device__ __forceinline__ void greedy_chunk(const TIn* __restrict__ tgt, int rb
 // Published word of a chunk: (max, lowest id) with bit 31 of the id set as the written flag
 // (ids are below 2^31; an all -inf chunk keeps the id 0x7fffffff).
 constexpr uint64_t kArgFlag = 1ull << 63;
+// What a decider leaves in a word it stopped waiting for (never a published word: no flag).
+constexpr uint64_t kAbandoned = 1ull;
 
 template <typename TIn>
 __global__ __launch_bounds__(kBlock) void greedy_kernel(
@@ -157,8 +162,13 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
         a = load_coherent(pw + j);
       }
       if ((a & kArgFlag) == 0ull) {
-        late = true;
-        continue;
+        // give up on this word: the sentinel tells the clean-up below that its publish is still
+        // to come; a publish that lands first makes the swap fail and is taken here
+        a = cas_coherent(pw + j, 0ull, kAbandoned);
+        if ((a & kArgFlag) == 0ull) {
+          late = true;
+          continue;
+        }
       }
       a &= ~kArgFlag;
       if (better(lo_float(a), hi_int(a), v, i)) {
@@ -174,9 +184,7 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
   __syncthreads();
   if (s_late != 0) {
     // a row's words did not all arrive within the poll budget, or the mark was set: stream the
-    // request's rows here, chunk by chunk in order (so the same maximum and lowest id); words
-    // that arrive later stay set, which the mark covers
-    if (tid == 0) store_coherent_u32(mark, 1u);
+    // request's rows here, chunk by chunk in order (so the same maximum and lowest id)
     for (int rr = 0; rr < rows && rr <= nb; ++rr) {
       float v = -INFINITY;
       int i = 0x7fffffff;
@@ -192,6 +200,24 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
       }
       if (tid == 0) row_g[rr] = (i == 0x7fffffff) ? 0 : i;
     }
+    // clean-up: every word of the request given up on above is published by now or soon (its
+    // workgroup was dispatched before this one); wait for it and clear it, and clear any word
+    // that landed after the polls, so the request's words are all zero again for the next call.
+    // A word still not there after a full budget marks the workspace.
+    bool stuck = false;
+    for (int rr = w; rr < rows && rr <= nb; rr += kWaves) {
+      uint64_t* pw = words + (static_cast<size_t>(b) * rows + rr) * nchunk;
+      for (int j = lane; j < nchunk; j += kWave) {
+        uint64_t a = load_coherent(pw + j);
+        for (int polls = SPEC_DEFAULT_WAIT_POLLS; a == kAbandoned && polls > 0; --polls) {
+          __builtin_amdgcn_s_sleep(2);
+          a = load_coherent(pw + j);
+        }
+        if (a == kAbandoned) stuck = true;
+        else if (a != 0ull) store_coherent(pw + j, 0ull);
+      }
+    }
+    if (__syncthreads_or(stuck) && tid == 0) store_coherent_u32(mark, 1u);
     __syncthreads();
   }
   if (w != 0) return;
