@@ -94,10 +94,10 @@ SV_HD inline KernelPlan predict_plan(int B, int K, int V, int epv) {
 struct ReqState {
   int m;          // first rejected slot (K when all kept), -1 for a row error
   int xm;         // point-mass drafts: the rejected draft token, removed from the residual (-1)
-  float M_t;      // maximum of the target row the draw reads (p = 2^((l - M_t) c) / S_t)
-  float inv_t;    // fl32(1 / S_t)
+  float M_t;      // maximum of the target row the draw reads (p = 2^((l - M_t) c - ls_t))
+  float ls_t;     // log2 S_t of that row
   float M_d;      // same for the draft row of slot m (unused when m == K)
-  float inv_d;
+  float ls_d;
 };
 
 struct WsLayout {

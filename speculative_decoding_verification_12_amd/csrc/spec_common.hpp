@@ -97,6 +97,12 @@ __device__ __forceinline__ float rel_exp2(float l, float M, float c) {
   return fast_exp2((l - M) * c);
 }
 
+// A probability 2^((l - M) c) / S with its row's normaliser folded into the exponent
+// (ls = log2 S): one subtraction, one fma and one exp2 per element.
+__device__ __forceinline__ float prob_exp2(float l, float M, float c, float ls) {
+  return fast_exp2(fmaf(l - M, c, -ls));
+}
+
 // ------------------------------------------------------------------------------ row layout
 struct RowSpan {
   int head;   // elements [0, head) precede the first 16-byte boundary

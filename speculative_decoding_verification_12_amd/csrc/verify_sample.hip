@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
 
 // ------------------------------------------------------------------------------ draw
 // Weights of the draw over row m: w = max(0, p - q) (residual, m < K) or w = p (bonus, m == K),
-// with p = 2^((l - M_t) c) / S_t and q likewise. `use_p` switches to w = p, the fallback when
+// with p = 2^((l - M_t) c - log2 S_t) and q likewise. `use_p` switches to w = p, the fallback when
 // round-off leaves no residual mass.
 // With a point-mass draft (kMask) the residual max(0, p - q) is p with the draft token `mask`
 // removed (mask < 0: the bonus row, w = p).
@@ -235,10 +235,10 @@ struct DrawRows {
 template <bool kMask, typename TIn>
 __device__ __forceinline__ float weight_one(const DrawRows<TIn>& R, const ReqState& st, float c,
                                             int tok, bool use_p, float& p) {
-  p = rel_exp2(Elem<TIn>::one(R.t, tok), st.M_t, c) * st.inv_t;
+  p = prob_exp2(Elem<TIn>::one(R.t, tok), st.M_t, c, st.ls_t);
   if constexpr (kMask) return (tok == R.mask && !use_p) ? 0.f : p;
   if (!R.resid || use_p) return p;
-  const float q = rel_exp2(Elem<TIn>::one(R.d, tok), st.M_d, c) * st.inv_d;
+  const float q = prob_exp2(Elem<TIn>::one(R.d, tok), st.M_d, c, st.ls_d);
   return fmaxf(p - q, 0.f);
 }
 
@@ -252,7 +252,7 @@ __device__ __forceinline__ void weight_group(const DrawRows<TIn>& R, const ReqSt
   float lt[N];
   E::unpack(qt, lt);
 #pragma unroll
-  for (int j = 0; j < N; ++j) p[j] = rel_exp2(lt[j], st.M_t, c) * st.inv_t;
+  for (int j = 0; j < N; ++j) p[j] = prob_exp2(lt[j], st.M_t, c, st.ls_t);
   if constexpr (kMask) {
     const int tok0 = R.sp.head + v * N;
 #pragma unroll
@@ -273,7 +273,7 @@ __device__ __forceinline__ void weight_group(const DrawRows<TIn>& R, const ReqSt
   }
 #pragma unroll
   for (int j = 0; j < N; ++j)
-    w[j] = fmaxf(p[j] - rel_exp2(ld[j], st.M_d, c) * st.inv_d, 0.f);
+    w[j] = fmaxf(p[j] - prob_exp2(ld[j], st.M_d, c, st.ls_d), 0.f);
 }
 
 template <typename TIn>
@@ -548,9 +548,10 @@ __device__ __forceinline__ void decide_slots(int b, int ch, int K, int V, float 
     st.m = err ? -1 : mm;
     st.xm = (kPoint && mm < nb) ? xm : -1;
     st.M_t = sh.row_m[mm];
-    st.inv_t = 1.f / static_cast<float>(sh.row_s[mm]);
+    st.ls_t = __builtin_amdgcn_logf(static_cast<float>(sh.row_s[mm]));
     st.M_d = (!kPoint && mm < K) ? sh.row_m[K + 1 + mm] : 0.f;
-    st.inv_d = (!kPoint && mm < K) ? 1.f / static_cast<float>(sh.row_s[K + 1 + mm]) : 0.f;
+    st.ls_d = (!kPoint && mm < K) ? __builtin_amdgcn_logf(static_cast<float>(sh.row_s[K + 1 + mm]))
+                                  : 0.f;
     sh.s_st = st;
   }
 }
@@ -709,12 +710,12 @@ __device__ __forceinline__ void search_in_chunk(const DrawRows<TIn>& R, const Re
     }
     float we = 0.f;
     if (has) {
-      const float p = rel_exp2(lt, st.M_t, c) * st.inv_t;
+      const float p = prob_exp2(lt, st.M_t, c, st.ls_t);
       if constexpr (kPoint)
         we = (tok == R.mask && !use_p) ? 0.f : p;
       else
         we = (!R.resid || use_p) ? p
-                                 : fmaxf(p - rel_exp2(ld, st.M_d, c) * st.inv_d, 0.f);
+                                 : fmaxf(p - prob_exp2(ld, st.M_d, c, st.ls_d), 0.f);
     }
     const double cum = sh.s_cb + wave_scan_incl(static_cast<double>(we));
     const unsigned long long pos = __ballot(we > 0.f);
@@ -881,7 +882,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
   const float u_draw = uni[static_cast<size_t>(b) * (K + 1) + K];
 
   // ---- every draft kept (the weights are p_m of the extra row): when the statistics pass cut
-  // the row into the draw's chunks, chunk j's mass is S_j 2^((M_j - M) c) / S from its
+  // the row into the draw's chunks, chunk j's mass is S_j 2^((M_j - M) c - log2 S) from its
   // partial, so no chunk is read for the masses and nothing is exchanged; only the workgroup of
   // the chunk holding u*Z reads its chunk, to find the token
   if (aligned && st.m == nb && !R.resid && R.mask < 0) {
@@ -892,8 +893,8 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
         const double P = q.x > -INFINITY
                              ? static_cast<double>(q.y) *
                                    exp2_wide(static_cast<double>(q.x - st.M_t) *
-                                             static_cast<double>(c)) *
-                                   static_cast<double>(st.inv_t)
+                                                 static_cast<double>(c) -
+                                             static_cast<double>(st.ls_t))
                              : 0.0;
         sh.s_cm[j] = make_double2(P, P);
       }
