@@ -62,6 +62,12 @@ def parse():
                     help="skip the C1/C2 latency, C4 throughput and C5 hit-rate figures")
     ap.add_argument("--no-c4", action="store_true",
                     help="skip C4 (its 1.32 GB input takes ~30 s to generate on the host)")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="print the markdown summary of a rocprofv3 --kernel-trace run of this "
+                         "bench and exit")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the markdown summary of two rocprofv3 --pmc runs of this bench "
+                         "(FETCH_SIZE, then WRITE_SIZE) and exit")
     ap.add_argument("--calib-mib", type=int, default=256,
                     help="size of one plain device-to-device copy run before timing; under "
                          "rocprofv3 --pmc its FETCH_SIZE/WRITE_SIZE calibrate the counters")
@@ -69,8 +75,9 @@ def parse():
 
 
 # ------------------------------------------------------------------------------ counter traffic
-COUNTERS_MD = os.path.join(ROOT, "profiles", "sample_verify_c3_hbm_counters.md")
-KERNEL_SOURCES = ("verify_sample.hip", "row_keys.hpp", "spec_common.hpp", "plan.hpp")
+COUNTERS_MD = os.path.join(ROOT, "profiles", "hbm_counters_all_kernels.md")
+KERNEL_SOURCES = ("verify_sample.hip", "verify_greedy.hip", "predict.hip", "row_keys.hpp",
+                  "spec_common.hpp", "plan.hpp")
 
 
 def kernel_source_hash():
@@ -83,20 +90,152 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def counter_traffic():
-    """HBM bytes per launch of the statistics kernel from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when that summary
-    was taken on other kernel sources."""
+def counter_traffic(label):
+    """Measured HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy) of
+    the kernel launch `label` from the committed rocprofv3 counter summary, or None when that
+    summary was taken on other kernel sources or does not cover it."""
     try:
         with open(COUNTERS_MD) as fh:
             for line in fh:
                 f = line.split()
-                if len(f) == 5 and f[0] == "traffic_bytes_per_launch" and \
-                        f[1] == "sample_stats_kernel" and f[3] == "source_sha256_16":
+                if len(f) == 5 and f[0] == "traffic_bytes_per_launch" and f[1] == label and \
+                        f[3] == "source_sha256_16":
                     return int(f[2]) if f[4] == kernel_source_hash() else None
     except OSError:
         return None
     return None
+
+
+def _chunks(rows, V, epv, max_cv=0):
+    """Chunks per row of a streaming launch (the library's plan: 256 threads, 4 vectors each,
+    8 workgroups per CU on 256 CUs), to name the launches a counter run records."""
+    nvec = max(V // epv, 1)
+    cap = 256 * 8
+    nchunk = -(-nvec // 1024)
+    if rows * nchunk < 4 * cap:
+        fill, finest = cap // rows, -(-nvec // 256)
+        nchunk = 1 if fill < 1 else min(fill, finest)
+    cv = -(-(-(-nvec // nchunk)) // 256) * 256
+    if max_cv and cv > max_cv:
+        cv = max_cv
+    return -(-nvec // cv)
+
+
+def bench_launches():
+    """(label, kernel name prefix, workgroups, algorithmic bytes or None, workload) of every
+    streaming launch the bench makes (bf16 rows)."""
+    out = []
+    for cid, B, K, V in ((3, 64, 4, 128256), (4, 256, 8, 152064)):
+        rows = B * (2 * K + 1)
+        ns, nd = _chunks(rows, V, 8), -(-(V // 8) // 1024)
+        ng = _chunks(B * (K + 1), V, 8, 1024)
+        out += [(f"c{cid}_sample_stats", "sample_stats_kernel<unsigned short, false, false, false>",
+                 rows * ns, rows * V * 2, f"C{cid} sampling, statistics pass"),
+                (f"c{cid}_sample_draw", "sample_draw_kernel<unsigned short, false, false, false>",
+                 B * nd, None, f"C{cid} sampling, draw"),
+                (f"c{cid}_greedy", "greedy_kernel<unsigned short>", B * (K + 1) * ng + B,
+                 B * (K + 1) * V * 2, f"C{cid} greedy")]
+        if cid == 3:
+            out += [("c5_keys_stats", "sample_stats_kernel<unsigned short, true, false, false>",
+                     rows * ns, rows * V * 2, "C5 verification with keys, statistics pass"),
+                    ("c5_keys_draw", "sample_draw_kernel<unsigned short, true, false, false>",
+                     B * nd + B * K, None, "C5 verification with keys, draw and key selection"),
+                    ("c3_mixed_stats", "sample_stats_kernel<unsigned short, false, true, false>",
+                     rows * ns, (B // 2) * (2 * K + 1) * V * 2 + (B // 2) * (K + 1) * V * 2,
+                     "C3 mixed batch (half at T = 0), statistics pass"),
+                    ("c3_mixed_draw", "sample_draw_kernel<unsigned short, false, true, false>",
+                     B * nd, None, "C3 mixed batch, draw"),
+                    ("c3_point_stats", "sample_stats_kernel<unsigned short, false, false, true>",
+                     B * (K + 1) * _chunks(B * (K + 1), V, 8, 1024), None,
+                     "C3 point-mass verification (lookup and full drafts), statistics pass"),
+                    ("c3_point_draw", "sample_draw_kernel<unsigned short, false, false, true>",
+                     B * nd, None, "C3 point-mass verification, draw"),
+                    ("c5_predict_stats", "predict_stats_kernel<unsigned short>",
+                     B * K * _chunks(B * K, V, 8, 1024), B * K * V * 2,
+                     "C5 outcome keys (and fan-out keys), statistics pass"),
+                    ("c5_predict_select", "predict_select_kernel<unsigned short>", B * K, None,
+                     "C5 outcome keys, selection")]
+    return out
+
+
+def trace_summary(trace_dir):
+    """Markdown summary of a rocprofv3 --kernel-trace run of this bench: dispatches, mean and
+    median duration of every streaming launch (grouped by kernel and grid), with the launch's
+    algorithmic bytes over its mean duration against the 8 TB/s HBM peak."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            wg = -(-int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+            per.setdefault((r["Kernel_Name"], wg), []).append(dur)
+    lines = ["| workload | kernel | workgroups | dispatches | mean us | median us | "
+             "algorithmic rate |", "|---|---|---|---|---|---|---|"]
+    for label, prefix, wg, alg, what in bench_launches():
+        d = [v for (k, g), vs in per.items() if prefix in k and g == wg for v in vs]
+        if not d:
+            lines.append(f"| {what} | {prefix} | {wg} | 0 | - | - | - |")
+            continue
+        mean, med = float(np.mean(d)), float(np.median(d))
+        rate = f"{alg / (mean * 1e-6) / 1e12:.2f} TB/s ({alg / (mean * 1e-6) / 1e9 / HBM_PEAK_GBPS:.1%})" \
+            if alg else "-"
+        lines.append(f"| {what} | {prefix} | {wg} | {len(d)} | {mean:.2f} | {med:.2f} | {rate} |")
+    return "\n".join(lines)
+
+
+def _sum_traffic(*labels):
+    """Measured bytes of a call made of these launches, or None when one is not covered."""
+    vals = [counter_traffic(lb) for lb in labels]
+    return None if any(v is None for v in vals) else sum(vals)
+
+
+def counter_summary(fetch_dir, write_dir):
+    """Markdown summary of two rocprofv3 --pmc runs of this bench (FETCH_SIZE, then
+    WRITE_SIZE): mean KiB per dispatch of every streaming launch, scaled by what the counters
+    read for the bench's plain device-to-device copy of --calib-mib MiB, against the launch's
+    algorithmic bytes; then one machine-readable line per launch for the bench's `traffic`
+    fields."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        per = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                wg = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+                per.setdefault((r["Kernel_Name"], wg), []).append(float(r["Counter_Value"]))
+        return per
+
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    calib_kib = 256 * 1024
+    copies_f = [v for (k, wg), vs in fetch.items() if "copyBuffer" in k for v in vs]
+    copies_w = [v for (k, wg), vs in write.items() if "copyBuffer" in k for v in vs]
+    sf, sw = calib_kib / max(copies_f), calib_kib / max(copies_w)
+    lines = [f"Calibration: the bench's plain copy of 256 MiB reads FETCH_SIZE = {max(copies_f):.1f} "
+             f"KiB and WRITE_SIZE = {max(copies_w):.1f} KiB for 262144 KiB each way, so FETCH_SIZE is "
+             f"scaled by {sf:.4f} and WRITE_SIZE by {sw:.4f}.", "",
+             "| workload | kernel | workgroups | dispatches | read MB | write MB | algorithmic MB | "
+             "measured / algorithmic |", "|---|---|---|---|---|---|---|---|"]
+    machine = []
+    for label, prefix, wg, alg, what in bench_launches():
+        fk = [v for (k, g), vs in fetch.items() if prefix in k and g == wg for v in vs]
+        wk = [v for (k, g), vs in write.items() if prefix in k and g == wg for v in vs]
+        if not fk or not wk:
+            lines.append(f"| {what} | {prefix} | {wg} | 0 | - | - | - | - |")
+            continue
+        rd = float(np.mean(fk)) * 1024 * sf
+        wr = float(np.mean(wk)) * 1024 * sw
+        ratio = f"{(rd + wr) / alg:.4f}" if alg else "-"
+        algs = f"{alg / 1e6:.3f}" if alg else "-"
+        lines.append(f"| {what} | {prefix} | {wg} | {len(fk)} | {rd / 1e6:.3f} | {wr / 1e6:.3f} | "
+                     f"{algs} | {ratio} |")
+        machine.append(f"traffic_bytes_per_launch {label} {int(round(rd + wr))} source_sha256_16 "
+                       f"{kernel_source_hash()}")
+    return "\n".join(lines + ["", "Machine-readable lines used by bench.py (dropped when the "
+                               "kernel sources no longer hash to this value):", ""] + machine)
 
 
 # ------------------------------------------------------------------------------ CPU baseline
@@ -135,6 +274,12 @@ def cpu_baseline(wl, repeats):
 # ------------------------------------------------------------------------------ GPU
 def main():
     args = parse()
+    if args.counter_summary:
+        print(counter_summary(*args.counter_summary))
+        return
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the verification step runs on a single MI355X "
               "(requests are independent, so a batch splits across GPUs by request with no "
@@ -289,7 +434,8 @@ def main():
                                      median=round(float(np.median(draw_ms)) * 1e3, 3)),
                  bytes_per_call=bytes_per_call,
                  call_hbm_gbps=round(call_gbps, 1),
-                 call_pct_of_peak=round(100 * call_gbps / HBM_PEAK_GBPS, 2))
+                 call_pct_of_peak=round(100 * call_gbps / HBM_PEAK_GBPS, 2),
+                 draw_kernel_traffic=counter_traffic("c3_sample_draw"))
 
     if not args.no_secondary:
         extra.update(secondary(sv, torch, dev, hip, sets, dsets, ws, args))
@@ -320,10 +466,11 @@ def main():
         "pct_of_hbm_peak": round(100 * call_gbps / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": counter_traffic(),
+                     "traffic": counter_traffic("c3_sample_stats"),
                      "kernel": "sample_stats_kernel<bf16>",
                      "bytes_per_launch": bytes_per_call,
-                     "avg_launch_us": round(stats_avg_s * 1e6, 3)},
+                     "avg_launch_us": round(stats_avg_s * 1e6, 3),
+                     "call_frac": round(call_gbps / HBM_PEAK_GBPS, 4)},
         "cpu_baseline": cpu,
         "extra": extra,
     }
@@ -459,7 +606,9 @@ def other_configs(sv, torch, dev, args):
                 bytes_per_call=nbytes, hbm_gbps=round(nbytes / (ms * 1e-3) / 1e9, 1),
                 frac_of_hbm_peak=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                 bonus_path_share=round(float(np.mean(tau == K + 1)), 4),
-                mean_tau=round(float(tau.mean()), 3))
+                mean_tau=round(float(tau.mean()), 3),
+                traffic=(_sum_traffic("c4_sample_stats", "c4_sample_draw")
+                         if fn_name == "sample" else counter_traffic("c4_greedy")))
         del d4
 
     # ---- C5 hit rates: keys (F=3, every slot, draft token kept) against the outcome of the
@@ -521,7 +670,8 @@ def secondary(sv, torch, dev, hip, sets, dsets, ws, args):
     ms = start.elapsed_time(stop) / steps
     gb = B * (K + 1) * V * 2
     res["greedy_c3"] = dict(ms_per_call=round(ms, 5), rows_per_s=round(B * K / (ms * 1e-3), 1),
-                            hbm_gbps=round(gb / (ms * 1e-3) / 1e9, 1), bytes_per_call=gb)
+                            hbm_gbps=round(gb / (ms * 1e-3) / 1e9, 1), bytes_per_call=gb,
+                            traffic=counter_traffic("c3_greedy"))
 
     log("C5 outcome keys")
     c5 = [make_workload(5, r) for r in range(8)]
@@ -551,7 +701,9 @@ def secondary(sv, torch, dev, hip, sets, dsets, ws, args):
         res[f"predict_c5_T{Tp:g}"] = dict(ms_per_call=round(ms, 5),
                                            keys_per_s=round(B * K * F / (ms * 1e-3), 1),
                                            hbm_gbps=round(pb / (ms * 1e-3) / 1e9, 1),
-                                           bytes_per_call=pb)
+                                           bytes_per_call=pb,
+                                           traffic=_sum_traffic("c5_predict_stats",
+                                                                "c5_predict_select"))
 
     # per-slot fan-out with the draft token skipped (two candidates per slot, the D3D page's
     # setting), then the lookup of each outcome's prepared continuation
@@ -648,7 +800,8 @@ def secondary(sv, torch, dev, hip, sets, dsets, ws, args):
     res["mixed_c3_half_greedy"] = dict(ms_per_call=round(ms, 5),
                                        rows_per_s=round(B * K / (ms * 1e-3), 1),
                                        bytes_per_call=mb_bytes,
-                                       hbm_gbps=round(mb_bytes / (ms * 1e-3) / 1e9, 1))
+                                       hbm_gbps=round(mb_bytes / (ms * 1e-3) / 1e9, 1),
+                                       traffic=_sum_traffic("c3_mixed_stats", "c3_mixed_draw"))
 
     # paged KV-cache rewind of both caches after a C3 round (block size 16)
     log("KV-cache rewind")
@@ -728,15 +881,20 @@ def secondary(sv, torch, dev, hip, sets, dsets, ws, args):
     res["point_verify_c3_full_K"] = dict(ms_per_call=round(ms, 5), bytes_per_call=fb,
                                          rows_per_s=round(B * K / (ms * 1e-3), 1),
                                          hbm_gbps=round(fb / (ms * 1e-3) / 1e9, 1))
+    # the counter run records the lookup-draft and full-draft calls of this grid together
+    res["point_verify_c3_traffic_mean_of_both"] = _sum_traffic("c3_point_stats", "c3_point_draw")
 
     vb = B * (2 * K + 1) * V * 2
     r5 = res["sample_keys_c5"]
     r5.update(F=F, draft_token_skipped=True, bytes_per_call=vb,
               hbm_gbps=round(vb / (r5["fused_ms_per_call"] * 1e-3) / 1e9, 1),
-              rows_per_s=round(B * K / (r5["fused_ms_per_call"] * 1e-3), 1))
+              rows_per_s=round(B * K / (r5["fused_ms_per_call"] * 1e-3), 1),
+              traffic=_sum_traffic("c5_keys_stats", "c5_keys_draw"))
     # every line that streams logits also states its algorithmic rate as a fraction of the
     # 8 TB/s HBM peak; the prompt-lookup drafter reads a few MB and is bound by latency instead
     for entry in res.values():
+        if not isinstance(entry, dict):
+            continue
         for key in [k for k in entry if k.endswith("hbm_gbps")]:
             entry[key[:-len("hbm_gbps")] + "frac_of_hbm_peak"] = round(entry[key] / HBM_PEAK_GBPS, 4)
     res["ngram_draft_64x16k"]["bound"] = "latency"
