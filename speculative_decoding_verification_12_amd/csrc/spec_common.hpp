@@ -84,6 +84,16 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p, int i) {
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// An ordinary 16-byte load of p[i] from global memory. A row pointer that reaches a load through
+// a select or a struct loses its address space, and the compiler then emits a flat load, which
+// the LDS wait counter also tracks; the cast keeps it a global load.
+__device__ __forceinline__ uint4 load_global(const uint4* p, int i) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(1))) v4u GlobalVec;
+  const v4u t = ((GlobalVec*)p)[i];
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // 2^x on the hardware exponential unit (results below 2^-126 may flush to zero, which is far
 // below the resolution any sum here can see)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -55,12 +55,16 @@ __device__ __forceinline__ void greedy_chunk(const TIn* __restrict__ tgt, int rb
   }
   const uint4* vrow = reinterpret_cast<const uint4*>(row + sp.head);
   for (int base = cr.vbeg; base < cr.vend; base += kPassVecs) {
+    // Every lane loads, a lane past the chunk its last vector again (dropped below), so the
+    // loads leave back to back with no branch between them and all are in flight at once.
+    const unsigned last = static_cast<unsigned>(cr.vend - 1);
     uint4 q[kVecPerThread];
 #pragma unroll
-    for (int i = 0; i < kVecPerThread; ++i) {
-      const int vi = base + i * kBlock + tid;
-      q[i] = vi < cr.vend ? load_stream(vrow, vi) : neg_inf_vec<TIn>();
-    }
+    for (int i = 0; i < kVecPerThread; ++i)
+      q[i] = load_stream(vrow, min(static_cast<unsigned>(base + i * kBlock + tid), last));
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i)
+      if (static_cast<unsigned>(base + i * kBlock + tid) > last) q[i] = neg_inf_vec<TIn>();
 #pragma unroll
     for (int i = 0; i < kVecPerThread; ++i) {
       float t[N];
@@ -147,6 +151,12 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
   // wave takes rows w, w + 4, ... and clears each word it has read. Every call's chunk
   // workgroups publish their words, so the polls end whether or not the mark is set; the mark,
   // read alongside them, only decides afterwards whether the words are trusted.
+  // wave 0's decision inputs (lane k: draft token k; the KV length) are loaded first, so their
+  // latency passes while the words are polled
+  const int k = lane;
+  const bool valid = k < nb;
+  const int xk = (w == 0 && valid) ? xtok[static_cast<size_t>(b) * K + k] : 0;
+  const int kv0 = (w == 0 && kv_in != nullptr) ? kv_in[b] : 0;
   if (tid == 0) s_late = 0;
   __syncthreads();
   const bool marked = load_coherent_u32(mark) != 0u;
@@ -222,9 +232,6 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
   }
   if (w != 0) return;
 
-  const int k = lane;
-  const bool valid = k < nb;
-  const int xk = valid ? xtok[static_cast<size_t>(b) * K + k] : 0;
   const bool bad = valid && (xk < 0 || xk >= V);
   const bool err = nb_bad || __ballot(bad) != 0ull;
   const unsigned long long miss = __ballot(valid && xk != row_g[valid ? k : 0]);
@@ -240,7 +247,6 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
     out_tok[static_cast<size_t>(b) * (K + 1) + j] = tok;
   }
   if (lane == 0) {
-    const int kv0 = kv_in ? kv_in[b] : 0;
     out_tau[b] = err ? -1 : mm + 1;
     if (out_kv) out_kv[b] = err ? kv0 : kv0 + mm + 1;
   }

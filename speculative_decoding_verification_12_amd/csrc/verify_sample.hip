@@ -281,8 +281,8 @@ __device__ __forceinline__ void load_pair(const DrawRows<TIn>& R, int v, bool ha
                                           uint4& qd) {
   const uint4* tv = reinterpret_cast<const uint4*>(R.t + R.sp.head);
   const uint4* dv = reinterpret_cast<const uint4*>(R.d + R.sp.head);
-  qt = has ? tv[v] : neg_inf_vec<TIn>();
-  qd = (has && R.resid && R.d_aligned) ? dv[v] : neg_inf_vec<TIn>();
+  qt = has ? load_global(tv, v) : neg_inf_vec<TIn>();
+  qd = (has && R.resid && R.d_aligned) ? load_global(dv, v) : neg_inf_vec<TIn>();
 }
 
 // The elements a thread of the draw owns, in token order: the scalar head (thread 0 of chunk 0),
