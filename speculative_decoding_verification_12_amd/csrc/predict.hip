@@ -38,9 +38,12 @@ namespace {
 struct FanoutTable {
   int P;
   int S;
-  int8_t pick[SPEC_MAX_K];
-  int8_t count[SPEC_MAX_K];
-  int16_t off[SPEC_MAX_K];
+  // 32-bit entries: a workgroup reads its slot's entries with a uniform runtime index, which a
+  // scalar load serves only for whole dwords (a byte entry became a vector load and a wait for
+  // it before the workgroup's first row load)
+  int32_t pick[SPEC_MAX_K];
+  int32_t count[SPEC_MAX_K];
+  int32_t off[SPEC_MAX_K];
 };
 
 template <typename TIn>
@@ -85,16 +88,18 @@ __global__ __launch_bounds__(kSelectWaves * kWave) void predict_select_kernel(
   const int xk = xtok ? xtok[static_cast<size_t>(b) * K + k] : -1;   // excluded token, if any
   // the chunk statistics, loaded now and merged by wave 0 only when the keys are written
   const float2* pr = part + static_cast<size_t>(rk) * nchunk;
-  const float2 a0 = lane < nchunk ? pr[lane] : make_float2(-INFINITY, 0.f);
+  // (every lane loads, from a clamped index, so no wait for it comes before the maxima's loads)
+  const float2 a0r = load_f2(pr + min(lane, nchunk - 1));
   auto row_stat = [&]() {   // the row's (M, S) from its chunks (wave 0)
+    const float2 a0 = lane < nchunk ? a0r : make_float2(-INFINITY, 0.f);
     float lm = a0.x;
-    for (int j = lane + kWave; j < nchunk; j += kWave) lm = fmaxf(lm, pr[j].x);
+    for (int j = lane + kWave; j < nchunk; j += kWave) lm = fmaxf(lm, load_f2(pr + j).x);
     const float Mr = wave_max(lm);
     double ls = 0.0;
     if (c > 0.f) {
       if (a0.x > -INFINITY) ls += static_cast<double>(a0.y) * rel_exp2(a0.x, Mr, c);
       for (int j = lane + kWave; j < nchunk; j += kWave) {
-        const float2 a = pr[j];
+        const float2 a = load_f2(pr + j);
         if (a.x > -INFINITY) ls += static_cast<double>(a.y) * rel_exp2(a.x, Mr, c);
       }
     }
@@ -165,9 +170,9 @@ bool fanout_table(const int32_t* fanout, int P, bool exclude, int V, FanoutTable
     const int F = fanout[k];
     const int pick = F > 0 ? F + (exclude ? 1 : 0) : 0;
     if (F < 0 || pick > SPEC_MAX_F || pick > V) return false;
-    ft.pick[k] = static_cast<int8_t>(pick);
-    ft.count[k] = static_cast<int8_t>(F);
-    ft.off[k] = static_cast<int16_t>(ft.S);
+    ft.pick[k] = pick;
+    ft.count[k] = F;
+    ft.off[k] = ft.S;
     ft.S += F;
   }
   return ft.S > 0;

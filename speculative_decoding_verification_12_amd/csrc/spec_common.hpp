@@ -94,6 +94,14 @@ __device__ __forceinline__ uint4 load_global(const uint4* p, int i) {
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// A float2 read with one 8-byte load. Read as a float2, a pair whose .y is used only under a
+// condition on .x compiles to two dependent loads (the second issued after the first returns).
+__device__ __forceinline__ float2 load_f2(const float2* p) {
+  const uint64_t v = *reinterpret_cast<const uint64_t*>(p);
+  return make_float2(__uint_as_float(static_cast<uint32_t>(v)),
+                     __uint_as_float(static_cast<uint32_t>(v >> 32)));
+}
+
 // 2^x on the hardware exponential unit (results below 2^-126 may flush to zero, which is far
 // below the resolution any sum here can see)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

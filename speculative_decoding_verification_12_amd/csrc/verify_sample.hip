@@ -439,7 +439,7 @@ __device__ __forceinline__ void merge_row_stats_rd(Rd rd, bool has, int n, int W
 
 __device__ __forceinline__ void merge_row_stats(const float2* pr, bool has, int n, int W, int i,
                                                 float c, float& Mr, double& Sr) {
-  merge_row_stats_rd([pr](int j) { return pr[j]; }, has, n, W, i, c, Mr, Sr);
+  merge_row_stats_rd([pr](int j) { return load_f2(pr + j); }, has, n, W, i, c, Mr, Sr);
 }
 
 // The group width the merges use for `rows` rows of n chunks: the widest power of two (at most
@@ -804,7 +804,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
           float v = -INFINITY;
           int i = 0x7fffffff;
           for (int j = lane; j < nchunk_s; j += kWave) {
-            const float2 q = pr[j];
+            const float2 q = load_f2(pr + j);
             if (better(q.x, __float_as_int(q.y), v, i)) {
               v = q.x;
               i = __float_as_int(q.y);
@@ -889,7 +889,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     if (w == 0) {
       const float2* pr = part_s + (static_cast<size_t>(b) * rows + st.m) * nchunk_s;
       for (int j = lane; j < nchunk; j += kWave) {
-        const float2 q = pr[j];
+        const float2 q = load_f2(pr + j);
         const double P = q.x > -INFINITY
                              ? static_cast<double>(q.y) *
                                    exp2_wide(static_cast<double>(q.x - st.M_t) *
