@@ -183,17 +183,7 @@ __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
     }
   }
 
-  // The workgroup whose chunk holds the slot's draft token also reads that token's logit, so
-  // the merge finds it without another dependent load. Rows 0..K-1 are target slots, K+1..2K
-  // draft slots; row K (the extra target row) has no draft token.
   const int slot = r < K ? r : r - K - 1;
-  if (r != K && threadIdx.x == 0) {
-    const int x = xtok[static_cast<size_t>(b) * K + slot];
-    const int lo = cr.first ? 0 : sp.head + cr.vbeg * N;
-    const int hi = cr.last ? V : sp.head + cr.vend * N;
-    if (x >= lo && x < hi)
-      gath[static_cast<size_t>(b) * 2 * K + (r < K ? slot : K + slot)] = E::one(row, x);
-  }
 
   float m, s, M, S;
   // The draw re-reads target row m (and draft row m below the extra row) right after this pass.
@@ -212,6 +202,18 @@ __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
   float* wmax = (kKeys && r > K)
                     ? key_wave_max + ((static_cast<size_t>(b) * K + slot) * nchunk + ch) * kWaves
                     : nullptr;
+  // The workgroup whose chunk holds the slot's draft token also reads that token's logit, so
+  // the merge finds it without another dependent load. Rows 0..K-1 are target slots, K+1..2K
+  // draft slots; row K (the extra target row) has no draft token. It is read once the chunk has
+  // streamed (the chunk's lines were just fetched), so neither the draft token's load nor the
+  // logit's delays the chunk's own loads.
+  if (r != K && threadIdx.x == 0) {
+    const int x = xtok[static_cast<size_t>(b) * K + slot];
+    const int lo = cr.first ? 0 : sp.head + cr.vbeg * N;
+    const int hi = cr.last ? V : sp.head + cr.vend * N;
+    if (x >= lo && x < hi)
+      gath[static_cast<size_t>(b) * 2 * K + (r < K ? slot : K + slot)] = E::one(row, x);
+  }
   block_stats(m, s, c, sm, ss, M, S, wmax);
   if (threadIdx.x == 0) part[static_cast<size_t>(rb) * nchunk + ch] = make_float2(M, S);
 }
