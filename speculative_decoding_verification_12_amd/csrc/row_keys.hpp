@@ -332,10 +332,17 @@ __device__ __forceinline__ void select_keys(const TIn* __restrict__ row, int V, 
     const float v = mine ? s_cv[lw][lj] : -INFINITY;
     const int id = mine ? s_ci[lw][lj] : kSentinelId;
     int rank = 0;
+    if (tot <= kWave) {
+      // the usual case: every candidate sits in one lane, and candidate h reaches the others by
+      // a lane read (no LDS round trip per compare)
+      for (int h = 0; h < tot; ++h)   // uniform
+        rank += better(readlane_f32(v, h), __builtin_amdgcn_readlane(id, h), v, id) ? 1 : 0;
+    } else {
 #pragma unroll
-    for (int wl = 0; wl < NW; ++wl)
-      for (int h = 0; h < pre[wl + 1] - pre[wl]; ++h)   // uniform
-        rank += better(s_cv[wl][h], s_ci[wl][h], v, id) ? 1 : 0;
+      for (int wl = 0; wl < NW; ++wl)
+        for (int h = 0; h < pre[wl + 1] - pre[wl]; ++h)   // uniform
+          rank += better(s_cv[wl][h], s_ci[wl][h], v, id) ? 1 : 0;
+    }
     if (mine && rank < Fp) {
       s_pv[rank] = v;
       s_pi[rank] = id;
