@@ -71,6 +71,20 @@ SV_HD inline KernelPlan draw_plan(int B, int K, int V, int epv) {
   const int nvec = V / epv > 0 ? V / epv : 1;
   return KernelPlan{kBlock * kDrawVecs, ceil_div(nvec, kBlock * kDrawVecs)};
 }
+// Draw workgroups per CU at once (from the compiler's resource report for gfx950: registers and
+// LDS both allow eight).
+constexpr int kDrawResident = 8;
+// Consecutive chunks of row m that one draw workgroup takes: one while every request's chunks fit
+// on the GPU at once; otherwise as many as bring the draw's workgroups down to one round (at most
+// kMaxDrawGroup). A workgroup whose chunks are all resident never waits for a workgroup that has
+// not started, and each extra round would cost the whole chain of a draw workgroup again.
+constexpr int kMaxDrawGroup = 4;
+SV_HD inline int draw_group(int B, int nchunk) {
+  const long long chunks = static_cast<long long>(B) * nchunk;
+  const long long slots = static_cast<long long>(kCUs) * kDrawResident;
+  const long long g = (chunks + slots - 1) / slots;
+  return g < 1 ? 1 : (g > kMaxDrawGroup ? kMaxDrawGroup : static_cast<int>(g));
+}
 // point-mass drafts: the statistics pass streams only the K+1 target rows, in chunks of at most
 // one pass of the block (16 KiB of bf16) so that even a batch that would fill the GPU once with
 // larger chunks runs in several rounds (measured faster: the pass has no per-workgroup handshake)

@@ -631,8 +631,10 @@ __device__ __forceinline__ void find_chunk(int nchunk, float u_draw, DrawShared&
 // the token among that thread's elements, which it hands to wave 0 through LDS; writes the token
 // to *out_y. Called by the whole workgroup. The vectors are read again here (from the cache):
 // holding every thread's vectors in registers across the mass exchange cost 32 registers per
-// thread in every draw workgroup.
-template <typename TIn, bool kPoint>
+// thread in every draw workgroup. With kRecompute (a workgroup that published several chunks
+// and kept none of their thread masses) ws and ps are computed again from the vectors read here:
+// thread_mass gives the same bits.
+template <typename TIn, bool kPoint, bool kRecompute = false>
 __device__ __forceinline__ void search_in_chunk(const DrawRows<TIn>& R, const ReqState& st,
                                                 float c, int V, int nchunk, int cv, int ch,
                                                 const ThreadElems& el, float ws, float ps,
@@ -643,8 +645,12 @@ __device__ __forceinline__ void search_in_chunk(const DrawRows<TIn>& R, const Re
   // every thread reads its vectors again now (cache hits), so the one that turns out to hold
   // u*Z has them when the block scan below has named it
   uint4 qt[kDrawVecs], qd[kDrawVecs];
+  if constexpr (kRecompute) {
+    thread_mass<kPoint>(R, st, c, V, el, qt, qd, ws, ps);
+  } else {
 #pragma unroll
-  for (int i = 0; i < kDrawVecs; ++i) load_pair(R, el.v0 + i, i < el.nv, qt[i], qd[i]);
+    for (int i = 0; i < kDrawVecs; ++i) load_pair(R, el.v0 + i, i < el.nv, qt[i], qd[i]);
+  }
   const bool use_p = sh.s_usep != 0;
   const bool fb = sh.s_fallback != 0;
   const double t = sh.s_t;
@@ -730,14 +736,37 @@ __device__ __forceinline__ void search_in_chunk(const DrawRows<TIn>& R, const Re
   }
 }
 
-// Chunks of kBlock * kDrawVecs vectors (see draw_plan). cm holds the published (R, P) of every
-// chunk, [b][ch][2] words, zeroed by the statistics kernel of the same call.
-template <typename TIn, bool kKeys, bool kMixed, bool kPoint>
+// Every chunk mass marked missing in sh.s_cm (R < 0: not published within the poll budget),
+// computed by this workgroup: the same bits the chunk's own workgroup publishes. Called by the
+// whole workgroup after a barrier.
+template <typename TIn, bool kPoint>
+__device__ __forceinline__ void help_missing_masses(const DrawRows<TIn>& R, const ReqState& st,
+                                                 float c, int V, int nchunk, int cv,
+                                                 DrawShared& sh) {
+  const int tid = threadIdx.x;
+  for (int j = 0; j < nchunk; ++j) {
+    if (!(sh.s_cm[j].x < 0.0)) continue;   // uniform: read after a barrier
+    uint4 ht[kDrawVecs], hd[kDrawVecs];
+    float hw, hp;
+    thread_mass<kPoint>(R, st, c, V, thread_elems(R.sp, V, nchunk, cv, j, tid), ht, hd, hw, hp);
+    double hr, hq;
+    chunk_mass(hw, hp, sh.s_red, hr, hq);
+    if (tid == 0) sh.s_cm[j] = make_double2(hr, hq);
+    __syncthreads();
+  }
+}
+
+// Chunks of kBlock * kDrawVecs vectors (see draw_plan); each workgroup takes `group` consecutive
+// chunks of its request (draw_group: one, unless the chunks would not all be resident at once).
+// kGroups = false is the one-chunk instance (group is then 1 and folds away).
+// cm holds the published (R, P) of every chunk, [b][ch][2] words, zeroed by the statistics
+// kernel of the same call.
+template <typename TIn, bool kKeys, bool kMixed, bool kPoint, bool kGroups>
 __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     const TIn* __restrict__ tgt, const TIn* __restrict__ drf, const int32_t* __restrict__ xtok,
     const float* __restrict__ uni, const int32_t* __restrict__ kv_in, int K, int V, float c_call,
     int nchunk_s, const float2* __restrict__ part_s, const float* __restrict__ gath,
-    int nchunk, int cv, int aligned, uint64_t* __restrict__ cm, int wait_polls,
+    int nchunk, int cv, int aligned, int group, uint64_t* __restrict__ cm, int wait_polls,
     int32_t* __restrict__ out_tok, int32_t* __restrict__ out_tau, int32_t* __restrict__ out_kv,
     float* __restrict__ out_p, float* __restrict__ out_q, KeyArgs ka,
     const float* __restrict__ temps, const int32_t* __restrict__ dlen, int n_draw) {
@@ -770,8 +799,11 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     }
   }
 
-  const int b = blockIdx.x / nchunk;
-  const int ch = blockIdx.x % nchunk;
+  const int grp = kGroups ? group : 1;
+  const int nq = kGroups ? (nchunk + grp - 1) / grp : nchunk;   // workgroups per request
+  const int b = blockIdx.x / nq;
+  const int c0 = static_cast<int>(blockIdx.x % nq) * grp;   // this workgroup's chunks [c0, c1)
+  const int c1 = kGroups ? min(c0 + grp, nchunk) : c0 + 1;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int rows = kPoint ? K + 1 : 2 * K + 1;
 
@@ -799,7 +831,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     const bool t_ok = greedy || (Tb > 0.f && isfinite(Tb) && isfinite(cc));
     c = cc;
     if (greedy || !t_ok) {
-      if (ch != 0) return;   // one workgroup of the request does all of it
+      if (c0 != 0) return;   // one workgroup of the request does all of it
       if (t_ok)
         for (int rr = w; rr <= K; rr += kWaves) {
           const float2* pr = part_s + (static_cast<size_t>(b) * rows + rr) * nchunk_s;
@@ -854,7 +886,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       lt = gath[static_cast<size_t>(b) * 2 * K + lane];
       if constexpr (!kPoint) ld = gath[static_cast<size_t>(b) * 2 * K + K + lane];
     }
-    const int kv0 = (ch == 0 && tid == 0 && kv_in) ? kv_in[b] : 0;
+    const int kv0 = (c0 == 0 && tid == 0 && kv_in) ? kv_in[b] : 0;
     // Rows are merged in groups of W lanes (merge_width), 64/W rows per wave, so one pass over
     // the block issues every partial load at once. Lanes past nchunk_s (or past the last row)
     // carry (-inf, 0).
@@ -873,7 +905,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     }
     __syncthreads();
     if (w == 0)
-      decide_slots<kPoint>(b, ch, K, V, c, nb, nb_bad, valid, xk, uk, lt, ld, kv0, sh, out_tok,
+      decide_slots<kPoint>(b, c0, K, V, c, nb, nb_bad, valid, xk, uk, lt, ld, kv0, sh, out_tok,
                            out_tau, out_kv, out_p, out_q);
     __syncthreads();
   }
@@ -904,61 +936,98 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     __syncthreads();
     if (w == 0) find_chunk(nchunk, u_draw, sh);
     __syncthreads();
-    if (sh.s_cs != ch) return;
+    const int cs = sh.s_cs;
+    if (cs < c0 || cs >= c1) return;
+    const ThreadElems el = thread_elems(R.sp, V, nchunk, cv, cs, tid);
+    int32_t* const out_y = out_tok + static_cast<size_t>(b) * (K + 1) + st.m;
+    if constexpr (kGroups) {
+      search_in_chunk<TIn, kPoint, true>(R, st, c, V, nchunk, cv, cs, el, 0.f, 0.f, sh, out_y);
+    } else {
+      float ws, ps;
+      {
+        uint4 qt[kDrawVecs], qd[kDrawVecs];
+        thread_mass<kPoint>(R, st, c, V, el, qt, qd, ws, ps);
+      }
+      search_in_chunk<TIn, kPoint>(R, st, c, V, nchunk, cv, cs, el, ws, ps, sh, out_y);
+    }
+    return;
+  }
+
+  const FlaggedMasses pub{cm + static_cast<size_t>(b) * nchunk * 2};
+
+  if constexpr (!kGroups) {
+    // ---- one chunk: its masses, published; then every other chunk mass of the request into
+    // LDS (the general loop below measured 0.3-0.5 us slower per C3 call in this instance)
+    const int ch = c0;
     const ThreadElems el = thread_elems(R.sp, V, nchunk, cv, ch, tid);
     float ws, ps;
     {
       uint4 qt[kDrawVecs], qd[kDrawVecs];
       thread_mass<kPoint>(R, st, c, V, el, qt, qd, ws, ps);
     }
+    double R0, P0;
+    chunk_mass(ws, ps, sh.s_red, R0, P0);
+    if (tid == 0) pub.publish(ch, R0, P0);
+    bool missing = false;
+    for (int j = tid; j < nchunk; j += kBlock) {
+      double r = R0, q = P0;
+      if (j != ch && !pub.poll(j, wait_polls, r, q)) {
+        r = -1.0;   // marks the entry missing
+        missing = true;
+      }
+      sh.s_cm[j] = make_double2(r, q);
+    }
+    if (__syncthreads_or(missing)) help_missing_masses<TIn, kPoint>(R, st, c, V, nchunk, cv, sh);
+    if (w == 0) find_chunk(nchunk, u_draw, sh);
+    __syncthreads();
+    if (sh.s_cs != ch) return;
     search_in_chunk<TIn, kPoint>(R, st, c, V, nchunk, cv, ch, el, ws, ps, sh,
                                  out_tok + static_cast<size_t>(b) * (K + 1) + st.m);
     return;
   }
 
-  const FlaggedMasses pub{cm + static_cast<size_t>(b) * nchunk * 2};
-
-  // ---- this chunk's masses, published
-  const ThreadElems el = thread_elems(R.sp, V, nchunk, cv, ch, tid);
-  float ws, ps;
-  {
-    uint4 qt[kDrawVecs], qd[kDrawVecs];
-    thread_mass<kPoint>(R, st, c, V, el, qt, qd, ws, ps);
+  // ---- this workgroup's chunk masses, published one chunk after another (each also to LDS)
+  ThreadElems el;
+  float ws = 0.f, ps = 0.f;   // the thread masses of the last chunk (the only one when group = 1)
+  for (int k = c0; k < c1; ++k) {
+    el = thread_elems(R.sp, V, nchunk, cv, k, tid);
+    {
+      uint4 qt[kDrawVecs], qd[kDrawVecs];
+      thread_mass<kPoint>(R, st, c, V, el, qt, qd, ws, ps);
+    }
+    double R0, P0;
+    chunk_mass(ws, ps, sh.s_red, R0, P0);
+    if (tid == 0) {
+      pub.publish(k, R0, P0);
+      sh.s_cm[k] = make_double2(R0, P0);
+    }
   }
-  double R0, P0;
-  chunk_mass(ws, ps, sh.s_red, R0, P0);
-  if (tid == 0) pub.publish(ch, R0, P0);
 
-  // ---- gather every chunk mass of the request into LDS; a chunk not published within the
+  // ---- gather every other chunk mass of the request into LDS; a chunk not published within the
   // poll budget is computed here (the same bits its owner publishes)
   bool missing = false;
   for (int j = tid; j < nchunk; j += kBlock) {
-    double r = R0, q = P0;
-    if (j != ch && !pub.poll(j, wait_polls, r, q)) {
+    if (j >= c0 && j < c1) continue;
+    double r = 0.0, q = 0.0;
+    if (!pub.poll(j, wait_polls, r, q)) {
       r = -1.0;   // marks the entry missing
       missing = true;
     }
     sh.s_cm[j] = make_double2(r, q);
   }
-  if (__syncthreads_or(missing)) {
-    for (int j = 0; j < nchunk; ++j) {
-      if (!(sh.s_cm[j].x < 0.0)) continue;   // uniform: read after a barrier
-      uint4 ht[kDrawVecs], hd[kDrawVecs];
-      float hw, hp;
-      thread_mass<kPoint>(R, st, c, V, thread_elems(R.sp, V, nchunk, cv, j, tid), ht, hd, hw,
-                          hp);
-      double hr, hq;
-      chunk_mass(hw, hp, sh.s_red, hr, hq);
-      if (tid == 0) sh.s_cm[j] = make_double2(hr, hq);
-      __syncthreads();
-    }
-  }
+  if (__syncthreads_or(missing)) help_missing_masses<TIn, kPoint>(R, st, c, V, nchunk, cv, sh);
 
   if (w == 0) find_chunk(nchunk, u_draw, sh);
   __syncthreads();
-  if (sh.s_cs != ch) return;
-  search_in_chunk<TIn, kPoint>(R, st, c, V, nchunk, cv, ch, el, ws, ps, sh,
-                               out_tok + static_cast<size_t>(b) * (K + 1) + st.m);
+  const int cs = sh.s_cs;
+  if (cs < c0 || cs >= c1) return;
+  int32_t* const out_y = out_tok + static_cast<size_t>(b) * (K + 1) + st.m;
+  if (c1 - c0 == 1)   // uniform: the thread masses of this workgroup's one chunk are at hand
+    search_in_chunk<TIn, kPoint>(R, st, c, V, nchunk, cv, cs, el, ws, ps, sh, out_y);
+  else
+    search_in_chunk<TIn, kPoint, true>(R, st, c, V, nchunk, cv, cs,
+                                       thread_elems(R.sp, V, nchunk, cv, cs, tid), 0.f, 0.f, sh,
+                                       out_y);
 }
 
 
@@ -989,7 +1058,9 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
                     hipStream_t stream, hipEvent_t* ev, int wait_polls, const SamplePlan& P,
                     const KeyRequest& kr, const float* temps, const int32_t* dlen = nullptr) {
   const size_t g1 = static_cast<size_t>(B) * (kPoint ? K + 1 : 2 * K + 1) * P.stats.nchunk;
-  const size_t n_draw = static_cast<size_t>(B) * P.draw.nchunk;
+  const int group = draw_group(B, P.draw.nchunk);   // chunks per draw workgroup
+  const size_t n_chunks = static_cast<size_t>(B) * P.draw.nchunk;
+  const size_t n_draw = static_cast<size_t>(B) * ((P.draw.nchunk + group - 1) / group);
   // with keys, one more workgroup per draft slot selects that slot's keys during the draw
   const size_t g2 = n_draw + (kKeys ? static_cast<size_t>(B) * K : 0);
   if (!grid_fits(g1) || !grid_fits(g2) || P.draw.cv != kBlock * kDrawVecs ||
@@ -1003,7 +1074,7 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
   float* gath = ws_ptr<float>(ws, L.gathered);
   uint64_t* cm = ws_ptr<uint64_t>(ws, L.part_draw);
   float* kwmax = ws_ptr<float>(ws, L.part_vwm);
-  const int nclear = static_cast<int>(n_draw * 2);
+  const int nclear = static_cast<int>(n_chunks * 2);
   const dim3 grid1(static_cast<unsigned>(g1)), grid2(static_cast<unsigned>(g2)), block(kBlock);
   const int ns = P.stats.nchunk, cs = P.stats.cv, nd = P.draw.nchunk, cd = P.draw.cv;
   const int polls = wait_polls < 0 ? SPEC_DEFAULT_WAIT_POLLS : wait_polls;
@@ -1028,20 +1099,35 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
     hipLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0, stream,
                        t, d, xtok, K, V, c, ns, cs, part1, gath, cm, nclear, kwmax, temps, dlen,
                        nt);
-    hipLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint>), grid2, block, 0, stream,
-                       t, d, xtok, uni, kv_in, K, V, c, ns, static_cast<const float2*>(part1),
-                       static_cast<const float*>(gath), nd, cd, aligned, cm, polls, out_tok,
-                       out_tau, out_kv, out_p, out_q, ka, temps, dlen, nd_wg);
+    if (group > 1)
+      hipLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint, true>), grid2, block, 0,
+                         stream, t, d, xtok, uni, kv_in, K, V, c, ns,
+                         static_cast<const float2*>(part1), static_cast<const float*>(gath), nd,
+                         cd, aligned, group, cm, polls, out_tok, out_tau, out_kv, out_p, out_q, ka,
+                         temps, dlen, nd_wg);
+    else
+      hipLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint, false>), grid2, block, 0,
+                         stream, t, d, xtok, uni, kv_in, K, V, c, ns,
+                         static_cast<const float2*>(part1), static_cast<const float*>(gath), nd,
+                         cd, aligned, 1, cm, polls, out_tok, out_tau, out_kv, out_p, out_q, ka,
+                         temps, dlen, nd_wg);
   } else {
     // profiling: the runtime records the events at each kernel's start and end
     hipExtLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0,
                           stream, ev[0], ev[1], 0, t, d, xtok, K, V, c, ns, cs, part1, gath, cm,
                           nclear, kwmax, temps, dlen, nt);
-    hipExtLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint>), grid2, block, 0, stream,
-                          ev[2], ev[3], 0, t, d, xtok, uni, kv_in, K, V, c, ns,
-                          static_cast<const float2*>(part1), static_cast<const float*>(gath), nd,
-                          cd, aligned, cm, polls, out_tok, out_tau, out_kv, out_p, out_q, ka,
-                          temps, dlen, nd_wg);
+    if (group > 1)
+      hipExtLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint, true>), grid2, block,
+                            0, stream, ev[2], ev[3], 0, t, d, xtok, uni, kv_in, K, V, c, ns,
+                            static_cast<const float2*>(part1), static_cast<const float*>(gath),
+                            nd, cd, aligned, group, cm, polls, out_tok, out_tau, out_kv, out_p,
+                            out_q, ka, temps, dlen, nd_wg);
+    else
+      hipExtLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint, false>), grid2, block,
+                            0, stream, ev[2], ev[3], 0, t, d, xtok, uni, kv_in, K, V, c, ns,
+                            static_cast<const float2*>(part1), static_cast<const float*>(gath),
+                            nd, cd, aligned, 1, cm, polls, out_tok, out_tau, out_kv, out_p, out_q,
+                            ka, temps, dlen, nd_wg);
   }
   return launch_status();
 }

@@ -291,6 +291,26 @@ def test_draw_help_path_bit_identical(cid, B, V, rnd):
     compare_sample(wl, h, requests=range(min(wl.B, 16)))
 
 
+@pytest.mark.parametrize("cid,rnd", [(3, 28), (1, 29)])
+def test_draw_chunk_groups(cid, rnd):
+    """More draw chunks than the GPU holds at once, so each draw workgroup takes several
+    consecutive chunks of row m. B=512, K=1, V=40000 of the C3 recipe (bf16, 5 chunks a row, 2560
+    chunks) gives two chunks per workgroup and one in the last; the C1 recipe (fp32, 10 chunks a
+    row) gives three, three, three and one. With K = 1 about half the requests keep their draft,
+    so both the residual draw and the all-kept draw run with groups. The default and the zero
+    poll budget (every mass not found published is computed by the workgroup that needs it)
+    agree bit for bit, and every request matches the oracle."""
+    wl = make_workload(cid, rnd, B=512, K=1, V=40000)
+    dev = upload(wl)
+    ws = sv.new_workspace(wl.B, wl.K, wl.V)
+    announce(f"draw chunk groups C{cid} B={wl.B} K={wl.K} V={wl.V} {wl.dtype}")
+    a = gpu_sample(wl, dev=dev, ws=ws)
+    h = gpu_sample(wl, dev=dev, ws=ws, wait_polls=0)
+    for k in a:
+        assert np.array_equal(a[k].view(np.int32), h[k].view(np.int32)), k
+    compare_sample(wl, a)
+
+
 def _first_half_clean(ws):
     """The workspace's first half (the greedy path's published words and its mark) is all zero,
     as every greedy call must leave it."""
