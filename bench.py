@@ -121,6 +121,20 @@ def _chunks(rows, V, epv, max_cv=0):
     return -(-nvec // cv)
 
 
+def _draw_group(B, nd):
+    """Chunks per draw workgroup, as the library's plan picks them (draw_group: the fewest that
+    fit every draw workgroup on the 256 CUs at 8 each, at most 4)."""
+    return max(1, min(4, -(-(B * nd) // (256 * 8))))
+
+
+def _draw_kernel(flags, B, nd):
+    """(kernel name, workgroups) of a draw launch with template flags `flags` (keys, mixed,
+    point) over B requests of nd chunks (keys add B·K workgroups on top)."""
+    g = _draw_group(B, nd)
+    name = f"sample_draw_kernel<unsigned short, {flags}, {'true' if g > 1 else 'false'}>"
+    return name, B * -(-nd // g)
+
+
 def bench_launches():
     """(label, kernel name prefix, workgroups, algorithmic bytes or None, workload) of every
     streaming launch the bench makes (bf16 rows)."""
@@ -129,27 +143,28 @@ def bench_launches():
         rows = B * (2 * K + 1)
         ns, nd = _chunks(rows, V, 8), -(-(V // 8) // 1024)
         ng = _chunks(B * (K + 1), V, 8, 1024)
+        dname, dwg = _draw_kernel("false, false, false", B, nd)
         out += [(f"c{cid}_sample_stats", "sample_stats_kernel<unsigned short, false, false, false>",
                  rows * ns, rows * V * 2, f"C{cid} sampling, statistics pass"),
-                (f"c{cid}_sample_draw", "sample_draw_kernel<unsigned short, false, false, false>",
-                 B * nd, None, f"C{cid} sampling, draw"),
+                (f"c{cid}_sample_draw", dname, dwg, None, f"C{cid} sampling, draw"),
                 (f"c{cid}_greedy", "greedy_kernel<unsigned short>", B * (K + 1) * ng + B,
                  B * (K + 1) * V * 2, f"C{cid} greedy")]
         if cid == 3:
             out += [("c5_keys_stats", "sample_stats_kernel<unsigned short, true, false, false>",
                      rows * ns, rows * V * 2, "C5 verification with keys, statistics pass"),
-                    ("c5_keys_draw", "sample_draw_kernel<unsigned short, true, false, false>",
-                     B * nd + B * K, None, "C5 verification with keys, draw and key selection"),
+                    ("c5_keys_draw", _draw_kernel("true, false, false", B, nd)[0],
+                     _draw_kernel("true, false, false", B, nd)[1] + B * K, None,
+                     "C5 verification with keys, draw and key selection"),
                     ("c3_mixed_stats", "sample_stats_kernel<unsigned short, false, true, false>",
                      rows * ns, (B // 2) * (2 * K + 1) * V * 2 + (B // 2) * (K + 1) * V * 2,
                      "C3 mixed batch (half at T = 0), statistics pass"),
-                    ("c3_mixed_draw", "sample_draw_kernel<unsigned short, false, true, false>",
-                     B * nd, None, "C3 mixed batch, draw"),
+                    ("c3_mixed_draw", *_draw_kernel("false, true, false", B, nd), None,
+                     "C3 mixed batch, draw"),
                     ("c3_point_stats", "sample_stats_kernel<unsigned short, false, false, true>",
                      B * (K + 1) * _chunks(B * (K + 1), V, 8, 1024), None,
                      "C3 point-mass verification (lookup and full drafts), statistics pass"),
-                    ("c3_point_draw", "sample_draw_kernel<unsigned short, false, false, true>",
-                     B * nd, None, "C3 point-mass verification, draw"),
+                    ("c3_point_draw", *_draw_kernel("false, false, true", B, nd), None,
+                     "C3 point-mass verification, draw"),
                     ("c5_predict_stats", "predict_stats_kernel<unsigned short>",
                      B * K * _chunks(B * K, V, 8, 1024), B * K * V * 2,
                      "C5 outcome keys (and fan-out keys), statistics pass"),
