@@ -311,6 +311,24 @@ def test_draw_chunk_groups(cid, rnd):
     compare_sample(wl, a)
 
 
+def test_draw_chunk_groups_mixed_and_point():
+    """The mixed-temperature and point-mass draws with chunk groups (B=512, V=40000 bf16: 2560
+    draw chunks, two per workgroup): a mixed batch with every other request at T = 0, and
+    point-mass drafts of lengths 0..K, against the oracle."""
+    wl = make_workload(3, 30, B=512, K=2, V=40000)
+    dev = upload(wl)
+    temps = np.where(np.arange(wl.B) % 2 == 0, 0.0, float(wl.T)).astype(np.float32)
+    announce(f"draw chunk groups, mixed B={wl.B} K={wl.K} V={wl.V}")
+    n, f = compare_mixed(wl, gpu_mixed(wl, temps, dev=dev), temps)
+    announce(f"mixed with groups: {n} checked, {f} flagged")
+    rng = np.random.default_rng(90)
+    lens = rng.integers(0, wl.K + 1, wl.B).astype(np.int32)
+    x = _point_tokens(wl, lens, rng)
+    announce(f"draw chunk groups, point B={wl.B} K={wl.K} V={wl.V}")
+    n, f = compare_point(wl, gpu_point(wl, x, lens, float(wl.T), dev=dev), x, lens, float(wl.T))
+    announce(f"point with groups: {n} checked, {f} flagged")
+
+
 def _first_half_clean(ws):
     """The workspace's first half (the greedy path's published words and its mark) is all zero,
     as every greedy call must leave it."""
