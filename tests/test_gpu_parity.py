@@ -396,20 +396,23 @@ def test_workspace_reuse_across_shapes():
         _same_bits(gpu_mixed(wl, mixed_T, dev=dev, ws=fresh), gpu_mixed(wl, mixed_T, dev=dev, ws=ws))
 
 
-def test_graph_capture_replays():
+@pytest.mark.parametrize("B,K", [(8, 4), (512, 1)])
+def test_graph_capture_replays(B, K):
     """Captured into a HIP graph (no memset node: the draw's published-mass words are cleared
     by the statistics kernel's own stores), every replay after new inputs are copied in equals
-    an eager call on them, with eager calls on the same workspace between the replays."""
-    wls = [make_workload(3, 50 + i, B=8, V=40000) for i in range(3)]
+    an eager call on them, with eager calls on the same workspace between the replays. B = 512
+    (2560 draw chunks) runs the draw with two chunks per workgroup."""
+    V = 40000
+    wls = [make_workload(3, 50 + i, B=B, K=K, V=V) for i in range(3)]
     devs = [upload(w) for w in wls]
-    ws = sv.new_workspace(8, 4, 40000)
-    eager = [gpu_sample(w, dev=d, ws=sv.new_workspace(8, 4, 40000)) for w, d in zip(wls, devs)]
+    ws = sv.new_workspace(B, K, V)
+    eager = [gpu_sample(w, dev=d, ws=sv.new_workspace(B, K, V)) for w, d in zip(wls, devs)]
     static = {k: v.clone() for k, v in devs[0].items()}
-    out = dict(tokens=torch.empty((8, 5), dtype=torch.int32, device="cuda"),
-               tau=torch.empty(8, dtype=torch.int32, device="cuda"),
-               kv_len=torch.empty(8, dtype=torch.int32, device="cuda"),
-               p=torch.empty((8, 4), dtype=torch.float32, device="cuda"),
-               q=torch.empty((8, 4), dtype=torch.float32, device="cuda"))
+    out = dict(tokens=torch.empty((B, K + 1), dtype=torch.int32, device="cuda"),
+               tau=torch.empty(B, dtype=torch.int32, device="cuda"),
+               kv_len=torch.empty(B, dtype=torch.int32, device="cuda"),
+               p=torch.empty((B, K), dtype=torch.float32, device="cuda"),
+               q=torch.empty((B, K), dtype=torch.float32, device="cuda"))
     T = float(wls[0].T)
 
     def call():
@@ -422,7 +425,7 @@ def test_graph_capture_replays():
         call()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    announce("graph capture")
+    announce(f"graph capture B={B} K={K}")
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         call()
