@@ -291,16 +291,19 @@ def test_draw_help_path_bit_identical(cid, B, V, rnd):
     compare_sample(wl, h, requests=range(min(wl.B, 16)))
 
 
-@pytest.mark.parametrize("cid,rnd", [(3, 28), (1, 29)])
-def test_draw_chunk_groups(cid, rnd):
+@pytest.mark.parametrize("cid,rnd,B,V", [(3, 28, 512, 40000), (1, 29, 512, 40000),
+                                         (3, 32, 129, None), (1, 33, 3000, 1000)])
+def test_draw_chunk_groups(cid, rnd, B, V):
     """More draw chunks than the GPU holds at once, so each draw workgroup takes several
     consecutive chunks of row m. B=512, K=1, V=40000 of the C3 recipe (bf16, 5 chunks a row, 2560
     chunks) gives two chunks per workgroup and one in the last; the C1 recipe (fp32, 10 chunks a
-    row) gives three, three, three and one. With K = 1 about half the requests keep their draft,
-    so both the residual draw and the all-kept draw run with groups. The default and the zero
-    poll budget (every mass not found published is computed by the workgroup that needs it)
-    agree bit for bit, and every request matches the oracle."""
-    wl = make_workload(cid, rnd, B=512, K=1, V=40000)
+    row) gives three, three, three and one. B=129 at C3's V (2064 chunks, just over one round)
+    gives two each; B=3000 rows of one chunk (V=1000 fp32) runs the grouped kernel with one chunk
+    in every workgroup. With K = 1 about half the requests keep their draft, so both the residual
+    draw and the all-kept draw run with groups. The default and the zero poll budget (every mass
+    not found published is computed by the workgroup that needs it) agree bit for bit, and every
+    request matches the oracle."""
+    wl = make_workload(cid, rnd, B=B, K=1, V=V)
     dev = upload(wl)
     ws = sv.new_workspace(wl.B, wl.K, wl.V)
     announce(f"draw chunk groups C{cid} B={wl.B} K={wl.K} V={wl.V} {wl.dtype}")
