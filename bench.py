@@ -68,6 +68,10 @@ def parse():
     ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the markdown summary of two rocprofv3 --pmc runs of this bench "
                          "(FETCH_SIZE, then WRITE_SIZE) and exit")
+    ap.add_argument("--issue-summary", nargs="+", metavar="PMC_DIR",
+                    help="print the markdown summary of rocprofv3 --pmc runs of this bench that "
+                         "collected SQ wave, wait, VALU and memory-instruction counters and "
+                         "SQC_ICACHE_MISSES, and exit")
     ap.add_argument("--calib-mib", type=int, default=256,
                     help="size of one plain device-to-device copy run before timing; under "
                          "rocprofv3 --pmc its FETCH_SIZE/WRITE_SIZE calibrate the counters")
@@ -199,6 +203,49 @@ def trace_summary(trace_dir):
     return "\n".join(lines)
 
 
+def issue_summary(*dirs):
+    """Markdown summary of rocprofv3 --pmc runs of this bench with the SQ wave counters
+    (SQ_WAVES, SQ_WAVE_CYCLES, SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_VALU, SQ_INSTS_VALU,
+    SQ_INSTS_VMEM_RD) and SQC_ICACHE_MISSES: per streaming launch, the mean wave lifetime and how
+    its wave-cycles split between waiting (for memory, a barrier or a dependency), waiting to
+    issue, and vector ALU work. The cycle counters count quad-cycles summed over every SIMD."""
+    import csv
+    import glob
+    per = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                wg = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+                key = (r["Kernel_Name"], wg, r["Counter_Name"])
+                per.setdefault(key, []).append(float(r["Counter_Value"]))
+
+    def mean(prefix, wg, counter):
+        v = [x for (k, g, c), xs in per.items() if prefix in k and g == wg and c == counter
+             for x in xs]
+        return (float(np.mean(v)), len(v)) if v else (None, 0)
+
+    lines = ["| workload | kernel | workgroups | waves | cycles per wave | waiting | "
+             "waiting to issue | VALU active | VALU instructions per wave | memory reads per wave "
+             "| icache misses per dispatch |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for label, prefix, wg, alg, what in bench_launches():
+        waves, n = mean(prefix, wg, "SQ_WAVES")
+        cyc = mean(prefix, wg, "SQ_WAVE_CYCLES")[0]
+        if not waves or not cyc:
+            lines.append(f"| {what} | {prefix} | {wg} | - | - | - | - | - | - | - | - |")
+            continue
+        wait, issue, valu_c = (mean(prefix, wg, c)[0] for c in
+                               ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU"))
+        valu_i, vmem, icm = (mean(prefix, wg, c)[0] for c in
+                             ("SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD", "SQC_ICACHE_MISSES"))
+        share = lambda x: f"{x / cyc:.0%}" if x is not None else "-"
+        perw = lambda x: f"{x / waves:.0f}" if x is not None else "-"
+        icms = f"{icm:.0f}" if icm is not None else "-"
+        lines.append(f"| {what} | {prefix} | {wg} | {waves:.0f} | {4 * cyc / waves:.0f} | "
+                     f"{share(wait)} | {share(issue)} | {share(valu_c)} | {perw(valu_i)} | "
+                     f"{perw(vmem)} | {icms} |")
+    return "\n".join(lines)
+
+
 def _sum_traffic(*labels):
     """Measured bytes of a call made of these launches, or None when one is not covered."""
     vals = [counter_traffic(lb) for lb in labels]
@@ -291,6 +338,9 @@ def main():
     args = parse()
     if args.counter_summary:
         print(counter_summary(*args.counter_summary))
+        return
+    if args.issue_summary:
+        print(issue_summary(*args.issue_summary))
         return
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
