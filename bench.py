@@ -143,6 +143,12 @@ def bench_launches():
     """(label, kernel name prefix, workgroups, algorithmic bytes or None, workload) of every
     streaming launch the bench makes (bf16 rows)."""
     out = []
+    # C1 (fp32, 4 elements a vector) and C2: one request each, statistics and draw in one launch
+    for cid, K, V, epv, tname in ((1, 4, 1000, 4, "float"), (2, 5, 32000, 8, "unsigned short")):
+        rows = 2 * K + 1
+        out.append((f"c{cid}_sample_one_launch", f"sample_fused_kernel<{tname}>",
+                    rows * _chunks(rows, V, epv) + -(-(V // epv) // 1024), rows * V * (16 // epv),
+                    f"C{cid} sampling, one launch (statistics and draw)"))
     for cid, B, K, V in ((3, 64, 4, 128256), (4, 256, 8, 152064)):
         rows = B * (2 * K + 1)
         ns, nd = _chunks(rows, V, 8), -(-(V // 8) // 1024)

@@ -126,7 +126,12 @@ int spec_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t str
  *   out_kv_len [B]     int32   kv_len_in[b] + tau (nullable; kv_len_in may be NULL = 0)
  *   out_p, out_q [B,K] float   p_k(x_k), q_k(x_k) for every slot (nullable)
  * Inputs are read once in one streaming pass; the target and draft rows of slot m are read
- * again by the draw (only the extra target row when every draft is kept). */
+ * again by the draw (only the extra target row when every draft is kept). The pass and the draw
+ * are two kernels on `stream`; for small batches (every workgroup of both fitting on the GPU at
+ * once, e.g. one request at V = 32000) they are one kernel whose workgroups hand results over
+ * through tagged workspace words, except while `stream` is being captured into a HIP graph
+ * (a replay would repeat the call's tag), where the two kernels are recorded. Both give the same
+ * outputs bit for bit. */
 int spec_verify_sample(const void* target_logits, const void* draft_logits, int dtype,
                        const int32_t* draft_tokens, const float* uniforms,
                        const int32_t* kv_len_in, int B, int K, int V, float temperature,
@@ -139,12 +144,15 @@ int spec_verify_sample(const void* target_logits, const void* draft_logits, int 
  *   events     NULL, or four caller-created hipEvent_t (timing enabled, none NULL, else
  *              SPEC_ERR_ARG): the runtime records events[0]/events[1] at the start/end of the
  *              streaming statistics kernel and events[2]/events[3] at the start/end of the draw
- *              kernel (hipExtLaunchKernelGGL).
- *   wait_polls the draw's workgroups of one request exchange their chunk masses; a workgroup
- *              re-polls for another's mass at most this many times (a short sleep apart)
- *              before computing that mass itself. Negative selects SPEC_DEFAULT_WAIT_POLLS
- *              (what spec_verify_sample uses); 0 makes every workgroup compute each mass it
- *              does not find already published, which exercises that path. */
+ *              kernel (hipExtLaunchKernelGGL). With events a small batch runs as two kernels
+ *              too, so that each can be timed.
+ *   wait_polls the draw's workgroups of one request exchange their chunk masses (and, in
+ *              the one-kernel form, read the pass's chunk statistics and draft-token logits
+ *              from the workgroups that publish them); a workgroup re-polls for such a value at
+ *              most this many times (a short sleep apart) before computing it itself. Negative
+ *              selects SPEC_DEFAULT_WAIT_POLLS (what spec_verify_sample uses); 0 makes every
+ *              workgroup compute each value it does not find already published, which
+ *              exercises that path. */
 int spec_verify_sample_ex(const void* target_logits, const void* draft_logits, int dtype,
                           const int32_t* draft_tokens, const float* uniforms,
                           const int32_t* kv_len_in, int B, int K, int V, float temperature,

@@ -85,6 +85,20 @@ SV_HD inline int draw_group(int B, int nchunk) {
   const long long g = (chunks + slots - 1) / slots;
   return g < 1 ? 1 : (g > kMaxDrawGroup ? kMaxDrawGroup : static_cast<int>(g));
 }
+// Small batches run the statistics and the draw of a sampling call in one launch when every
+// workgroup of it can be resident at once and the draw's merge can hold a request's chunk
+// partials in LDS; the statistics chunks must not be the draw's chunks (the all-kept shortcut
+// of the two-launch draw reads the partials of exactly those chunks).
+constexpr int kFusedMaxPartials = 1024;   // chunk partials of one request, held in LDS
+constexpr int kFusedMaxGrid = 1024;       // workgroups of one launch
+SV_HD inline bool fused_shape_ok(int B, int K, int V, int epv) {
+  const KernelPlan s = stats_plan(B, K, V, epv), d = draw_plan(B, K, V, epv);
+  const long long rows = 2ll * K + 1;
+  const long long grid = static_cast<long long>(B) * (rows * s.nchunk + d.nchunk);
+  const bool aligned = s.nchunk == d.nchunk && s.cv == d.cv;
+  return !aligned && rows * s.nchunk <= kFusedMaxPartials && grid <= kFusedMaxGrid &&
+         draw_group(B, d.nchunk) == 1;
+}
 // point-mass drafts: the statistics pass streams only the K+1 target rows, in chunks of at most
 // one pass of the block (16 KiB of bf16) so that even a batch that would fill the GPU once with
 // larger chunks runs in several rounds (measured faster: the pass has no per-workgroup handshake)
@@ -125,12 +139,31 @@ struct WsLayout {
   size_t part_pred;  // 8 B [B*K*nchunk]: outcome keys, chunk (max, scaled sum)
   size_t part_pwm;   // 4 B [B*K*nchunk*4]: outcome keys, wave maxima
   size_t part_vwm;   // 4 B [B*K*nchunk*4]: wave maxima of the draft rows (outcome keys)
+  size_t fused;      // one-launch sampling (small batches only): tagged words, FusedWords below
   size_t data_end;   // end of the last data region
   size_t total;      // bytes this shape needs: twice the larger of the two halves' regions
   bool fits;         // the caller's workspace holds this shape's words and data
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Tagged 64-bit words of the one-launch sampling path, relative to WsLayout::fused: chunk
+// partials [B][2K+1][nchunk_s][2] (max, sum), gathered logits [B][2K], chunk masses
+// [B][nchunk_d][4] (residual and target mass, each in two halves).
+struct FusedWords {
+  size_t part, gath, mass, bytes;
+};
+inline FusedWords fused_words(int B, int K, int V, int epv) {
+  FusedWords f{0, 0, 0, 0};
+  if (!fused_shape_ok(B, K, V, epv)) return f;
+  const size_t b = static_cast<size_t>(B), rows = 2 * static_cast<size_t>(K) + 1;
+  const size_t ns = static_cast<size_t>(stats_plan(B, K, V, epv).nchunk);
+  const size_t nd = static_cast<size_t>(draw_plan(B, K, V, epv).nchunk);
+  f.gath = align256(16 * b * rows * ns);
+  f.mass = f.gath + align256(8 * b * 2 * static_cast<size_t>(K));
+  f.bytes = f.mass + align256(32 * b * nd);
+  return f;
+}
 
 template <typename PlanFn>
 inline size_t max_chunks(PlanFn fn, int B, int K, int V) {
@@ -171,6 +204,11 @@ inline WsLayout ws_layout(int B, int K, int V, int F, size_t ws_bytes) {
   d = align256(d + 4 * b * k * np * 4);
   L.part_vwm = d;
   d = align256(d + 4 * b * k * ns * 4);
+  L.fused = d;
+  {
+    const size_t f4 = fused_words(B, K, V, 4).bytes, f8 = fused_words(B, K, V, 8).bytes;
+    d += f4 > f8 ? f4 : f8;
+  }
   const size_t need_half = L.words_end > d ? L.words_end : d;
   L.total = 2 * need_half;
   const size_t half = (ws_bytes / 2) & ~static_cast<size_t>(255);
@@ -181,6 +219,7 @@ inline WsLayout ws_layout(int B, int K, int V, int F, size_t ws_bytes) {
   L.part_pred += half;
   L.part_pwm += half;
   L.part_vwm += half;
+  L.fused += half;
   L.data_end = half + d;
   return L;
 }

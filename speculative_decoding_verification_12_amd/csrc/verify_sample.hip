@@ -36,6 +36,7 @@
 // only, so the draw re-reads target row m from the cache and draft row m from HBM at once.
 #include <hip/hip_ext.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "api_common.hpp"
@@ -634,18 +635,26 @@ __device__ __forceinline__ void find_chunk(int nchunk, float u_draw, DrawShared&
 // thread in every draw workgroup. With kRecompute (a workgroup that published several chunks
 // and kept none of their thread masses) ws and ps are computed again from the vectors read here:
 // thread_mass gives the same bits.
-template <typename TIn, bool kPoint, bool kRecompute = false>
+template <typename TIn, bool kPoint, bool kRecompute = false, bool kHeld = false>
 __device__ __forceinline__ void search_in_chunk(const DrawRows<TIn>& R, const ReqState& st,
                                                 float c, int V, int nchunk, int cv, int ch,
                                                 const ThreadElems& el, float ws, float ps,
-                                                DrawShared& sh, int32_t* __restrict__ out_y) {
+                                                DrawShared& sh, int32_t* __restrict__ out_y,
+                                                const uint4* held_t = nullptr,
+                                                const uint4* held_d = nullptr) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   // every thread reads its vectors again now (cache hits), so the one that turns out to hold
-  // u*Z has them when the block scan below has named it
+  // u*Z has them when the block scan below has named it (kHeld: the caller kept them)
   uint4 qt[kDrawVecs], qd[kDrawVecs];
-  if constexpr (kRecompute) {
+  if constexpr (kHeld) {
+#pragma unroll
+    for (int i = 0; i < kDrawVecs; ++i) {
+      qt[i] = held_t[i];
+      qd[i] = held_d[i];
+    }
+  } else if constexpr (kRecompute) {
     thread_mass<kPoint>(R, st, c, V, el, qt, qd, ws, ps);
   } else {
 #pragma unroll
@@ -1031,6 +1040,237 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
 }
 
 
+// ------------------------------------------------------------------------------ one launch
+// Small batches (fused_shape_ok: every workgroup of the call resident at once) run the
+// statistics and the draw in one launch. The statistics workgroups come first in the grid and
+// publish their chunk (M, S) and the gathered logits as tagged words; the draw workgroups after
+// them read those words instead of waiting for a kernel boundary, then publish and gather their
+// chunk masses the same way. A word holds a 32-bit payload in its low half and the call's tag in
+// its high half: the tag is new for every call (a host counter, never 0), so words left by
+// earlier calls never match and nothing is cleared between calls. Every wait is bounded; a
+// workgroup that stops waiting computes the missing item itself with the code that publishes
+// it, so the bits never depend on who produced them. The merge, the slot decisions, the masses,
+// the scan and the search are the two-launch draw's own functions: the outputs equal that
+// path's bit for bit.
+
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t v) {
+  return (static_cast<uint64_t>(tag) << 32) | v;
+}
+__device__ __forceinline__ bool has_tag(uint64_t w, uint32_t tag) {
+  return static_cast<uint32_t>(w >> 32) == tag;
+}
+
+// A chunk's (R, P) masses as four tagged words (each float64 in two halves).
+struct TaggedMasses {
+  uint64_t* tm;   // [nchunk][4] of one request
+  uint32_t tag;
+  __device__ void publish(int j, double R, double P) const {
+    const uint64_t r = dbits(R), p = dbits(P);
+    store_coherent(&tm[4 * j], tagged(tag, static_cast<uint32_t>(r)));
+    store_coherent(&tm[4 * j + 1], tagged(tag, static_cast<uint32_t>(r >> 32)));
+    store_coherent(&tm[4 * j + 2], tagged(tag, static_cast<uint32_t>(p)));
+    store_coherent(&tm[4 * j + 3], tagged(tag, static_cast<uint32_t>(p >> 32)));
+  }
+  // Reads chunk j's masses, re-polling at most `polls` times; false if they are not all there.
+  __device__ bool poll(int j, int polls, double& R, double& P) const {
+    uint64_t w0 = load_coherent(&tm[4 * j]), w1 = load_coherent(&tm[4 * j + 1]);
+    uint64_t w2 = load_coherent(&tm[4 * j + 2]), w3 = load_coherent(&tm[4 * j + 3]);
+    while (!(has_tag(w0, tag) && has_tag(w1, tag) && has_tag(w2, tag) && has_tag(w3, tag))) {
+      if (polls-- <= 0) return false;
+      __builtin_amdgcn_s_sleep(2);
+      if (!has_tag(w0, tag)) w0 = load_coherent(&tm[4 * j]);
+      if (!has_tag(w1, tag)) w1 = load_coherent(&tm[4 * j + 1]);
+      if (!has_tag(w2, tag)) w2 = load_coherent(&tm[4 * j + 2]);
+      if (!has_tag(w3, tag)) w3 = load_coherent(&tm[4 * j + 3]);
+    }
+    R = bits_d((w1 << 32) | static_cast<uint32_t>(w0));
+    P = bits_d((w3 << 32) | static_cast<uint32_t>(w2));
+    return true;
+  }
+};
+
+// Chunk ch of row r of request b, as the statistics pass computes it (plain loads); (M, S) in
+// thread 0. Called by the whole workgroup.
+template <typename TIn>
+__device__ __forceinline__ void fused_chunk_stats(const TIn* tgt, const TIn* drf, int b, int r,
+                                                  int ch, int K, int V, float c, int ns, int cs,
+                                                  float* sm, float* ss, float& M, float& S) {
+  const TIn* row = slot_row(tgt, drf, b, r, K, V);
+  const RowSpan sp = row_span(row, V);
+  const ChunkRange cr = chunk_range(sp, ch, ns, cs);
+  float m, s;
+  thread_chunk_stats<TIn, true, false>(row, sp, cr, V, c, m, s);
+  block_stats(m, s, c, sm, ss, M, S);
+}
+
+// Grid: B * (2K+1) * ns statistics workgroups (request, row, chunk), then B * nd draw
+// workgroups (request, chunk of row m). part: [B][2K+1][ns][2] tagged (M, S); gath: [B][2K]
+// tagged logits of the draft tokens (target slots, then draft slots); mass: [B][nd][4].
+template <typename TIn>
+__global__ __launch_bounds__(kBlock) void sample_fused_kernel(
+    const TIn* __restrict__ tgt, const TIn* __restrict__ drf, const int32_t* __restrict__ xtok,
+    const float* __restrict__ uni, const int32_t* __restrict__ kv_in, int K, int V, float c,
+    int ns, int cs, int nd, int cv, int n_stats, uint32_t tag, uint64_t* __restrict__ part,
+    uint64_t* __restrict__ gath, uint64_t* __restrict__ mass, int wait_polls,
+    int32_t* __restrict__ out_tok, int32_t* __restrict__ out_tau, int32_t* __restrict__ out_kv,
+    float* __restrict__ out_p, float* __restrict__ out_q) {
+  using E = Elem<TIn>;
+  constexpr int N = E::N;
+  __shared__ float sm[kWaves], ss[kWaves];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int rows = 2 * K + 1;
+
+  if (static_cast<int>(blockIdx.x) < n_stats) {
+    // ---- statistics of one (request, row, chunk), as sample_stats_kernel computes them
+    const int ch = blockIdx.x % ns;
+    const int rb = blockIdx.x / ns;
+    const int r = rb % rows, b = rb / rows;
+    float M, S;
+    fused_chunk_stats<TIn>(tgt, drf, b, r, ch, K, V, c, ns, cs, sm, ss, M, S);
+    if (tid == 0) {
+      uint64_t* pw = part + 2 * (static_cast<size_t>(rb) * ns + ch);
+      store_coherent(pw, tagged(tag, __float_as_uint(M)));
+      store_coherent(pw + 1, tagged(tag, __float_as_uint(S)));
+      if (r != K) {   // the chunk holding the slot's draft token publishes that token's logit
+        const TIn* row = slot_row(tgt, drf, b, r, K, V);
+        const RowSpan sp = row_span(row, V);
+        const ChunkRange cr = chunk_range(sp, ch, ns, cs);
+        const int slot = r < K ? r : r - K - 1;
+        const int x = xtok[static_cast<size_t>(b) * K + slot];
+        const int lo = cr.first ? 0 : sp.head + cr.vbeg * N;
+        const int hi = cr.last ? V : sp.head + cr.vend * N;
+        if (x >= lo && x < hi)
+          store_coherent(gath + static_cast<size_t>(b) * 2 * K + (r < K ? slot : K + slot),
+                         tagged(tag, __float_as_uint(E::one(row, x))));
+      }
+    }
+    return;
+  }
+
+  // ---- draw: one (request, chunk of row m)
+  __shared__ DrawShared sh;
+  __shared__ float2 s_part[kFusedMaxPartials];
+  __shared__ float s_gath[2 * SPEC_MAX_K];
+  const int dq = static_cast<int>(blockIdx.x) - n_stats;
+  const int b = dq / nd, ch = dq % nd;
+  const bool valid = w == 0 && lane < K;
+  const int xk = valid ? xtok[static_cast<size_t>(b) * K + lane] : 0;
+  const float uk = valid ? uni[static_cast<size_t>(b) * (K + 1) + lane] : 0.f;
+  const int kv0 = (ch == 0 && tid == 0 && kv_in) ? kv_in[b] : 0;
+
+  // the request's chunk partials into LDS; one not published within the poll budget is marked
+  // (S = -1: a published sum is >= 0 or NaN) and computed below
+  const int np = rows * ns;
+  const uint64_t* pw = part + 2 * static_cast<size_t>(b) * np;
+  bool miss = false;
+  for (int j = tid; j < np; j += kBlock) {
+    uint64_t a = load_coherent(pw + 2 * j), z = load_coherent(pw + 2 * j + 1);
+    for (int polls = wait_polls; !(has_tag(a, tag) && has_tag(z, tag)) && polls > 0; --polls) {
+      __builtin_amdgcn_s_sleep(2);
+      if (!has_tag(a, tag)) a = load_coherent(pw + 2 * j);
+      if (!has_tag(z, tag)) z = load_coherent(pw + 2 * j + 1);
+    }
+    const bool ok = has_tag(a, tag) && has_tag(z, tag);
+    s_part[j] = ok ? make_float2(__uint_as_float(static_cast<uint32_t>(a)),
+                                 __uint_as_float(static_cast<uint32_t>(z)))
+                   : make_float2(0.f, -1.f);
+    miss = miss || !ok;
+  }
+  // the draft tokens' logits; one not published in time is read here (the value its chunk
+  // publishes). An out-of-range token has none: the slot decisions report it as a row error.
+  for (int j = tid; j < 2 * K; j += kBlock) {
+    const int slot = j < K ? j : j - K;
+    const int x = xtok[static_cast<size_t>(b) * K + slot];
+    float v = 0.f;
+    if (x >= 0 && x < V) {
+      const uint64_t* gw = gath + static_cast<size_t>(b) * 2 * K + j;
+      uint64_t a = load_coherent(gw);
+      for (int polls = wait_polls; !has_tag(a, tag) && polls > 0; --polls) {
+        __builtin_amdgcn_s_sleep(2);
+        a = load_coherent(gw);
+      }
+      v = has_tag(a, tag)
+              ? __uint_as_float(static_cast<uint32_t>(a))
+              : E::one(slot_row(tgt, drf, b, j < K ? slot : K + 1 + slot, K, V), x);
+    }
+    s_gath[j] = v;
+  }
+  if (__syncthreads_or(miss)) {
+    for (int j = 0; j < np; ++j) {
+      if (!(s_part[j].y < 0.f)) continue;   // uniform: read after a barrier
+      float M, S;
+      fused_chunk_stats<TIn>(tgt, drf, b, j / ns, j % ns, K, V, c, ns, cs, sm, ss, M, S);
+      if (tid == 0) s_part[j] = make_float2(M, S);
+      __syncthreads();
+    }
+  }
+
+  // ---- merge and slot decisions, as the two-launch draw (partials from LDS)
+  {
+    const float lt = valid ? s_gath[lane] : 0.f;
+    const float ld = valid ? s_gath[K + lane] : 0.f;
+    const int W = merge_width(ns, rows);
+    const int per_wave = kWave / W, g = lane / W, i = lane % W;
+    for (int base = 0; base < rows; base += kWaves * per_wave) {
+      const int rr = base + w * per_wave + g;
+      const float2* pr = s_part + (rr < rows ? rr : 0) * ns;
+      float Mr;
+      double Sr;
+      merge_row_stats_rd([pr](int j) { return pr[j]; }, rr < rows, ns, W, i, c, Mr, Sr);
+      if (i == 0 && rr < rows) {
+        sh.row_m[rr] = Mr;
+        sh.row_s[rr] = Sr;
+      }
+    }
+    __syncthreads();
+    if (w == 0)
+      decide_slots<false>(b, ch, K, V, c, K, false, valid, xk, uk, lt, ld, kv0, sh, out_tok,
+                          out_tau, out_kv, out_p, out_q);
+    __syncthreads();
+  }
+  const ReqState st = sh.s_st;
+  if (st.m < 0) return;   // row error: nothing to draw (every workgroup of b agrees)
+
+  // ---- the chunk's masses, exchanged; the chunk holding u*Z finds the token
+  const DrawRows<TIn> R = draw_rows(tgt, drf, b, K, V, st, false);
+  const float u_draw = uni[static_cast<size_t>(b) * (K + 1) + K];
+  const TaggedMasses pub{mass + static_cast<size_t>(b) * nd * 4, tag};
+  const ThreadElems el = thread_elems(R.sp, V, nd, cv, ch, tid);
+  // the vectors stay in registers until the search (the grid is small: occupancy is no concern)
+  float ws, ps;
+  uint4 qt[kDrawVecs], qd[kDrawVecs];
+  thread_mass<false>(R, st, c, V, el, qt, qd, ws, ps);
+  double R0, P0;
+  chunk_mass(ws, ps, sh.s_red, R0, P0);
+  if (tid == 0) pub.publish(ch, R0, P0);
+  bool missing = false;
+  for (int j = tid; j < nd; j += kBlock) {
+    double rm = R0, qm = P0;
+    if (j != ch && !pub.poll(j, wait_polls, rm, qm)) {
+      rm = -1.0;   // marks the entry missing
+      missing = true;
+    }
+    sh.s_cm[j] = make_double2(rm, qm);
+  }
+  if (__syncthreads_or(missing)) help_missing_masses<TIn, false>(R, st, c, V, nd, cv, sh);
+  if (w == 0) find_chunk(nd, u_draw, sh);
+  __syncthreads();
+  if (sh.s_cs != ch) return;
+  search_in_chunk<TIn, false, false, true>(R, st, c, V, nd, cv, ch, el, ws, ps, sh,
+                                           out_tok + static_cast<size_t>(b) * (K + 1) + st.m,
+                                           qt, qd);
+}
+
+// The tag of a one-launch call: a process-wide counter that skips 0 (the value of cleared
+// words). A word is mistaken for a current one only if it was written exactly 2^32 calls earlier
+// and has not been written since.
+uint32_t next_call_tag() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  while (t == 0) t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  return t;
+}
+
 struct SamplePlan {
   KernelPlan stats, draw;
 };
@@ -1095,6 +1335,25 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
   // the statistics pass cut every row into the draw's chunks (chunk masses of an extra row can be
   // taken from its partials)
   const int aligned = (ns == nd && cs == cd) ? 1 : 0;
+  if constexpr (!kKeys && !kMixed && !kPoint) {
+    // small batches: one launch, unless the call is timed by events or captured into a graph (a
+    // replay would repeat the tag, and words of the previous replay would match it)
+    constexpr int kEpv = 16 / static_cast<int>(sizeof(TIn));
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusActive;
+    if (ev == nullptr && fused_shape_ok(B, K, V, kEpv) &&
+        hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
+      const FusedWords fw = fused_words(B, K, V, kEpv);
+      unsigned char* base = static_cast<unsigned char*>(ws) + L.fused;
+      const int n_stats = static_cast<int>(g1);
+      hipLaunchKernelGGL((sample_fused_kernel<TIn>), dim3(static_cast<unsigned>(g1 + n_draw)),
+                         block, 0, stream, t, d, xtok, uni, kv_in, K, V, c, ns, cs, nd, cd,
+                         n_stats, next_call_tag(), reinterpret_cast<uint64_t*>(base + fw.part),
+                         reinterpret_cast<uint64_t*>(base + fw.gath),
+                         reinterpret_cast<uint64_t*>(base + fw.mass), polls, out_tok, out_tau,
+                         out_kv, out_p, out_q);
+      return launch_status();
+    }
+  }
   if (ev == nullptr) {
     hipLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0, stream,
                        t, d, xtok, K, V, c, ns, cs, part1, gath, cm, nclear, kwmax, temps, dlen,

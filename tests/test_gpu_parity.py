@@ -291,6 +291,31 @@ def test_draw_help_path_bit_identical(cid, B, V, rnd):
     compare_sample(wl, h, requests=range(min(wl.B, 16)))
 
 
+@pytest.mark.parametrize("cid,B,K,V,rnd", [(1, 1, 4, None, 60), (2, 1, 5, None, 61),
+                                           (3, 4, 4, 32000, 62), (1, 8, 4, 1003, 63),
+                                           (3, 2, 8, 12345, 64), (2, 1, 1, 2, 65),
+                                           (3, 1, 16, 60000, 66), (1, 3, 2, 257, 67)])
+def test_one_launch_equals_two_launches(cid, B, K, V, rnd):
+    """Small batches run the statistics and the draw in one launch (statistics workgroups first
+    in the grid, tagged words instead of the kernel boundary). Its outputs must equal the
+    two-launch path's (forced by timing the kernels with events) bit for bit, also with a zero
+    poll budget, where every draw workgroup computes each chunk partial, gathered logit and
+    chunk mass it does not find already published; and every request must match the oracle.
+    The shapes cover C1 and C2, ragged vocabularies (V = 2, 257, 1003, 12345), one and several
+    requests, and K from 1 to 16."""
+    kw = dict(B=B, K=K) if V is None else dict(B=B, K=K, V=V)
+    wl = make_workload(cid, rnd, **kw)
+    dev = upload(wl)
+    ws = sv.new_workspace(wl.B, wl.K, wl.V)
+    announce(f"one launch C{cid} B={wl.B} K={wl.K} V={wl.V} {wl.dtype}")
+    one = gpu_sample(wl, dev=dev, ws=ws)
+    two = gpu_sample(wl, dev=dev, ws=ws, two_launch=True)
+    _same_bits(two, one)
+    _same_bits(two, gpu_sample(wl, dev=dev, ws=ws, wait_polls=0))
+    _same_bits(two, gpu_sample(wl, dev=dev, ws=ws))
+    compare_sample(wl, one)
+
+
 @pytest.mark.parametrize("cid,rnd,B,V", [(3, 28, 512, 40000), (1, 29, 512, 40000),
                                          (3, 32, 129, None), (1, 33, 3000, 1000)])
 def test_draw_chunk_groups(cid, rnd, B, V):
@@ -399,12 +424,14 @@ def test_workspace_reuse_across_shapes():
         _same_bits(gpu_mixed(wl, mixed_T, dev=dev, ws=fresh), gpu_mixed(wl, mixed_T, dev=dev, ws=ws))
 
 
-@pytest.mark.parametrize("B,K", [(8, 4), (512, 1)])
+@pytest.mark.parametrize("B,K", [(8, 4), (512, 1), (2, 4)])
 def test_graph_capture_replays(B, K):
     """Captured into a HIP graph (no memset node: the draw's published-mass words are cleared
     by the statistics kernel's own stores), every replay after new inputs are copied in equals
     an eager call on them, with eager calls on the same workspace between the replays. B = 512
-    (2560 draw chunks) runs the draw with two chunks per workgroup."""
+    (2560 draw chunks) runs the draw with two chunks per workgroup. B = 2 runs eagerly in one
+    launch; under capture it takes the two launches (a replayed call tag would match the
+    previous replay's words), so the replays check the one-launch results too."""
     V = 40000
     wls = [make_workload(3, 50 + i, B=B, K=K, V=V) for i in range(3)]
     devs = [upload(w) for w in wls]
