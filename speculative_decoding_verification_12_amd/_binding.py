@@ -130,12 +130,18 @@ def _torch():
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: every pointer parameter is declared c_void_p, so ctypes converts it
+    return None if t is None else t.data_ptr()
 
 
 def _stream(device):
+    """The current HIP stream of `device` as an int (torch's raw-stream query when it has one:
+    it skips building a Stream object on every call)."""
     torch = _torch()
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None and device.index is not None:
+        return raw(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _dtype_code(t) -> int:
@@ -148,13 +154,16 @@ def _dtype_code(t) -> int:
 
 
 def _need(t, name, shape, dtype, device):
+    # one compound test on the common path (these checks run on every call)
+    if t is not None and t.shape == shape and t.dtype == dtype and t.device == device and \
+            t.is_contiguous():
+        return
     if t is None:
         raise ValueError(f"{name} is required")
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device:
         raise ValueError(f"{name}: expected {tuple(shape)} {dtype} on {device}, "
                          f"got {tuple(t.shape)} {t.dtype} on {t.device}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    raise ValueError(f"{name} must be contiguous")
 
 
 def new_workspace(B: int, K: int, V: int, F: int = 1, device="cuda"):
@@ -176,13 +185,7 @@ def spec_workspace_init(workspace):
     return workspace
 
 
-def spec_verify_sample(target, draft, draft_tokens, uniforms, kv_len, temperature, workspace,
-                       out=None, events=None, wait_polls=None):
-    """Speculative-sampling verification. Returns dict(tokens, tau, kv_len, p, q).
-
-    `events` (optional) is a ctypes array of four hipEvent_t handles that then bracket the two
-    kernels; `wait_polls` (optional) bounds the draw's polling for other workgroups' masses.
-    Either one routes the call through spec_verify_sample_ex."""
+def _sample_args(target, draft, draft_tokens, uniforms, kv_len, temperature, workspace, out):
     torch = _torch()
     B, K1, V = target.shape
     K = K1 - 1
@@ -203,6 +206,18 @@ def spec_verify_sample(target, draft, draft_tokens, uniforms, kv_len, temperatur
             _ptr(kv_len), B, K, V, float(temperature), _ptr(out["tokens"]), _ptr(out["tau"]),
             _ptr(out.get("kv_len")), _ptr(out.get("p")), _ptr(out.get("q")), _ptr(workspace),
             workspace.numel(), _stream(dev))
+    return args, out
+
+
+def spec_verify_sample(target, draft, draft_tokens, uniforms, kv_len, temperature, workspace,
+                       out=None, events=None, wait_polls=None):
+    """Speculative-sampling verification. Returns dict(tokens, tau, kv_len, p, q).
+
+    `events` (optional) is a ctypes array of four hipEvent_t handles that then bracket the two
+    kernels; `wait_polls` (optional) bounds the draw's polling for other workgroups' masses.
+    Either one routes the call through spec_verify_sample_ex."""
+    args, out = _sample_args(target, draft, draft_tokens, uniforms, kv_len, temperature,
+                             workspace, out)
     lib = load_library()
     if events is None and wait_polls is None:
         _check("spec_verify_sample", lib.spec_verify_sample(*args))
@@ -303,12 +318,7 @@ def spec_verify_mixed(target, draft, draft_tokens, uniforms, kv_len, temperature
     return out
 
 
-def spec_verify_greedy(target, draft_tokens, kv_len, workspace, temperature=0.0, out=None,
-                       wait_polls=None):
-    """Greedy verification. Returns dict(tokens, tau, kv_len).
-
-    `wait_polls` (optional) bounds the deciders' polling for the chunk results and routes the
-    call through spec_verify_greedy_ex."""
+def _greedy_args(target, draft_tokens, kv_len, workspace, temperature, out):
     torch = _torch()
     B, K1, V = target.shape
     K = K1 - 1
@@ -324,12 +334,47 @@ def spec_verify_greedy(target, draft_tokens, kv_len, workspace, temperature=0.0,
     args = (_ptr(target), _dtype_code(target), _ptr(draft_tokens), _ptr(kv_len), B, K, V,
             float(temperature), _ptr(out["tokens"]), _ptr(out["tau"]), _ptr(out.get("kv_len")),
             _ptr(workspace), workspace.numel(), _stream(dev))
+    return args, out
+
+
+def spec_verify_greedy(target, draft_tokens, kv_len, workspace, temperature=0.0, out=None,
+                       wait_polls=None):
+    """Greedy verification. Returns dict(tokens, tau, kv_len).
+
+    `wait_polls` (optional) bounds the deciders' polling for the chunk results and routes the
+    call through spec_verify_greedy_ex."""
+    args, out = _greedy_args(target, draft_tokens, kv_len, workspace, temperature, out)
     lib = load_library()
     if wait_polls is None:
         _check("spec_verify_greedy", lib.spec_verify_greedy(*args))
     else:
         _check("spec_verify_greedy_ex", lib.spec_verify_greedy_ex(*args, int(wait_polls)))
     return out
+
+
+def _prepared(name, args):
+    fn = getattr(load_library(), name)
+
+    def call():
+        status = fn(*args)
+        if status != 0:
+            _check(name, status)
+    return call
+
+
+def prepared_sample(target, draft, draft_tokens, uniforms, kv_len, temperature, workspace, out):
+    """A zero-argument callable that calls spec_verify_sample on these tensors, checked and
+    marshalled once (the stream is the current one now). For latency-bound loops over the same
+    buffers, where the per-call checks of spec_verify_sample cost host time comparable to the
+    library's own launch."""
+    return _prepared("spec_verify_sample", _sample_args(target, draft, draft_tokens, uniforms,
+                                                        kv_len, temperature, workspace, out)[0])
+
+
+def prepared_greedy(target, draft_tokens, kv_len, workspace, out, temperature=0.0):
+    """prepared_sample for spec_verify_greedy."""
+    return _prepared("spec_verify_greedy", _greedy_args(target, draft_tokens, kv_len, workspace,
+                                                        temperature, out)[0])
 
 
 def spec_predict_outcomes(draft, F, temperature, workspace, out=None):

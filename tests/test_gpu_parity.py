@@ -13,7 +13,7 @@ from gpu_helpers import (announce, compare_fanout, compare_greedy, compare_looku
                          compare_mixed, compare_ngram, compare_point, compare_predict,
                          compare_sample, compare_sample_keys, dev_logits, gpu_fanout, gpu_greedy,
                          gpu_mixed, gpu_ngram, gpu_point, gpu_predict, gpu_sample,
-                         gpu_sample_keys, upload)
+                         gpu_sample_keys, poisoned, upload)
 from synthetic import as_greedy, make_contexts, make_runs, make_tiny_random, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -314,6 +314,34 @@ def test_one_launch_equals_two_launches(cid, B, K, V, rnd):
     _same_bits(two, gpu_sample(wl, dev=dev, ws=ws, wait_polls=0))
     _same_bits(two, gpu_sample(wl, dev=dev, ws=ws))
     compare_sample(wl, one)
+
+
+def test_prepared_calls_equal_binding_calls():
+    """The binding's prepared calls (arguments checked and marshalled once, for latency-bound
+    loops) give what the per-call binding gives, call after call."""
+    wl = make_workload(2, 70)
+    dev = upload(wl)
+    ws = sv.new_workspace(wl.B, wl.K, wl.V)
+    announce("prepared calls C2")
+    ref = gpu_sample(wl, dev=dev, ws=ws)
+    out = dict(tokens=poisoned((wl.B, wl.K + 1), torch.int32), tau=poisoned((wl.B,), torch.int32),
+               kv_len=poisoned((wl.B,), torch.int32), p=poisoned((wl.B, wl.K), torch.float32),
+               q=poisoned((wl.B, wl.K), torch.float32))
+    call = sv.prepared_sample(dev["target"], dev["draft"], dev["tokens"], dev["uniforms"],
+                              dev["kv"], float(wl.T), ws, out)
+    for _ in range(3):
+        call()
+        torch.cuda.synchronize()
+        _same_bits(ref, {k: v.cpu().numpy() for k, v in out.items()})
+    wg = make_workload(2, 70, "greedy")
+    dg = upload(wg, with_draft=False)
+    gref = gpu_greedy(wg, dev=dg, ws=ws)
+    gout = {k: out[k] for k in ("tokens", "tau", "kv_len")}
+    gcall = sv.prepared_greedy(dg["target"], dg["tokens"], dg["kv"], ws, gout)
+    for _ in range(3):
+        gcall()
+        torch.cuda.synchronize()
+        _same_bits(gref, {k: v.cpu().numpy() for k, v in gout.items()})
 
 
 @pytest.mark.parametrize("cid,rnd,B,V", [(3, 28, 512, 40000), (1, 29, 512, 40000),
