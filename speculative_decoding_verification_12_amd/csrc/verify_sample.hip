@@ -28,6 +28,8 @@
 //     When every draft was kept and the statistics pass cut the extra row into the draw's
 //     chunks, the chunk masses come from its partials instead: nothing is re-read but the
 //     chunk holding u*Z, and nothing is exchanged.
+// Small batches (every workgroup of both fitting on the GPU at once) run both as one launch,
+// sample_fused_kernel, with the same arithmetic and the kernel boundary replaced by tagged words.
 // With outcome keys (kKeys) the statistics pass also keeps the draft rows' wave maxima, and the
 // draw's grid has one more workgroup per draft slot that selects the slot's keys meanwhile.
 // Load hints of the statistics pass: non-temporal loads everywhere when the rows it streams
