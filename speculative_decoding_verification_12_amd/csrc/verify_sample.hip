@@ -1482,8 +1482,9 @@ extern "C" int spec_verify_sample(const void* target_logits, const void* draft_l
 // per GPU, loaded with the code object and held until the process ends. In host code this name
 // is a host-side stand-in, not a device address; the device address comes from
 // hipGetSymbolAddress, once per device (scratch_address below), and only that address is ever
-// passed to a kernel. Nothing in it has to start at zero: the call's streaming kernel clears the
-// published-mass words its draw polls, and every other region is written before it is read.
+// passed to a kernel. Nothing in it has to start at zero: in the two-launch form the streaming
+// kernel clears the published-mass words its draw polls, in the one-launch form every polled word
+// carries the call's tag, and every other region is written before it is read.
 static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
 
 namespace sv {
