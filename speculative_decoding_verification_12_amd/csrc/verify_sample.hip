@@ -34,8 +34,10 @@
 // draw's grid has one more workgroup per draft slot that selects the slot's keys meanwhile.
 // Load hints of the statistics pass: non-temporal loads everywhere when the rows it streams
 // exceed the Infinity Cache (the draw's re-read of row m then comes from HBM whatever the hint);
-// for a large pass that fits, non-temporal loads on the draft rows and the extra target row
-// only, so the draw re-reads target row m from the cache and draft row m from HBM at once.
+// for a large pass that fits, non-temporal loads on the draft rows of the later half of the
+// slots and on the extra target row only. The first rejection is most often an early slot, so
+// the draw mostly finds both of its rows in the cache, and the pass streams a third of its
+// bytes at the faster non-temporal rate.
 #include <hip/hip_ext.h>
 
 #include <atomic>
@@ -125,7 +127,8 @@ __device__ __forceinline__ void chunk_argmax(const TIn* row, const RowSpan& sp,
 enum LoadHint : int {
   kHintCached = 0,       // ordinary loads: the rows stay in the Infinity Cache for the draw
   kHintStream = 1,       // non-temporal loads on every row
-  kHintStreamDraft = 2,  // non-temporal loads on the draft rows and the extra target row
+  kHintStreamDraft = 2,  // non-temporal loads on the draft rows of slots >= ceil(K/2) and on
+                         // the extra target row
 };
 
 template <typename TIn, bool kKeys, bool kMixed, bool kPoint>
@@ -193,10 +196,12 @@ __global__ __launch_bounds__(kBlock) void sample_stats_kernel(
   // When the rows do not fit in the Infinity Cache, the re-read comes from HBM either way and
   // non-temporal loads only speed up the pass. When they fit, ordinary loads on every row keep
   // both re-read rows in the cache, which is best while the re-read is latency-bound (small
-  // batches, mixed batches); for a large batch, streaming the draft rows and the extra target
-  // row (whose re-read, on the all-kept path, is one chunk) makes the pass faster and splits
-  // the draw's re-read between the cache and HBM. `nt` is uniform.
-  if (nt == kHintStream || (nt == kHintStreamDraft && r >= K))
+  // batches, mixed batches). For a large batch, the draft rows of the later slots (a first
+  // rejection that late is the less likely) and the extra target row (whose re-read, on the
+  // all-kept path, is one chunk) are streamed: that makes the pass faster, and row m is still
+  // found in the cache for most requests. `nt` is uniform.
+  const bool late_draft = r > K && r - K - 1 >= (K + 1) / 2;
+  if (nt == kHintStream || (nt == kHintStreamDraft && (r == K || late_draft)))
     thread_chunk_stats<TIn, true, true>(row, sp, cr, V, c, m, s);
   else
     thread_chunk_stats<TIn, true, false>(row, sp, cr, V, c, m, s);
@@ -1324,9 +1329,11 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
   const KeyArgs ka{pick, kr.F, kr.exclude, cs, kwmax, kr.out_keys, kr.out_prob};
   const int nd_wg = static_cast<int>(n_draw);
   // load hint of the statistics pass, from the bytes it streams (measured at C3 shapes cut to B
-  // requests, alternating A/B: draft rows streamed at B = 32 (74 MB) and B = 64 (148 MB) saved
-  // 0.5 and 0.9-1.3 us per call; at B <= 16 (37 MB and less) the call is latency-bound and
-  // nothing changed, at B = 1 it lost 0.4 us; a mixed batch lost 1 us)
+  // requests, alternating A/B: every draft row streamed at B = 32 (74 MB) and B = 64 (148 MB)
+  // saved 0.5 and 0.9-1.3 us per call against ordinary loads everywhere, and streaming only the
+  // later half of the slots' draft rows saved another 0.3 and 0.7-0.8 us; at B <= 16 (37 MB and
+  // less) the call is latency-bound and nothing changed, at B = 1 it lost 0.4 us; a mixed batch
+  // lost 1 us)
   const long long streamed =
       static_cast<long long>(B) * (kPoint ? K + 1 : 2 * K + 1) * V *
       static_cast<long long>(sizeof(TIn));
