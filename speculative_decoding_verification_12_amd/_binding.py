@@ -366,7 +366,8 @@ def prepared_sample(target, draft, draft_tokens, uniforms, kv_len, temperature, 
     """A zero-argument callable that calls spec_verify_sample on these tensors, checked and
     marshalled once (the stream is the current one now). For latency-bound loops over the same
     buffers, where the per-call checks of spec_verify_sample cost host time comparable to the
-    library's own launch."""
+    library's own launch. The callable holds raw device pointers: the tensors (inputs, outputs
+    and workspace) must stay alive, and in place, for as long as it is used."""
     return _prepared("spec_verify_sample", _sample_args(target, draft, draft_tokens, uniforms,
                                                         kv_len, temperature, workspace, out)[0])
 
