@@ -352,13 +352,14 @@ def spec_verify_greedy(target, draft_tokens, kv_len, workspace, temperature=0.0,
     return out
 
 
-def _prepared(name, args):
+def _prepared(name, args, tensors):
     fn = getattr(load_library(), name)
 
     def call():
         status = fn(*args)
         if status != 0:
             _check(name, status)
+    call.tensors = tensors   # keeps the buffers behind the raw pointers alive
     return call
 
 
@@ -366,16 +367,18 @@ def prepared_sample(target, draft, draft_tokens, uniforms, kv_len, temperature, 
     """A zero-argument callable that calls spec_verify_sample on these tensors, checked and
     marshalled once (the stream is the current one now). For latency-bound loops over the same
     buffers, where the per-call checks of spec_verify_sample cost host time comparable to the
-    library's own launch. The callable holds raw device pointers: the tensors (inputs, outputs
-    and workspace) must stay alive, and in place, for as long as it is used."""
-    return _prepared("spec_verify_sample", _sample_args(target, draft, draft_tokens, uniforms,
-                                                        kv_len, temperature, workspace, out)[0])
+    library's own launch. The callable holds raw device pointers, and references to the tensors
+    behind them; they must not be resized or moved in place while it is used."""
+    args, out = _sample_args(target, draft, draft_tokens, uniforms, kv_len, temperature,
+                             workspace, out)
+    return _prepared("spec_verify_sample", args,
+                     (target, draft, draft_tokens, uniforms, kv_len, workspace, out))
 
 
 def prepared_greedy(target, draft_tokens, kv_len, workspace, out, temperature=0.0):
     """prepared_sample for spec_verify_greedy."""
-    return _prepared("spec_verify_greedy", _greedy_args(target, draft_tokens, kv_len, workspace,
-                                                        temperature, out)[0])
+    args, out = _greedy_args(target, draft_tokens, kv_len, workspace, temperature, out)
+    return _prepared("spec_verify_greedy", args, (target, draft_tokens, kv_len, workspace, out))
 
 
 def spec_predict_outcomes(draft, F, temperature, workspace, out=None):
