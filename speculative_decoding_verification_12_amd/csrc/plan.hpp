@@ -72,8 +72,10 @@ SV_HD inline KernelPlan draw_plan(int B, int K, int V, int epv) {
   return KernelPlan{kBlock * kDrawVecs, ceil_div(nvec, kBlock * kDrawVecs)};
 }
 // Draw workgroups per CU at once (from the compiler's resource report for gfx950: registers and
-// LDS both allow eight).
+// LDS both allow eight), and four for the one-chunk instance that holds each thread's vectors
+// and its search scan across the mass exchange (104 registers).
 constexpr int kDrawResident = 8;
+constexpr int kDrawResidentHeld = 4;
 // Consecutive chunks of row m that one draw workgroup takes: one while every request's chunks fit
 // on the GPU at once; otherwise as many as bring the draw's workgroups down to one round (at most
 // kMaxDrawGroup). A workgroup whose chunks are all resident never waits for a workgroup that has
@@ -98,6 +100,11 @@ SV_HD inline bool fused_shape_ok(int B, int K, int V, int epv) {
   const bool aligned = s.nchunk == d.nchunk && s.cv == d.cv;
   return !aligned && rows * s.nchunk <= kFusedMaxPartials && grid <= kFusedMaxGrid &&
          draw_group(B, d.nchunk) == 1;
+}
+// Whether the draw runs its one-chunk instance: one workgroup per chunk, every one of them
+// resident at once at `resident` workgroups per CU.
+SV_HD inline bool draw_one_chunk(int B, int nchunk, int resident) {
+  return static_cast<long long>(B) * nchunk <= static_cast<long long>(kCUs) * resident;
 }
 // point-mass drafts: the statistics pass streams only the K+1 target rows, in chunks of at most
 // one pass of the block (16 KiB of bf16) so that even a batch that would fill the GPU once with

@@ -634,21 +634,51 @@ __device__ __forceinline__ void find_chunk(int nchunk, float u_draw, DrawShared&
   }
 }
 
+// The block-level part of the search that does not depend on which chunk holds u*Z: every
+// thread's inclusive scan of its draw mass within its wave, the wave totals and the last thread
+// of positive mass. Taken right after a workgroup publishes its chunk's masses, it overlaps the
+// wait for the other chunks' masses; search_in_chunk then adds the same terms in the same order
+// as when it takes the scan itself, so the bits are the same.
+struct ScanPrep {
+  double wi;
+  double tot[kWaves];
+  int last_thr;
+};
+
+__device__ __forceinline__ ScanPrep scan_prep(float mine, DrawShared& sh) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  ScanPrep p;
+  p.wi = wave_scan_incl(static_cast<double>(mine));
+  if (lane == kWave - 1) sh.s_red[0][w] = p.wi;
+  const int lpos = group_reduce(mine > 0.f ? tid : -1, kWave, OpMax{});
+  if (lane == 0) sh.s_first[w] = lpos;
+  __syncthreads();
+  p.last_thr = -1;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    p.tot[i] = sh.s_red[0][i];
+    p.last_thr = max(p.last_thr, sh.s_first[i]);
+  }
+  return p;   // s_red and s_first are rewritten only after the caller's next barrier
+}
+
 // The workgroup of the chunk holding u*Z (chunk `ch`, its threads' masses ws/ps and elements el
 // as thread_mass gave them): the thread holding it (block prefix scan of the thread masses), then
 // the token among that thread's elements, which it hands to wave 0 through LDS; writes the token
-// to *out_y. Called by the whole workgroup. The vectors are read again here (from the cache):
-// holding every thread's vectors in registers across the mass exchange cost 32 registers per
-// thread in every draw workgroup. With kRecompute (a workgroup that published several chunks
-// and kept none of their thread masses) ws and ps are computed again from the vectors read here:
-// thread_mass gives the same bits.
+// to *out_y. Called by the whole workgroup. With kHeld the caller kept every thread's vectors in
+// registers across the mass exchange (32 more registers per thread) and passes them, and `prep`
+// (if given) is the scan it took meanwhile; otherwise the vectors are read again here (from the
+// cache). With kRecompute (a workgroup that published several chunks and kept none of their
+// thread masses) ws and ps are computed again from the vectors read here: thread_mass gives the
+// same bits.
 template <typename TIn, bool kPoint, bool kRecompute = false, bool kHeld = false>
 __device__ __forceinline__ void search_in_chunk(const DrawRows<TIn>& R, const ReqState& st,
                                                 float c, int V, int nchunk, int cv, int ch,
                                                 const ThreadElems& el, float ws, float ps,
                                                 DrawShared& sh, int32_t* __restrict__ out_y,
                                                 const uint4* held_t = nullptr,
-                                                const uint4* held_d = nullptr) {
+                                                const uint4* held_d = nullptr,
+                                                const ScanPrep* prep = nullptr) {
   using E = Elem<TIn>;
   constexpr int N = E::N;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
@@ -671,17 +701,25 @@ __device__ __forceinline__ void search_in_chunk(const DrawRows<TIn>& R, const Re
   const bool fb = sh.s_fallback != 0;
   const double t = sh.s_t;
   const float mine = use_p ? ps : ws;
-  const double wi = wave_scan_incl(static_cast<double>(mine));
-  if (lane == kWave - 1) sh.s_red[0][w] = wi;
-  const int lpos = group_reduce(mine > 0.f ? tid : -1, kWave, OpMax{});
-  if (lane == 0) sh.s_first[w] = lpos;
-  __syncthreads();
-  double off = sh.s_cb;
+  double wi, off = sh.s_cb;
   int last_thr = -1;
+  if (prep != nullptr && !use_p) {   // uniform: the scan of ws was taken during the exchange
+    wi = prep->wi;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    if (i < w) off += sh.s_red[0][i];
-    last_thr = max(last_thr, sh.s_first[i]);
+    for (int i = 0; i < kWaves; ++i)
+      if (i < w) off += prep->tot[i];
+    last_thr = prep->last_thr;
+  } else {
+    wi = wave_scan_incl(static_cast<double>(mine));
+    if (lane == kWave - 1) sh.s_red[0][w] = wi;
+    const int lpos = group_reduce(mine > 0.f ? tid : -1, kWave, OpMax{});
+    if (lane == 0) sh.s_first[w] = lpos;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      if (i < w) off += sh.s_red[0][i];
+      last_thr = max(last_thr, sh.s_first[i]);
+    }
   }
   const double incl = off + wi;
   const double excl = off + wave_shift_up1(wi);
@@ -973,17 +1011,22 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
 
   if constexpr (!kGroups) {
     // ---- one chunk: its masses, published; then every other chunk mass of the request into
-    // LDS (the general loop below measured 0.3-0.5 us slower per C3 call in this instance)
+    // LDS (the general loop below measured 0.3-0.5 us slower per C3 call in this instance).
+    // Without outcome keys the thread's vectors stay in registers for the search and the
+    // search's scan is taken while the other masses arrive (0.4-0.6 us per C3 call); that takes
+    // the draw to 4 workgroups per CU, and the launch runs this instance only while every chunk
+    // fits at that occupancy. With keys the grid also holds the key selection: lighter form.
+    constexpr bool kHold = !kKeys;
     const int ch = c0;
     const ThreadElems el = thread_elems(R.sp, V, nchunk, cv, ch, tid);
     float ws, ps;
-    {
-      uint4 qt[kDrawVecs], qd[kDrawVecs];
-      thread_mass<kPoint>(R, st, c, V, el, qt, qd, ws, ps);
-    }
+    uint4 qt[kDrawVecs], qd[kDrawVecs];
+    thread_mass<kPoint>(R, st, c, V, el, qt, qd, ws, ps);
     double R0, P0;
     chunk_mass(ws, ps, sh.s_red, R0, P0);
     if (tid == 0) pub.publish(ch, R0, P0);
+    ScanPrep prep;
+    if constexpr (kHold) prep = scan_prep(ws, sh);
     bool missing = false;
     for (int j = tid; j < nchunk; j += kBlock) {
       double r = R0, q = P0;
@@ -997,8 +1040,9 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     if (w == 0) find_chunk(nchunk, u_draw, sh);
     __syncthreads();
     if (sh.s_cs != ch) return;
-    search_in_chunk<TIn, kPoint>(R, st, c, V, nchunk, cv, ch, el, ws, ps, sh,
-                                 out_tok + static_cast<size_t>(b) * (K + 1) + st.m);
+    search_in_chunk<TIn, kPoint, false, kHold>(
+        R, st, c, V, nchunk, cv, ch, el, ws, ps, sh,
+        out_tok + static_cast<size_t>(b) * (K + 1) + st.m, qt, qd, kHold ? &prep : nullptr);
     return;
   }
 
@@ -1250,6 +1294,7 @@ __global__ __launch_bounds__(kBlock) void sample_fused_kernel(
   double R0, P0;
   chunk_mass(ws, ps, sh.s_red, R0, P0);
   if (tid == 0) pub.publish(ch, R0, P0);
+  const ScanPrep prep = scan_prep(ws, sh);
   bool missing = false;
   for (int j = tid; j < nd; j += kBlock) {
     double rm = R0, qm = P0;
@@ -1265,7 +1310,7 @@ __global__ __launch_bounds__(kBlock) void sample_fused_kernel(
   if (sh.s_cs != ch) return;
   search_in_chunk<TIn, false, false, true>(R, st, c, V, nd, cv, ch, el, ws, ps, sh,
                                            out_tok + static_cast<size_t>(b) * (K + 1) + st.m,
-                                           qt, qd);
+                                           qt, qd, &prep);
 }
 
 // The tag of a one-launch call: a process-wide counter that skips 0 (the value of cleared
@@ -1306,6 +1351,10 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
                     const KeyRequest& kr, const float* temps, const int32_t* dlen = nullptr) {
   const size_t g1 = static_cast<size_t>(B) * (kPoint ? K + 1 : 2 * K + 1) * P.stats.nchunk;
   const int group = draw_group(B, P.draw.nchunk);   // chunks per draw workgroup
+  // the one-chunk instance, while every chunk fits on the GPU at its occupancy; otherwise the
+  // grouped instance (one chunk per workgroup too, if they fit at its higher occupancy)
+  const bool one_chunk = draw_one_chunk(B, P.draw.nchunk,
+                                        kKeys ? kDrawResident : kDrawResidentHeld);
   const size_t n_chunks = static_cast<size_t>(B) * P.draw.nchunk;
   const size_t n_draw = static_cast<size_t>(B) * ((P.draw.nchunk + group - 1) / group);
   // with keys, one more workgroup per draft slot selects that slot's keys during the draw
@@ -1367,7 +1416,7 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
     hipLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0, stream,
                        t, d, xtok, K, V, c, ns, cs, part1, gath, cm, nclear, kwmax, temps, dlen,
                        nt);
-    if (group > 1)
+    if (!one_chunk)
       hipLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint, true>), grid2, block, 0,
                          stream, t, d, xtok, uni, kv_in, K, V, c, ns,
                          static_cast<const float2*>(part1), static_cast<const float*>(gath), nd,
@@ -1384,7 +1433,7 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
     hipExtLaunchKernelGGL((sample_stats_kernel<TIn, kKeys, kMixed, kPoint>), grid1, block, 0,
                           stream, ev[0], ev[1], 0, t, d, xtok, K, V, c, ns, cs, part1, gath, cm,
                           nclear, kwmax, temps, dlen, nt);
-    if (group > 1)
+    if (!one_chunk)
       hipExtLaunchKernelGGL((sample_draw_kernel<TIn, kKeys, kMixed, kPoint, true>), grid2, block,
                             0, stream, ev[2], ev[3], 0, t, d, xtok, uni, kv_in, K, V, c, ns,
                             static_cast<const float2*>(part1), static_cast<const float*>(gath),

@@ -345,14 +345,16 @@ def test_prepared_calls_equal_binding_calls():
 
 
 @pytest.mark.parametrize("cid,rnd,B,V", [(3, 28, 512, 40000), (1, 29, 512, 40000),
-                                         (3, 32, 129, None), (1, 33, 3000, 1000)])
+                                         (3, 32, 129, None), (1, 33, 3000, 1000),
+                                         (3, 34, 96, None)])
 def test_draw_chunk_groups(cid, rnd, B, V):
     """More draw chunks than the GPU holds at once, so each draw workgroup takes several
     consecutive chunks of row m. B=512, K=1, V=40000 of the C3 recipe (bf16, 5 chunks a row, 2560
     chunks) gives two chunks per workgroup and one in the last; the C1 recipe (fp32, 10 chunks a
     row) gives three, three, three and one. B=129 at C3's V (2064 chunks, just over one round)
     gives two each; B=3000 rows of one chunk (V=1000 fp32) runs the grouped kernel with one chunk
-    in every workgroup. With K = 1 about half the requests keep their draft, so both the residual
+    in every workgroup, and so does B=96 at C3's V (1536 chunks: too many for the one-chunk
+    kernel at its four workgroups per CU, one round for the grouped kernel). With K = 1 about half the requests keep their draft, so both the residual
     draw and the all-kept draw run with groups. The default and the zero poll budget (every mass
     not found published is computed by the workgroup that needs it) agree bit for bit, and every
     request matches the oracle."""
