@@ -134,9 +134,9 @@ def _draw_group(B, nd):
 def _draw_kernel(flags, B, nd):
     """(kernel name, workgroups) of a draw launch with template flags `flags` (keys, mixed,
     point) over B requests of nd chunks (keys add B·K workgroups on top). The one-chunk
-    instance runs while every chunk fits at its occupancy: 4 workgroups per CU (8 with keys)."""
+    instance runs while every chunk fits at its occupancy: 5 workgroups per CU (8 with keys)."""
     g = _draw_group(B, nd)
-    one = B * nd <= 256 * (8 if flags.startswith("true") else 4)
+    one = B * nd <= 256 * (8 if flags.startswith("true") else 5)
     name = f"sample_draw_kernel<unsigned short, {flags}, {'false' if one else 'true'}>"
     return name, B * -(-nd // g)
 

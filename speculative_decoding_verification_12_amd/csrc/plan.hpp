@@ -72,10 +72,10 @@ SV_HD inline KernelPlan draw_plan(int B, int K, int V, int epv) {
   return KernelPlan{kBlock * kDrawVecs, ceil_div(nvec, kBlock * kDrawVecs)};
 }
 // Draw workgroups per CU at once (from the compiler's resource report for gfx950: registers and
-// LDS both allow eight), and four for the one-chunk instance that holds each thread's vectors
-// and its search scan across the mass exchange (104 registers).
+// LDS both allow eight), and five for the one-chunk instance that holds each thread's vectors
+// across the mass exchange (92-93 registers).
 constexpr int kDrawResident = 8;
-constexpr int kDrawResidentHeld = 4;
+constexpr int kDrawResidentHeld = 5;
 // Consecutive chunks of row m that one draw workgroup takes: one while every request's chunks fit
 // on the GPU at once; otherwise as many as bring the draw's workgroups down to one round (at most
 // kMaxDrawGroup). A workgroup whose chunks are all resident never waits for a workgroup that has

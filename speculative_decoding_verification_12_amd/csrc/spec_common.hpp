@@ -243,6 +243,7 @@ struct OpAdd {
   template <typename T> __device__ T operator()(T a, T b) const { return a + b; }
 };
 struct OpMax {
+  __device__ double operator()(double a, double b) const { return fmax(a, b); }
   __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
   __device__ int operator()(int a, int b) const { return max(a, b); }
 };

@@ -580,10 +580,19 @@ __device__ __forceinline__ DrawRows<TIn> draw_rows(const TIn* tgt, const TIn* dr
   return R;
 }
 
-// Wave 0, once sh.s_cm holds every chunk's (residual mass, target mass): float64 prefix scan over
-// the chunks (lane l takes a contiguous run of them), total Z, threshold t = u*Z, and the chunk
-// holding it, left in sh (s_cs, s_usep, s_fallback, s_cb = the mass before that chunk, s_t).
-__device__ __forceinline__ void find_chunk(int nchunk, float u_draw, DrawShared& sh) {
+// The chunk holding u*Z, as every lane of a wave finds it once sh.s_cm holds every chunk's
+// (residual mass, target mass): float64 prefix scan over the chunks (lane l takes a contiguous run
+// of them), total Z, threshold t = u*Z, then the chunk whose running mass passes t. Every wave
+// that runs it gets the same bits, in registers.
+struct ChunkPick {
+  int cs;          // the chunk holding u*Z
+  bool usep;       // no residual mass left by round-off: the draw takes p
+  bool fallback;   // round-off: no chunk's running mass passed t (cs is the last of positive mass)
+  double cb;       // mass of the chunks before cs
+  double t;        // u*Z
+};
+
+__device__ __forceinline__ ChunkPick pick_chunk(int nchunk, float u_draw, const DrawShared& sh) {
   const int lane = threadIdx.x & (kWave - 1);
   const int per = (nchunk + kWave - 1) / kWave;
   const int j0 = min(lane * per, nchunk), j1 = min(j0 + per, nchunk);
@@ -598,39 +607,48 @@ __device__ __forceinline__ void find_chunk(int nchunk, float u_draw, DrawShared&
   }
   const double ri = wave_scan_incl(rl), pi = wave_scan_incl(pl);
   const double zr = readlane_f64(ri, kWave - 1), zp = readlane_f64(pi, kWave - 1);
-  const bool usep = !(zr > 0.0);   // no residual mass left by round-off: draw from p
-  const double Z = usep ? zp : zr;
-  const double t = static_cast<double>(u_draw) * Z;
-  const double incl = usep ? pi : ri;
+  ChunkPick f;
+  f.usep = !(zr > 0.0);
+  const double Z = f.usep ? zp : zr;
+  f.t = static_cast<double>(u_draw) * Z;
+  const double incl = f.usep ? pi : ri;
   const double excl = wave_shift_up1(incl);
-  const unsigned long long cross = __ballot(incl > t);
-  const int last_pos = group_reduce(usep ? lp : lr, kWave, OpMax{});
+  const unsigned long long cross = __ballot(incl > f.t);
+  const int last_pos = group_reduce(f.usep ? lp : lr, kWave, OpMax{});
   if (cross) {
+    // lane L's run holds the crossing; every lane walks its own run, lane L's result is taken
     const int L = __ffsll(static_cast<long long>(cross)) - 1;
-    if (lane == L) {
-      double cum = excl;
-      int cs = -1, lastp = -1;
-      for (int j = j0; j < j1; ++j) {
-        const double mj = usep ? sh.s_cm[j].y : sh.s_cm[j].x;
-        if (mj > 0.0) lastp = j;
-        if (cum + mj > t) {
-          cs = j;
-          break;
-        }
-        cum += mj;
+    double cum = excl;
+    int cs = -1, lastp = -1;
+    for (int j = j0; j < j1; ++j) {
+      const double mj = f.usep ? sh.s_cm[j].y : sh.s_cm[j].x;
+      if (mj > 0.0) lastp = j;
+      if (cum + mj > f.t) {
+        cs = j;
+        break;
       }
-      sh.s_cs = cs >= 0 ? cs : max(lastp, 0);
-      sh.s_fallback = cs >= 0 ? 0 : 1;
-      sh.s_cb = cum;
+      cum += mj;
     }
-  } else if (lane == 0) {   // round-off: the last chunk of positive weight
-    sh.s_cs = max(last_pos, 0);
-    sh.s_fallback = 1;
-    sh.s_cb = 0.0;
+    f.cs = __builtin_amdgcn_readlane(cs >= 0 ? cs : max(lastp, 0), L);
+    f.fallback = __builtin_amdgcn_readlane(cs >= 0 ? 0 : 1, L) != 0;
+    f.cb = readlane_f64(cum, L);
+  } else {   // round-off: the last chunk of positive weight
+    f.cs = max(last_pos, 0);
+    f.fallback = true;
+    f.cb = 0.0;
   }
-  if (lane == 0) {
-    sh.s_usep = usep ? 1 : 0;
-    sh.s_t = t;
+  return f;
+}
+
+// Wave 0's pick_chunk, left in sh (s_cs, s_usep, s_fallback, s_cb, s_t) for the workgroup.
+__device__ __forceinline__ void find_chunk(int nchunk, float u_draw, DrawShared& sh) {
+  const ChunkPick f = pick_chunk(nchunk, u_draw, sh);
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    sh.s_cs = f.cs;
+    sh.s_fallback = f.fallback ? 1 : 0;
+    sh.s_cb = f.cb;
+    sh.s_usep = f.usep ? 1 : 0;
+    sh.s_t = f.t;
   }
 }
 
@@ -641,7 +659,8 @@ __device__ __forceinline__ void find_chunk(int nchunk, float u_draw, DrawShared&
 // as when it takes the scan itself, so the bits are the same.
 struct ScanPrep {
   double wi;
-  double tot[kWaves];
+  double tot[kWaves];   // every wave's total (its last lane's inclusive sum)
+  double top[kWaves];   // every wave's largest inclusive sum
   int last_thr;
 };
 
@@ -650,16 +669,69 @@ __device__ __forceinline__ ScanPrep scan_prep(float mine, DrawShared& sh) {
   ScanPrep p;
   p.wi = wave_scan_incl(static_cast<double>(mine));
   if (lane == kWave - 1) sh.s_red[0][w] = p.wi;
+  const double top = group_reduce(p.wi, kWave, OpMax{});
+  if (lane == 0) sh.s_red[1][w] = top;
   const int lpos = group_reduce(mine > 0.f ? tid : -1, kWave, OpMax{});
   if (lane == 0) sh.s_first[w] = lpos;
   __syncthreads();
-  p.last_thr = -1;
+  // the same in every lane: kept in scalar registers
+  int last = -1;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) {
-    p.tot[i] = sh.s_red[0][i];
-    p.last_thr = max(p.last_thr, sh.s_first[i]);
+    p.tot[i] = readlane_f64(sh.s_red[0][i], 0);
+    p.top[i] = readlane_f64(sh.s_red[1][i], 0);
+    last = max(last, sh.s_first[i]);
   }
+  p.last_thr = __builtin_amdgcn_readfirstlane(last);
   return p;   // s_red and s_first are rewritten only after the caller's next barrier
+}
+
+// One wave, once thread `first` of chunk `ch` has left its vectors in sh.s_raw and its prefix
+// mass in sh.s_cb: one element of that thread per lane (at most 7 + 32 + 7 for bf16), in token
+// order, weights as in its mass, float64 prefix scan, the first element past t (with walk_fb, the
+// last element of positive weight), written to *out_y.
+template <typename TIn, bool kPoint>
+__device__ __forceinline__ void token_in_thread(const DrawRows<TIn>& R, const ReqState& st,
+                                                float c, int V, int nchunk, int cv, int ch,
+                                                int first, bool use_p, bool walk_fb, double t,
+                                                const DrawShared& sh,
+                                                int32_t* __restrict__ out_y) {
+  using E = Elem<TIn>;
+  constexpr int N = E::N;
+  const int lane = threadIdx.x & (kWave - 1);
+  const ThreadElems fe = thread_elems(R.sp, V, nchunk, cv, ch, first);
+  const int nvel = fe.nv * N;
+  const bool has = lane < fe.nh + nvel + fe.nt;
+  int tok = 0;
+  float lt = -INFINITY, ld = -INFINITY;
+  if (has) {
+    if (lane < fe.nh || lane >= fe.nh + nvel) {   // scalar head or tail element
+      tok = lane < fe.nh ? lane : fe.tail0 + (lane - fe.nh - nvel);
+      lt = E::one(R.t, tok);
+      if (R.resid) ld = E::one(R.d, tok);
+    } else {
+      const int k = lane - fe.nh, i = k / N, e = k % N;
+      tok = R.sp.head + (fe.v0 + i) * N + e;
+      lt = E::from_words(&sh.s_raw[0][4 * i], e);
+      if (R.resid) ld = R.d_aligned ? E::from_words(&sh.s_raw[1][4 * i], e) : E::one(R.d, tok);
+    }
+  }
+  float we = 0.f;
+  if (has) {
+    const float p = prob_exp2(lt, st.M_t, c, st.ls_t);
+    if constexpr (kPoint)
+      we = (tok == R.mask && !use_p) ? 0.f : p;
+    else
+      we = (!R.resid || use_p) ? p : fmaxf(p - prob_exp2(ld, st.M_d, c, st.ls_d), 0.f);
+  }
+  const double cum = sh.s_cb + wave_scan_incl(static_cast<double>(we));
+  const unsigned long long pos = __ballot(we > 0.f);
+  const unsigned long long hit = walk_fb ? 0ull : __ballot(we > 0.f && cum > t);
+  int y;
+  if (hit) y = __shfl(tok, __ffsll(static_cast<long long>(hit)) - 1, kWave);
+  else if (pos) y = __shfl(tok, 63 - __clzll(static_cast<long long>(pos)), kWave);
+  else y = 0;   // no positive weight at all: only for rows without a finite logit
+  if (lane == 0) *out_y = y;
 }
 
 // The workgroup of the chunk holding u*Z (chunk `ch`, its threads' masses ws/ps and elements el
@@ -679,8 +751,6 @@ __device__ __forceinline__ void search_in_chunk(const DrawRows<TIn>& R, const Re
                                                 const uint4* held_t = nullptr,
                                                 const uint4* held_d = nullptr,
                                                 const ScanPrep* prep = nullptr) {
-  using E = Elem<TIn>;
-  constexpr int N = E::N;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   // every thread reads its vectors again now (cache hits), so the one that turns out to hold
   // u*Z has them when the block scan below has named it (kHeld: the caller kept them)
@@ -750,44 +820,60 @@ __device__ __forceinline__ void search_in_chunk(const DrawRows<TIn>& R, const Re
   }
   __syncthreads();
 
-  // ---- wave 0: one element of that thread per lane (at most 7 + 32 + 7 for bf16), in token
-  // order, weights as in its mass, float64 prefix scan, first element past u*Z
-  if (w == 0) {
-    const ThreadElems fe = thread_elems(R.sp, V, nchunk, cv, ch, first);
-    const int nvel = fe.nv * N;
-    const bool has = lane < fe.nh + nvel + fe.nt;
-    int tok = 0;
-    float lt = -INFINITY, ld = -INFINITY;
-    if (has) {
-      if (lane < fe.nh || lane >= fe.nh + nvel) {   // scalar head or tail element
-        tok = lane < fe.nh ? lane : fe.tail0 + (lane - fe.nh - nvel);
-        lt = E::one(R.t, tok);
-        if (R.resid) ld = E::one(R.d, tok);
-      } else {
-        const int k = lane - fe.nh, i = k / N, e = k % N;
-        tok = R.sp.head + (fe.v0 + i) * N + e;
-        lt = E::from_words(&sh.s_raw[0][4 * i], e);
-        if (R.resid) ld = R.d_aligned ? E::from_words(&sh.s_raw[1][4 * i], e) : E::one(R.d, tok);
-      }
+  if (w == 0) token_in_thread<TIn, kPoint>(R, st, c, V, nchunk, cv, ch, first, use_p, walk_fb, t,
+                                          sh, out_y);
+}
+
+// The search of search_in_chunk for a workgroup that kept its vectors and took its scan during
+// the exchange (prep), when the draw takes the residual or bonus weights (not the round-off
+// fallback to p): no workgroup barrier. The wave totals and each wave's largest inclusive sum
+// tell every wave, with the same additions in the same order as the block scan, which wave's
+// ballot would find the first thread past t; that wave alone goes on, its lane of that thread
+// hands its vectors over through LDS (one wave: no barrier), and it finds the token.
+template <typename TIn, bool kPoint>
+__device__ __forceinline__ void search_in_wave(const DrawRows<TIn>& R, const ReqState& st,
+                                               float c, int V, int nchunk, int cv, int ch,
+                                               const ChunkPick& f, const ScanPrep& prep,
+                                               const uint4 (&qt)[kDrawVecs],
+                                               const uint4 (&qd)[kDrawVecs], DrawShared& sh,
+                                               int32_t* __restrict__ out_y) {
+  const int tid = threadIdx.x, w = tid / kWave;
+  const double t = f.t;
+  int owner = -1;        // the first wave with a thread past t
+  double off_w = f.cb;   // this wave's offset, as the block scan forms it
+  {
+    double off = f.cb;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      if (i == w) off_w = off;
+      if (owner < 0 && !f.fallback && off + prep.top[i] > t) owner = i;
+      off += prep.tot[i];
     }
-    float we = 0.f;
-    if (has) {
-      const float p = prob_exp2(lt, st.M_t, c, st.ls_t);
-      if constexpr (kPoint)
-        we = (tok == R.mask && !use_p) ? 0.f : p;
-      else
-        we = (!R.resid || use_p) ? p
-                                 : fmaxf(p - prob_exp2(ld, st.M_d, c, st.ls_d), 0.f);
-    }
-    const double cum = sh.s_cb + wave_scan_incl(static_cast<double>(we));
-    const unsigned long long pos = __ballot(we > 0.f);
-    const unsigned long long hit = walk_fb ? 0ull : __ballot(we > 0.f && cum > t);
-    int y;
-    if (hit) y = __shfl(tok, __ffsll(static_cast<long long>(hit)) - 1, kWave);
-    else if (pos) y = __shfl(tok, 63 - __clzll(static_cast<long long>(pos)), kWave);
-    else y = 0;   // no positive weight at all: only for rows without a finite logit
-    if (lane == 0) *out_y = y;
   }
+  const bool walk_fb = owner < 0;   // round-off (or fallback): the last thread of positive mass
+  const int first_w = walk_fb ? max(prep.last_thr, 0) / kWave : owner;
+  if (w != first_w) return;
+  const double incl = off_w + prep.wi;
+  const double excl = off_w + wave_shift_up1(prep.wi);
+  const unsigned long long cross = __ballot(incl > t);
+  const int first = walk_fb ? max(prep.last_thr, 0)
+                            : w * kWave + __ffsll(static_cast<long long>(cross)) - 1;
+  if (tid == first) {   // hand this thread's vectors and prefix to its wave
+#pragma unroll
+    for (int i = 0; i < kDrawVecs; ++i) {
+      sh.s_raw[0][4 * i] = qt[i].x;
+      sh.s_raw[0][4 * i + 1] = qt[i].y;
+      sh.s_raw[0][4 * i + 2] = qt[i].z;
+      sh.s_raw[0][4 * i + 3] = qt[i].w;
+      sh.s_raw[1][4 * i] = qd[i].x;
+      sh.s_raw[1][4 * i + 1] = qd[i].y;
+      sh.s_raw[1][4 * i + 2] = qd[i].z;
+      sh.s_raw[1][4 * i + 3] = qd[i].w;
+    }
+    sh.s_cb = excl;
+  }
+  __builtin_amdgcn_wave_barrier();
+  token_in_thread<TIn, kPoint>(R, st, c, V, nchunk, cv, ch, first, false, walk_fb, t, sh, out_y);
 }
 
 // Every chunk mass marked missing in sh.s_cm (R < 0: not published within the poll budget),
@@ -1012,9 +1098,10 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
   if constexpr (!kGroups) {
     // ---- one chunk: its masses, published; then every other chunk mass of the request into
     // LDS (the general loop below measured 0.3-0.5 us slower per C3 call in this instance).
-    // Without outcome keys the thread's vectors stay in registers for the search and the
-    // search's scan is taken while the other masses arrive (0.4-0.6 us per C3 call); that takes
-    // the draw to 4 workgroups per CU, and the launch runs this instance only while every chunk
+    // Without outcome keys the thread's vectors stay in registers for the search, the search's
+    // scan is taken while the other masses arrive, and every wave finds the chunk holding u*Z
+    // itself, so the owner's search runs in one wave without a workgroup barrier. That takes
+    // the draw to 5 workgroups per CU, and the launch runs this instance only while every chunk
     // fits at that occupancy. With keys the grid also holds the key selection: lighter form.
     constexpr bool kHold = !kKeys;
     const int ch = c0;
@@ -1037,6 +1124,15 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       sh.s_cm[j] = make_double2(r, q);
     }
     if (__syncthreads_or(missing)) help_missing_masses<TIn, kPoint>(R, st, c, V, nchunk, cv, sh);
+    if constexpr (kHold) {   // every wave finds the chunk; the owner's search needs no barrier
+      const ChunkPick f = pick_chunk(nchunk, u_draw, sh);
+      if (f.cs != ch) return;
+      if (!f.usep) {
+        search_in_wave<TIn, kPoint>(R, st, c, V, nchunk, cv, ch, f, prep, qt, qd, sh,
+                                    out_tok + static_cast<size_t>(b) * (K + 1) + st.m);
+        return;
+      }
+    }
     if (w == 0) find_chunk(nchunk, u_draw, sh);
     __syncthreads();
     if (sh.s_cs != ch) return;
@@ -1305,6 +1401,15 @@ __global__ __launch_bounds__(kBlock) void sample_fused_kernel(
     sh.s_cm[j] = make_double2(rm, qm);
   }
   if (__syncthreads_or(missing)) help_missing_masses<TIn, false>(R, st, c, V, nd, cv, sh);
+  {
+    const ChunkPick f = pick_chunk(nd, u_draw, sh);
+    if (f.cs != ch) return;
+    if (!f.usep) {
+      search_in_wave<TIn, false>(R, st, c, V, nd, cv, ch, f, prep, qt, qd, sh,
+                                 out_tok + static_cast<size_t>(b) * (K + 1) + st.m);
+      return;
+    }
+  }
   if (w == 0) find_chunk(nd, u_draw, sh);
   __syncthreads();
   if (sh.s_cs != ch) return;

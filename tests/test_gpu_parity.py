@@ -354,7 +354,7 @@ def test_draw_chunk_groups(cid, rnd, B, V):
     row) gives three, three, three and one. B=129 at C3's V (2064 chunks, just over one round)
     gives two each; B=3000 rows of one chunk (V=1000 fp32) runs the grouped kernel with one chunk
     in every workgroup, and so does B=96 at C3's V (1536 chunks: too many for the one-chunk
-    kernel at its four workgroups per CU, one round for the grouped kernel). With K = 1 about half the requests keep their draft, so both the residual
+    kernel at its five workgroups per CU, one round for the grouped kernel). With K = 1 about half the requests keep their draft, so both the residual
     draw and the all-kept draw run with groups. The default and the zero poll budget (every mass
     not found published is computed by the workgroup that needs it) agree bit for bit, and every
     request matches the oracle."""
