@@ -585,6 +585,25 @@ def test_c4_large_full(rnd):
     assert np.all(gg["tau"][wl.forced] == wl.K + 1)
 
 
+@pytest.mark.parametrize("rnd", range(2, 20))
+def test_c4_recipe_more_rounds(rnd):
+    """Rounds 2-19 of the C4 recipe (K = 8, V = 152064, draft = target + N(0, 1), half the
+    requests forced to keep every draft), at 32 requests a round so that the host's generation
+    of the logits stays short: with the two full-size rounds above, twenty seeded rounds. Every
+    request of the sampling and the greedy call against the oracle."""
+    wl = make_workload(4, rnd, B=32)
+    dev = upload(wl)
+    announce(f"C4 recipe round {rnd}, B={wl.B}")
+    gpu = gpu_sample(wl, dev=dev)
+    n, f, fb = compare_sample(wl, gpu)
+    announce(f"C4 recipe round {rnd}: {n} checked, {f} flagged, {fb} differ")
+    _tally("C4 recipe B=32", n, f, fb, rnd == 19)
+    assert np.all(gpu["tau"][wl.forced] == wl.K + 1)
+    wg = as_greedy(wl)
+    dev["tokens"] = torch.from_numpy(wg.tokens).cuda()
+    compare_greedy(wg, gpu_greedy(wg, dev=dev))
+
+
 HITS = {}
 
 
