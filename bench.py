@@ -131,12 +131,12 @@ def _draw_group(B, nd):
     return max(1, min(4, -(-(B * nd) // (256 * 8))))
 
 
-def _draw_kernel(flags, B, nd):
+def _draw_kernel(flags, B, nd, K=0):
     """(kernel name, workgroups) of a draw launch with template flags `flags` (keys, mixed,
     point) over B requests of nd chunks (keys add B·K workgroups on top). The one-chunk
-    instance runs while every chunk fits at its occupancy: 5 workgroups per CU (8 with keys)."""
+    instance runs while its whole grid fits at 5 workgroups per CU."""
     g = _draw_group(B, nd)
-    one = B * nd <= 256 * (8 if flags.startswith("true") else 5)
+    one = B * (nd + (K if flags.startswith("true") else 0)) <= 256 * 5
     name = f"sample_draw_kernel<unsigned short, {flags}, {'false' if one else 'true'}>"
     return name, B * -(-nd // g)
 
@@ -164,8 +164,8 @@ def bench_launches():
         if cid == 3:
             out += [("c5_keys_stats", "sample_stats_kernel<unsigned short, true, false, false>",
                      rows * ns, rows * V * 2, "C5 verification with keys, statistics pass"),
-                    ("c5_keys_draw", _draw_kernel("true, false, false", B, nd)[0],
-                     _draw_kernel("true, false, false", B, nd)[1] + B * K, None,
+                    ("c5_keys_draw", _draw_kernel("true, false, false", B, nd, K)[0],
+                     _draw_kernel("true, false, false", B, nd, K)[1] + B * K, None,
                      "C5 verification with keys, draw and key selection"),
                     ("c3_mixed_stats", "sample_stats_kernel<unsigned short, false, true, false>",
                      rows * ns, (B // 2) * (2 * K + 1) * V * 2 + (B // 2) * (K + 1) * V * 2,

@@ -73,7 +73,7 @@ SV_HD inline KernelPlan draw_plan(int B, int K, int V, int epv) {
 }
 // Draw workgroups per CU at once (from the compiler's resource report for gfx950: registers and
 // LDS both allow eight), and five for the one-chunk instance that holds each thread's vectors
-// across the mass exchange (92-93 registers).
+// across the mass exchange (92-93 registers; 84-86 for fp32 rows).
 constexpr int kDrawResident = 8;
 constexpr int kDrawResidentHeld = 5;
 // Consecutive chunks of row m that one draw workgroup takes: one while every request's chunks fit
@@ -101,10 +101,11 @@ SV_HD inline bool fused_shape_ok(int B, int K, int V, int epv) {
   return !aligned && rows * s.nchunk <= kFusedMaxPartials && grid <= kFusedMaxGrid &&
          draw_group(B, d.nchunk) == 1;
 }
-// Whether the draw runs its one-chunk instance: one workgroup per chunk, every one of them
-// resident at once at `resident` workgroups per CU.
-SV_HD inline bool draw_one_chunk(int B, int nchunk, int resident) {
-  return static_cast<long long>(B) * nchunk <= static_cast<long long>(kCUs) * resident;
+// Whether the draw runs its one-chunk instance: `per_request` workgroups per request (one per
+// chunk, plus one per slot with outcome keys), every one of them resident at once at `resident`
+// workgroups per CU.
+SV_HD inline bool draw_one_chunk(int B, int per_request, int resident) {
+  return static_cast<long long>(B) * per_request <= static_cast<long long>(kCUs) * resident;
 }
 // point-mass drafts: the statistics pass streams only the K+1 target rows, in chunks of at most
 // one pass of the block (16 KiB of bf16) so that even a batch that would fill the GPU once with

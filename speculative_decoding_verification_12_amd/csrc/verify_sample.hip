@@ -1098,12 +1098,11 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
   if constexpr (!kGroups) {
     // ---- one chunk: its masses, published; then every other chunk mass of the request into
     // LDS (the general loop below measured 0.3-0.5 us slower per C3 call in this instance).
-    // Without outcome keys the thread's vectors stay in registers for the search, the search's
-    // scan is taken while the other masses arrive, and every wave finds the chunk holding u*Z
-    // itself, so the owner's search runs in one wave without a workgroup barrier. That takes
-    // the draw to 5 workgroups per CU, and the launch runs this instance only while every chunk
-    // fits at that occupancy. With keys the grid also holds the key selection: lighter form.
-    constexpr bool kHold = !kKeys;
+    // The thread's vectors stay in registers for the search, the search's scan is taken while
+    // the other masses arrive, and every wave finds the chunk holding u*Z itself, so the owner's
+    // search runs in one wave without a workgroup barrier. That takes the draw to 5 workgroups
+    // per CU, and the launch runs this instance only while its whole grid (with the key
+    // selection's workgroups) fits at that occupancy.
     const int ch = c0;
     const ThreadElems el = thread_elems(R.sp, V, nchunk, cv, ch, tid);
     float ws, ps;
@@ -1112,8 +1111,7 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     double R0, P0;
     chunk_mass(ws, ps, sh.s_red, R0, P0);
     if (tid == 0) pub.publish(ch, R0, P0);
-    ScanPrep prep;
-    if constexpr (kHold) prep = scan_prep(ws, sh);
+    const ScanPrep prep = scan_prep(ws, sh);
     bool missing = false;
     for (int j = tid; j < nchunk; j += kBlock) {
       double r = R0, q = P0;
@@ -1124,21 +1122,18 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
       sh.s_cm[j] = make_double2(r, q);
     }
     if (__syncthreads_or(missing)) help_missing_masses<TIn, kPoint>(R, st, c, V, nchunk, cv, sh);
-    if constexpr (kHold) {   // every wave finds the chunk; the owner's search needs no barrier
-      const ChunkPick f = pick_chunk(nchunk, u_draw, sh);
-      if (f.cs != ch) return;
-      if (!f.usep) {
-        search_in_wave<TIn, kPoint>(R, st, c, V, nchunk, cv, ch, f, prep, qt, qd, sh,
-                                    out_tok + static_cast<size_t>(b) * (K + 1) + st.m);
-        return;
-      }
+    const ChunkPick f = pick_chunk(nchunk, u_draw, sh);   // every wave: no barrier
+    if (f.cs != ch) return;
+    int32_t* const out_y = out_tok + static_cast<size_t>(b) * (K + 1) + st.m;
+    if (!f.usep) {
+      search_in_wave<TIn, kPoint>(R, st, c, V, nchunk, cv, ch, f, prep, qt, qd, sh, out_y);
+      return;
     }
+    // rare (round-off left no residual mass): the draw takes p, searched by the whole workgroup
     if (w == 0) find_chunk(nchunk, u_draw, sh);
     __syncthreads();
-    if (sh.s_cs != ch) return;
-    search_in_chunk<TIn, kPoint, false, kHold>(
-        R, st, c, V, nchunk, cv, ch, el, ws, ps, sh,
-        out_tok + static_cast<size_t>(b) * (K + 1) + st.m, qt, qd, kHold ? &prep : nullptr);
+    search_in_chunk<TIn, kPoint, false, true>(R, st, c, V, nchunk, cv, ch, el, ws, ps, sh, out_y,
+                                              qt, qd, &prep);
     return;
   }
 
@@ -1458,8 +1453,7 @@ int launch_sample_t(const void* target, const void* draft, const int32_t* xtok, 
   const int group = draw_group(B, P.draw.nchunk);   // chunks per draw workgroup
   // the one-chunk instance, while every chunk fits on the GPU at its occupancy; otherwise the
   // grouped instance (one chunk per workgroup too, if they fit at its higher occupancy)
-  const bool one_chunk = draw_one_chunk(B, P.draw.nchunk,
-                                        kKeys ? kDrawResident : kDrawResidentHeld);
+  const bool one_chunk = draw_one_chunk(B, P.draw.nchunk + (kKeys ? K : 0), kDrawResidentHeld);
   const size_t n_chunks = static_cast<size_t>(B) * P.draw.nchunk;
   const size_t n_draw = static_cast<size_t>(B) * ((P.draw.nchunk + group - 1) / group);
   // with keys, one more workgroup per draft slot selects that slot's keys during the draw
