@@ -147,8 +147,8 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
     return;
   }
 
-  // ---- decider of request b: per-row argmax over the published chunks (rows up to n_b); each
-  // wave takes rows w, w + 4, ... and clears each word it has read. Every call's chunk
+  // ---- decider of request b: per-row argmax over the published chunks (rows up to n_b), each
+  // row by a group of lanes, every word polled at once; it clears each word it has read. Every call's chunk
   // workgroups publish their words, so the polls end whether or not the mark is set; the mark,
   // read alongside them, only decides afterwards whether the words are trusted.
   // wave 0's decision inputs (lane k: draft token k; the KV length) are loaded first, so their
@@ -161,34 +161,51 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(
   __syncthreads();
   const bool marked = load_coherent_u32(mark) != 0u;
   bool late = false;
-  for (int rr = w; rr < rows && rr <= nb; rr += kWaves) {
-    uint64_t* pw = words + (static_cast<size_t>(b) * rows + rr) * nchunk;
+  // rows in groups of G lanes (G = nchunk rounded up to a power of two, at most a wave), so the
+  // block polls every word of up to 4 * 64 / G rows at once
+  int G = 1;
+  while (G < nchunk && G < kWave) G <<= 1;
+  const int per_wave = kWave / G, g = lane / G, gi = lane % G;
+  const int nrows = min(rows, nb + 1);   // rows 0..n_b (none for a bad length)
+  for (int base = 0; base < nrows; base += kWaves * per_wave) {
+    const int rr = base + w * per_wave + g;
     float v = -INFINITY;
     int i = 0x7fffffff;
-    for (int j = lane; j < nchunk; j += kWave) {
-      uint64_t a = load_coherent(pw + j);
-      for (int polls = wait_polls; (a & kArgFlag) == 0ull && polls > 0; --polls) {
-        __builtin_amdgcn_s_sleep(2);
-        a = load_coherent(pw + j);
-      }
-      if ((a & kArgFlag) == 0ull) {
-        // give up on this word: the sentinel tells the clean-up below that its publish is still
-        // to come; a publish that lands first makes the swap fail and is taken here
-        a = cas_coherent(pw + j, 0ull, kAbandoned);
-        if ((a & kArgFlag) == 0ull) {
-          late = true;
-          continue;
+    if (rr < nrows) {
+      uint64_t* pw = words + (static_cast<size_t>(b) * rows + rr) * nchunk;
+      for (int j = gi; j < nchunk; j += G) {
+        uint64_t a = load_coherent(pw + j);
+        for (int polls = wait_polls; (a & kArgFlag) == 0ull && polls > 0; --polls) {
+          __builtin_amdgcn_s_sleep(2);
+          a = load_coherent(pw + j);
         }
+        if ((a & kArgFlag) == 0ull) {
+          // give up on this word: the sentinel tells the clean-up below that its publish is
+          // still to come; a publish that lands first makes the swap fail and is taken here
+          a = cas_coherent(pw + j, 0ull, kAbandoned);
+          if ((a & kArgFlag) == 0ull) {
+            late = true;
+            continue;
+          }
+        }
+        a &= ~kArgFlag;
+        if (better(lo_float(a), hi_int(a), v, i)) {
+          v = lo_float(a);
+          i = hi_int(a);
+        }
+        store_coherent(pw + j, 0ull);   // read: back to zero for the next call
       }
-      a &= ~kArgFlag;
-      if (better(lo_float(a), hi_int(a), v, i)) {
-        v = lo_float(a);
-        i = hi_int(a);
-      }
-      store_coherent(pw + j, 0ull);   // read: back to zero for the next call
     }
-    wave_argmax(v, i);
-    if (lane == 0) row_g[rr] = (i == 0x7fffffff) ? 0 : i;   // an all -inf row: the lowest id
+    // the group's (max, lowest id): the same pair whatever the order of the merges
+    for (int off = G / 2; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(v, off, kWave);
+      const int oi = __shfl_xor(i, off, kWave);
+      if (better(ov, oi, v, i)) {
+        v = ov;
+        i = oi;
+      }
+    }
+    if (gi == 0 && rr < nrows) row_g[rr] = (i == 0x7fffffff) ? 0 : i;   // all -inf: lowest id
   }
   if (__any(late || marked) && lane == 0) s_late = 1;
   __syncthreads();
