@@ -972,26 +972,44 @@ __global__ __launch_bounds__(kBlock) void sample_draw_kernel(
     c = cc;
     if (greedy || !t_ok) {
       if (c0 != 0) return;   // one workgroup of the request does all of it
-      if (t_ok)
-        for (int rr = w; rr <= K; rr += kWaves) {
-          const float2* pr = part_s + (static_cast<size_t>(b) * rows + rr) * nchunk_s;
+      // wave 0's draft tokens are loaded first, so their latency passes during the merges
+      const bool valid = lane < K;
+      const int xk = (w == 0 && valid) ? xtok[static_cast<size_t>(b) * K + lane] : 0;
+      if (t_ok) {
+        // rows in groups of G lanes (nchunk_s rounded up to a power of two, at most a wave), so
+        // every partial of up to 4 * 64 / G rows is loaded at once; the (max, lowest id) merge
+        // gives the same pair in any order
+        int G = 1;
+        while (G < nchunk_s && G < kWave) G <<= 1;
+        const int per_wave = kWave / G, g = lane / G, gi = lane % G;
+        for (int base = 0; base <= K; base += kWaves * per_wave) {
+          const int rr = base + w * per_wave + g;
           float v = -INFINITY;
           int i = 0x7fffffff;
-          for (int j = lane; j < nchunk_s; j += kWave) {
-            const float2 q = load_f2(pr + j);
-            if (better(q.x, __float_as_int(q.y), v, i)) {
-              v = q.x;
-              i = __float_as_int(q.y);
+          if (rr <= K) {
+            const float2* pr = part_s + (static_cast<size_t>(b) * rows + rr) * nchunk_s;
+            for (int j = gi; j < nchunk_s; j += G) {
+              const float2 q = load_f2(pr + j);
+              if (better(q.x, __float_as_int(q.y), v, i)) {
+                v = q.x;
+                i = __float_as_int(q.y);
+              }
             }
           }
-          wave_argmax(v, i);
+          for (int off = G / 2; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(v, off, kWave);
+            const int oi = __shfl_xor(i, off, kWave);
+            if (better(ov, oi, v, i)) {
+              v = ov;
+              i = oi;
+            }
+          }
           // a row whose logits are all -inf keeps no index: its first token is the lowest id
-          if (lane == 0) row_g[rr] = i == 0x7fffffff ? 0 : i;
+          if (gi == 0 && rr <= K) row_g[rr] = i == 0x7fffffff ? 0 : i;
         }
+      }
       __syncthreads();
       if (w != 0) return;
-      const bool valid = lane < K;
-      const int xk = valid ? xtok[static_cast<size_t>(b) * K + lane] : 0;
       const bool err = __ballot(!t_ok || (valid && (xk < 0 || xk >= V))) != 0ull;
       const unsigned long long miss = __ballot(!err && valid && xk != row_g[valid ? lane : 0]);
       const int mm = miss ? __ffsll(static_cast<long long>(miss)) - 1 : K;
