@@ -22,9 +22,14 @@
 //     weights per thread and per chunk and publishes the chunk's mass, tagged as written. Every
 //     workgroup of the request gathers all chunk masses, runs the same float64 prefix scan and
 //     so learns which chunk holds u*Z; that chunk's own workgroup finds the thread (block scan
-//     of the thread masses), which reads its few vectors again, then the token. A workgroup
-//     that has polled for a mass too long computes that chunk's mass itself (bit for bit what
-//     its owner publishes), so no workgroup ever waits on one that has not been scheduled.
+//     of the thread masses), then the token among that thread's few vectors. While one
+//     workgroup per chunk fits on the GPU, the workgroup keeps its vectors in registers and
+//     takes the block scan while the other masses arrive, every wave runs the chunk scan
+//     itself, and the owner's search runs in the one wave holding u*Z, with no workgroup
+//     barrier after the exchange; otherwise each workgroup takes several chunks and the owner
+//     reads its vectors again. A workgroup that has polled for a mass too long computes that
+//     chunk's mass itself (bit for bit what its owner publishes), so no workgroup ever waits on
+//     one that has not been scheduled.
 //     When every draft was kept and the statistics pass cut the extra row into the draw's
 //     chunks, the chunk masses come from its partials instead: nothing is re-read but the
 //     chunk holding u*Z, and nothing is exchanged.
