@@ -27,7 +27,16 @@ __device__ __forceinline__ void absorb(const float (&v)[n], float c, float& m, f
     s *= rel_exp2(m, bm, c);   // s is 0 while m is -inf, so the factor (0) is then moot
     m = bm;
   }
-  if (m > -INFINITY) {
+  // While |m c| <= 64 in every lane of the wave, each term is 2^fl(l c - fl(m c)) by one fma: the
+  // reference's rounding error (|m c| 2^-24 <= 2^-18) then moves every term by less than 3e-6
+  // relative. Beyond that (tiny temperatures) the gap is taken first, as rel_exp2 does.
+  const float mc = m * c;
+  if (__all(!(m > -INFINITY) || fabsf(mc) <= 64.f)) {
+    if (m > -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < n; ++j) s += fast_exp2(fmaf(v[j], c, -mc));
+    }
+  } else if (m > -INFINITY) {
 #pragma unroll
     for (int j = 0; j < n; ++j) s += rel_exp2(v[j], m, c);
   }
