@@ -15,6 +15,7 @@ from gpu_helpers import (announce, compare_fanout, compare_greedy, compare_looku
                          gpu_mixed, gpu_ngram, gpu_point, gpu_predict, gpu_sample,
                          gpu_sample_keys, poisoned, upload)
 from synthetic import as_greedy, make_contexts, make_runs, make_tiny_random, make_workload
+from synthetic.bf16 import f32_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -687,6 +688,32 @@ def test_tiny_temperatures(T):
             assert np.array_equal(s[k][~ties], gg[k][~ties]), k
         announce(f"tiny T={T}: sampling equals greedy on {int((~ties).sum())} requests "
                  f"without tied maxima")
+
+
+LOGIT_SHIFTS = [0.0, 25.0, 40.0, 90.0, -90.0, 60.0]
+
+
+def test_large_logits():
+    """Logits far from 0 (softmax is unchanged by a constant added to a row, "speculative
+    decodingとは", stages 3 and 4, so only the rounding of the shifted values differs): C3's value
+    recipe with each request's rows shifted by one of 0, +25, +40, +90, -90, +60 and stored in
+    bf16 again. At T = 0.7 the shifts put |max * log2(e)/T| below, across and far beyond 64, so
+    the statistics loop's waves take its one-fma form, its exact-gap form, or both within a row.
+    Sampling, point-mass and outcome-key paths against the oracle on the shifted values."""
+    wl = make_workload(3, 61, B=36, V=12347)
+    shift = np.array([LOGIT_SHIFTS[b % len(LOGIT_SHIFTS)] for b in range(wl.B)], np.float32)
+    tgt = f32_to_bf16_bits(wl.target_values() + shift[:, None, None])
+    drf = f32_to_bf16_bits(wl.draft_values() + shift[:, None, None])
+    ws = replace(wl, target=tgt, draft=drf)
+    dev = upload(ws)
+    announce("large logits: sample")
+    n, f, fb = compare_sample(ws, gpu_sample(ws, dev=dev))
+    announce(f"large logits: {n} checked, {f} flagged, {fb} differ")
+    lens = (np.arange(ws.B) % (ws.K + 1)).astype(np.int32)
+    announce("large logits: point")
+    compare_point(ws, gpu_point(ws, ws.tokens, lens, ws.T, dev=dev), ws.tokens, lens, ws.T)
+    announce("large logits: predict")
+    compare_predict(ws, gpu_predict(ws, 3, float(ws.T), dev=dev), 3, float(ws.T))
 
 
 @pytest.mark.parametrize("T", [1.0, 0.0])
