@@ -699,7 +699,8 @@ def test_large_logits():
     recipe with each request's rows shifted by one of 0, +25, +40, +90, -90, +60 and stored in
     bf16 again. At T = 0.7 the shifts put |max * log2(e)/T| below, across and far beyond 64, so
     the statistics loop's waves take its one-fma form, its exact-gap form, or both within a row.
-    Sampling, point-mass and outcome-key paths against the oracle on the shifted values."""
+    Sampling, point-mass, outcome-key, sampling-with-keys and mixed-temperature paths against the
+    oracle on the shifted values."""
     wl = make_workload(3, 61, B=36, V=12347)
     shift = np.array([LOGIT_SHIFTS[b % len(LOGIT_SHIFTS)] for b in range(wl.B)], np.float32)
     tgt = f32_to_bf16_bits(wl.target_values() + shift[:, None, None])
@@ -714,6 +715,15 @@ def test_large_logits():
     compare_point(ws, gpu_point(ws, ws.tokens, lens, ws.T, dev=dev), ws.tokens, lens, ws.T)
     announce("large logits: predict")
     compare_predict(ws, gpu_predict(ws, 3, float(ws.T), dev=dev), 3, float(ws.T))
+    announce("large logits: sample with keys")
+    plain = gpu_sample(ws, dev=dev)
+    g = gpu_sample_keys(ws, 3, True, dev=dev)
+    for k in plain:
+        assert np.array_equal(plain[k].view(np.int32), g[k].view(np.int32)), k
+    compare_sample_keys(ws, g, 3, True)
+    announce("large logits: mixed")
+    temps = np.array([[float(ws.T), 0.0, 1.3][b % 3] for b in range(ws.B)], np.float32)
+    compare_mixed(ws, gpu_mixed(ws, temps, dev=dev), temps)
 
 
 @pytest.mark.parametrize("T", [1.0, 0.0])
